@@ -1,0 +1,347 @@
+"""CPU oracle for single-pass verification of a draft token tree.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg import this package.  It shares no code, header,
+table or helper with the GPU library and imports nothing from it; the two meet
+only in the seeded input generators of the ``workloads`` package.
+
+Everything here is the plain definition of what the verification step
+computes, written out in NumPy in float64 (inputs are bf16 or fp32 values,
+which float64 holds exactly).  There is no blocking, no split of the key
+range, no online softmax and no reordering beyond what the definitions state.
+
+Sources (web pages; cited by title and section):
+
+* "vLLM-TreeEagle: Tree Attention优化的EAGLE3推测解码框架" (README) -- section
+  核心组件, item 1 TreeAttentionLayer: every candidate path is verified in one
+  forward pass under a tree attention mask built at run time; section
+  技术创新点 1: the mask supports irregular candidate trees; architecture
+  graph: the tree-attention layer sits on PagedAttention.
+* "EAGLE代码实现原理：从树结构缓冲到KV缓存优化的技术细节" -- section
+  KV缓存优化: ``KVCache.copy(indices, prev_length)`` gathers the cache rows
+  named by ``indices`` and writes them contiguously starting at
+  ``prev_length``; section 树结构缓冲: candidate paths share the computation
+  of their common prefix.
+* "P-EAGLE：vLLM集成并行推测解码加速LLM推理" -- section 技术原理和实现方式,
+  steps 3 and 4: the target scores all proposed tokens in one pass (with a
+  tree attention mask), and the sequence is truncated at the first rejected
+  token; section 技术难点和解决方案: the block manager rolls the cache back or
+  appends to it.
+* "vLLM EAGLE 投机解码实战：EAGLE/EAGLE3 草稿模型配置、源码实现与接受率评测" --
+  section 无损性保障: greedy speculative decoding must produce exactly what
+  greedy decoding produces.
+
+Readings taken where the pages are silent (each is also listed with the
+design notes):
+
+* Node 0 of every tree is the root, the last verified token; its K/V is
+  written by this pass like every other node's, and its draft token is never
+  compared.  ``parents[0] == -1`` and ``0 <= parents[i] < i`` for i >= 1.
+* Node i's key and value sit in the paged cache at logical position
+  ``prefix_len + i`` (the in-cache layout that ``KVCache.copy`` implies).
+* Query head h reads KV head ``h // (Hq // Hkv)``; scale defaults to
+  ``1/sqrt(D)``; there is no positional term inside attention.
+* Greedy acceptance: the target's choice at a node is the lowest vocabulary
+  index among the row's maxima (``np.argmax``).  The accepted path is the
+  longest path from the root whose every child carries its parent's choice;
+  equally long paths are ordered as sequences of node indices and the
+  smallest is taken (this only matters when siblings share a token).
+* ``accept_len`` counts accepted draft tokens (root and bonus excluded);
+  ``accepted_nodes`` lists the path from the root, padded with -1; the bonus
+  token is the target's choice at the last accepted node.  Compaction moves
+  ``accept_len + 1`` cache rows (root plus accepted drafts) and the new
+  length is ``prefix_len + accept_len + 1``.
+
+Parity pins for every function here live in the CPU test suite (brute force,
+closed forms, textbook special cases, invariants).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# status bits reported for malformed inputs
+ST_BAD_TREE = 1      # parents[0] != -1 or parents[i] outside [0, i)
+ST_BAD_CACHE = 2     # a block id outside [0, num_blocks) or prefix_len > max_prefix_len
+ST_BAD_TOKEN = 4     # a draft token (nodes >= 1) outside [0, V)
+
+
+# --------------------------------------------------------------------------
+# tree structure
+# --------------------------------------------------------------------------
+
+def tree_valid(parents) -> bool:
+    """A parent array is a valid tree iff the root has parent -1 and every
+    other node's parent comes before it ("vLLM-TreeEagle" README, 技术创新点 1:
+    the candidate tree is built dynamically, any shape allowed)."""
+    p = np.asarray(parents)
+    if len(p) == 0 or p[0] != -1:
+        return False
+    return all(0 <= int(p[i]) < i for i in range(1, len(p)))
+
+
+def tree_structure(parents):
+    """Ancestor-or-self sets and depths of a draft tree.
+
+    anc[i, j] is True iff node j lies on the path from the root to node i
+    (j == i included): ``anc*(i) = {i} U anc*(parent(i))``.  This is the tree
+    attention mask of the "vLLM-TreeEagle" README (核心组件, TreeAttentionLayer):
+    node i may attend to tree node j iff j is an ancestor of i or i itself.
+    depth[0] = 0 and depth[i] = depth[parent(i)] + 1.
+    """
+    p = np.asarray(parents, dtype=np.int64)
+    if not tree_valid(p):
+        raise ValueError("invalid parent array")
+    n = len(p)
+    anc = np.zeros((n, n), dtype=bool)
+    depth = np.zeros(n, dtype=np.int64)
+    for i in range(n):
+        if i > 0:
+            anc[i] = anc[p[i]]
+            depth[i] = depth[p[i]] + 1
+        anc[i, i] = True
+    return anc, depth
+
+
+def mask_words(anc) -> np.ndarray:
+    """Pack ancestor rows into little-endian 64-bit words: bit (j % 64) of word
+    (j // 64) of row i is set iff anc[i, j]."""
+    anc = np.asarray(anc, dtype=bool)
+    n = anc.shape[0]
+    w = (n + 63) // 64
+    out = np.zeros((n, w), dtype=np.uint64)
+    for i in range(n):
+        for j in np.nonzero(anc[i])[0]:
+            out[i, j // 64] |= np.uint64(1) << np.uint64(j % 64)
+    return out
+
+
+def build_tree_mask(parents):
+    """Batched mask and depth: parents [B, N] -> (mask uint64 [B, N, W],
+    depth int32 [B, N]).  Rows of invalid trees are left zero."""
+    parents = np.asarray(parents)
+    B, N = parents.shape
+    W = (N + 63) // 64
+    mask = np.zeros((B, N, W), dtype=np.uint64)
+    depth = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        if tree_valid(parents[b]):
+            anc, d = tree_structure(parents[b])
+            mask[b] = mask_words(anc)
+            depth[b] = d
+    return mask, depth
+
+
+# --------------------------------------------------------------------------
+# paged addressing
+# --------------------------------------------------------------------------
+
+def cache_rows(block_table_row, positions, block_size: int) -> np.ndarray:
+    """Flat cache row of logical positions: block ``table[t // bs]``, row
+    ``t % bs`` (paged KV layout under the tree-attention layer, "vLLM-TreeEagle"
+    README architecture graph; block-manager paging in the "P-EAGLE" page,
+    技术难点和解决方案)."""
+    t = np.asarray(positions, dtype=np.int64)
+    blk = np.asarray(block_table_row, dtype=np.int64)[t // block_size]
+    return blk * block_size + t % block_size
+
+
+# --------------------------------------------------------------------------
+# tree attention
+# --------------------------------------------------------------------------
+
+def tree_attention(q, k_cache, v_cache, block_table, prefix_lens, parents, scale=None,
+                   seqs=None, return_weights=False):
+    """Tree-masked attention of every draft node over the prefix and its own
+    ancestors.
+
+    Source: "vLLM-TreeEagle" README, 核心组件 item 1 and 技术创新点 1 (one
+    forward pass verifies every candidate path under a tree attention mask);
+    "EAGLE代码实现原理", 树结构缓冲 (paths share the common prefix); "P-EAGLE"
+    page, 技术原理和实现方式 step 3 (the target scores all proposed tokens in one
+    pass).
+
+    For sequence b, node i, query head h (KV head kh = h // g, g = Hq // Hkv)
+    the visible keys are the prefix positions ``[0, P_b)`` and the tree
+    positions ``P_b + j`` for every j in anc*(i).  With
+    ``s_t = scale * <q[b,i,h], k[t, kh]>`` over visible t:
+
+        out[b,i,h] = sum_t exp(s_t - max s) v[t, kh] / sum_t exp(s_t - max s)
+
+    q: [B, N, Hq, D]; caches: [num_blocks, block_size, Hkv, D] (any float
+    dtype; computed in float64).  Returns float64 [B, N, Hq, D]; sequences not
+    in ``seqs`` (default: all) are NaN.  With ``return_weights`` it also
+    returns {(b, kh): (weights [N*g, P_b+N], visible [N*g, P_b+N])} with rows
+    ordered node-major (row = i*g + h % g).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, N, Hq, D = q.shape
+    nb, bs, Hkv, D2 = k_cache.shape
+    assert D2 == D and Hq % Hkv == 0
+    g = Hq // Hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(D)
+    kf = np.asarray(k_cache).reshape(nb * bs, Hkv, D)
+    vf = np.asarray(v_cache).reshape(nb * bs, Hkv, D)
+    out = np.full((B, N, Hq, D), np.nan)
+    weights = {}
+    for b in (range(B) if seqs is None else seqs):
+        P = int(prefix_lens[b])
+        anc, _ = tree_structure(parents[b])
+        rows = cache_rows(block_table[b], np.arange(P + N), bs)
+        K = kf[rows].astype(np.float64)          # [P+N, Hkv, D]
+        V = vf[rows].astype(np.float64)
+        # visible[i, t]: key position t is visible to node i
+        visible = np.zeros((N, P + N), dtype=bool)
+        visible[:, :P] = True
+        visible[:, P:] = anc
+        for kh in range(Hkv):
+            Qg = q[b, :, kh * g:(kh + 1) * g, :].reshape(N * g, D)     # row = i*g + hh
+            vis = np.repeat(visible, g, axis=0)
+            s = scale * (Qg @ K[:, kh, :].T)                             # [N*g, P+N]
+            s = np.where(vis, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            w = np.exp(s - m)                                            # 0 where invisible
+            w = w / w.sum(axis=1, keepdims=True)
+            o = w @ V[:, kh, :]
+            out[b, :, kh * g:(kh + 1) * g, :] = o.reshape(N, g, D)
+            if return_weights:
+                weights[(b, kh)] = (w, vis)
+    if return_weights:
+        return out, weights
+    return out
+
+
+# --------------------------------------------------------------------------
+# greedy acceptance
+# --------------------------------------------------------------------------
+
+def target_argmax(logits) -> np.ndarray:
+    """The target's greedy choice per tree node: the lowest index among the
+    row's maxima (``np.argmax`` returns the first occurrence).  -0.0 and +0.0
+    compare equal.  Rows are the target's next-token scores at each node
+    ("P-EAGLE" page, 技术原理和实现方式 step 3)."""
+    return np.argmax(np.asarray(logits), axis=-1).astype(np.int64)
+
+
+def greedy_walk(am, draft_tokens, parents):
+    """Longest accepted path of one tree under greedy verification.
+
+    Source: "P-EAGLE" page, 技术原理和实现方式 step 4 (draft tokens are accepted
+    while they agree with the target and the sequence is cut at the first
+    rejection); "vLLM EAGLE 投机解码实战", 无损性保障 (greedy speculative
+    decoding emits exactly the greedy tokens).
+
+    An edge parent(c) -> c is accepted iff ``draft_tokens[c] == am[parent(c)]``
+    (the child's draft token is the target's greedy choice after its parent).
+    The accepted path is the longest root-started path whose edges are all
+    accepted; if several are equally long, the lexicographically smallest
+    sequence of node indices.  Written as the plain recursion: from a node,
+    follow the accepted child with the longest accepted continuation, the
+    lowest child index among equals.  Returns (path, bonus), bonus being the
+    target's choice at the path's last node.
+    """
+    parents = np.asarray(parents)
+    draft_tokens = np.asarray(draft_tokens)
+    n = len(parents)
+
+    def longest_from(cur):
+        best = [cur]
+        for c in range(cur + 1, n):       # ascending: the first of equals is kept
+            if parents[c] == cur and draft_tokens[c] == am[cur]:
+                cand = [cur] + longest_from(c)
+                if len(cand) > len(best):
+                    best = cand
+        return best
+
+    path = longest_from(0)
+    return path, int(am[path[-1]])
+
+
+def accept_greedy(logits, draft_tokens, parents):
+    """Batched greedy acceptance: logits [B, N, V], draft_tokens [B, N],
+    parents [B, N] -> dict with accept_len [B], accepted_nodes [B, N] (path from
+    the root, -1 padded), bonus [B], argmax [B, N]."""
+    logits = np.asarray(logits)
+    B, N, _ = logits.shape
+    am = target_argmax(logits)
+    accept_len = np.zeros(B, dtype=np.int32)
+    nodes = np.full((B, N), -1, dtype=np.int32)
+    bonus = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        path, bon = greedy_walk(am[b], draft_tokens[b], parents[b])
+        accept_len[b] = len(path) - 1
+        nodes[b, :len(path)] = path
+        bonus[b] = bon
+    return {"accept_len": accept_len, "accepted_nodes": nodes, "bonus": bonus,
+            "argmax": am.astype(np.int32)}
+
+
+# --------------------------------------------------------------------------
+# KV compaction
+# --------------------------------------------------------------------------
+
+def kv_compact(k_cache, v_cache, block_table, prefix_lens, accepted_nodes, accept_len):
+    """Move the accepted path's K/V into contiguous slots after the prefix.
+
+    Source: "EAGLE代码实现原理", KV缓存优化 (``copy(indices, prev_length)``:
+    select the rows named by ``indices`` into a new tensor, then copy it into
+    the rows starting at ``prev_length``); "P-EAGLE" page, 技术难点和解决方案
+    (roll the cache back to the accepted tokens).  With L = accept_len + 1 and
+    path = accepted_nodes[:L], the rows at logical positions ``P + path`` are
+    gathered first and then written to positions ``P + 0 .. P + L - 1``; every
+    other row keeps its bytes.  Works on copies of the caches (any dtype, bytes
+    preserved); returns (k_new, v_new, new_lens = P + L).
+    """
+    k_new = np.array(k_cache, copy=True)
+    v_new = np.array(v_cache, copy=True)
+    nb, bs = k_new.shape[:2]
+    kf = k_new.reshape(nb * bs, *k_new.shape[2:])
+    vf = v_new.reshape(nb * bs, *v_new.shape[2:])
+    B = len(prefix_lens)
+    new_lens = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        P = int(prefix_lens[b])
+        L = int(accept_len[b]) + 1
+        path = np.asarray(accepted_nodes[b][:L], dtype=np.int64)
+        src = cache_rows(block_table[b], P + path, bs)
+        dst = cache_rows(block_table[b], P + np.arange(L), bs)
+        ks = kf[src].copy()
+        vs = vf[src].copy()
+        kf[dst] = ks
+        vf[dst] = vs
+        new_lens[b] = P + L
+    return k_new, v_new, new_lens
+
+
+# --------------------------------------------------------------------------
+# input validation
+# --------------------------------------------------------------------------
+
+def input_status(parents, block_table=None, prefix_lens=None, num_blocks=None,
+                 max_prefix_len=None, block_size=16, draft_tokens=None, V=None) -> int:
+    """Status bits a verification call should report for these inputs:
+    ST_BAD_TREE for an invalid parent array, ST_BAD_CACHE for a block id
+    outside [0, num_blocks) among the blocks a sequence uses (prefix plus
+    tree) or a prefix longer than ``max_prefix_len``, ST_BAD_TOKEN for a draft
+    token of a non-root node outside [0, V)."""
+    st = 0
+    parents = np.asarray(parents)
+    B, N = parents.shape
+    for b in range(B):
+        if not tree_valid(parents[b]):
+            st |= ST_BAD_TREE
+    if block_table is not None:
+        for b in range(B):
+            P = int(prefix_lens[b])
+            if P > max_prefix_len or P < 0:
+                st |= ST_BAD_CACHE
+                continue
+            used = (P + N + block_size - 1) // block_size
+            blk = np.asarray(block_table[b][:used])
+            if np.any(blk < 0) or np.any(blk >= num_blocks):
+                st |= ST_BAD_CACHE
+    if draft_tokens is not None:
+        d = np.asarray(draft_tokens)[:, 1:]
+        if np.any(d < 0) or np.any(d >= V):
+            st |= ST_BAD_TOKEN
+    return st
