@@ -1,0 +1,217 @@
+/*
+ * tv.h -- single-pass verification of a draft token tree on AMD Instinct
+ * MI355X (gfx950): tree mask, tree-masked paged attention, greedy acceptance
+ * and KV compaction.
+ *
+ * The problem (web pages, cited by title and section):
+ *   - "vLLM-TreeEagle: Tree Attention优化的EAGLE3推测解码框架" (README),
+ *     核心组件 item 1 TreeAttentionLayer and 技术创新点 1: the target model
+ *     verifies every candidate path of a draft tree in one forward pass under a
+ *     tree attention mask that is built at run time for any tree shape; the
+ *     architecture graph puts this layer on top of PagedAttention.
+ *   - "EAGLE代码实现原理：从树结构缓冲到KV缓存优化的技术细节", 树结构缓冲: all
+ *     candidate paths share their common prefix; KV缓存优化:
+ *     KVCache.copy(indices, prev_length) gathers accepted rows and writes them
+ *     contiguously from prev_length.
+ *   - "P-EAGLE：vLLM集成并行推测解码加速LLM推理", 技术原理和实现方式 steps 3-4:
+ *     the target scores all proposed tokens at once; drafts are accepted while
+ *     they agree with the target and the sequence is cut at the first
+ *     rejection.
+ *   - "vLLM EAGLE 投机解码实战：EAGLE/EAGLE3 草稿模型配置、源码实现与接受率评测",
+ *     无损性保障: greedy speculative decoding yields exactly the greedy tokens.
+ *
+ * Conventions shared by every call
+ *   - B sequences, N tree nodes per sequence (node 0 is the root, the last
+ *     verified token; 1 <= N <= TV_MAX_NODES), Hq query heads, Hkv KV heads
+ *     (Hq % Hkv == 0, query head h reads KV head h / (Hq/Hkv)), head dim D,
+ *     vocab V.  W = ceil(N / 64) mask words per node.
+ *   - parents[b][0] == -1 and 0 <= parents[b][i] < i for i >= 1.
+ *   - Paged K/V cache: k_cache and v_cache are [num_blocks][block_size][Hkv][D]
+ *     row-major.  Logical position t of sequence b lives in block
+ *     block_table[b][t / block_size], row t % block_size.  Sequence b's prefix
+ *     is t in [0, prefix_lens[b]); tree node i's key/value sit at
+ *     t = prefix_lens[b] + i and must be written before tv_tree_attention.
+ *   - All pointers are DEVICE pointers to caller-owned memory; the library
+ *     allocates nothing and keeps no global mutable state.  Integers are
+ *     int32 row-major.
+ *   - Every call checks its scalar arguments on the host, returns a status
+ *     and, on TV_OK, has enqueued its kernels on `stream` (asynchronous; no
+ *     host synchronisation).  On any error other than TV_ERR_LAUNCH nothing is
+ *     launched.
+ *   - dev_status (optional, may be NULL): device int32 that the kernels OR
+ *     status bits into for malformed data that only the device can see
+ *     (TV_DEV_*).  The caller zeroes it; bits accumulate across calls.  A
+ *     sequence that raises a bit gets unspecified (but in-bounds) outputs.
+ */
+#ifndef TV_H
+#define TV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TV_MAX_NODES 256
+
+/* exported symbols of libtv.so */
+#define TV_API __attribute__((visibility("default")))
+
+typedef enum {
+  TV_OK = 0,
+  TV_ERR_NULL = 1,        /* a required pointer is NULL */
+  TV_ERR_SHAPE = 2,       /* a size <= 0, Hq % Hkv != 0, N > TV_MAX_NODES, or the
+                             block table cannot hold max_prefix_len + N positions */
+  TV_ERR_DTYPE = 3,       /* dtype is neither TV_F32 nor TV_BF16 */
+  TV_ERR_UNSUPPORTED = 4, /* D not in {64, 128} or block_size != 16 */
+  TV_ERR_ALIGN = 5,       /* q, out, cache or logits pointer not 16-byte aligned */
+  TV_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the queried size */
+  TV_ERR_LAUNCH = 7       /* the HIP runtime reported an error at launch */
+} tv_status;
+
+typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+
+/* device status bits */
+#define TV_DEV_BAD_TREE 1   /* parents[b][0] != -1 or parents[b][i] not in [0, i) */
+#define TV_DEV_BAD_CACHE 2  /* a used block id outside [0, num_blocks), or a prefix
+                               length outside [0, max_prefix_len] */
+#define TV_DEV_BAD_TOKEN 4  /* draft_tokens[b][i] (i >= 1) outside [0, V) */
+
+/* Name of a status code (static string). */
+TV_API const char* tv_status_string(tv_status s);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+TV_API int tv_version(void);
+
+/*
+ * tv_build_tree_mask -- ancestor-or-self bitmask and depth of every node.
+ * ("vLLM-TreeEagle" README, 核心组件 item 1: the tree attention mask is built
+ * dynamically; 技术创新点 1: any tree shape.)
+ *
+ *   parents  [B][N] int32, device.
+ *   mask     [B][N][W] uint64, device, written: bit (j % 64) of word j / 64 of
+ *            mask[b][i] is set iff node j is node i or one of its ancestors.
+ *   depth    [B][N] int32, device, written (may be NULL): edges from the root.
+ *   Errors: TV_ERR_NULL, TV_ERR_SHAPE.  A sequence whose parent array is not
+ *   a tree sets TV_DEV_BAD_TREE and gets an all-zero mask and zero depths.
+ */
+TV_API tv_status tv_build_tree_mask(const int32_t* parents, int32_t B, int32_t N, uint64_t* mask,
+                             int32_t* depth, int32_t* dev_status, hipStream_t stream);
+
+/*
+ * Workspace bytes tv_tree_attention needs for these sizes (0 when the key
+ * range is not split).  The workspace holds per-split partial softmax state
+ * and needs no initialisation.
+ */
+TV_API size_t tv_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t max_prefix_len, tv_dtype dtype);
+
+/*
+ * tv_tree_attention -- tree-masked attention of every draft node over the
+ * paged prefix and its own ancestors, in one pass.
+ * ("vLLM-TreeEagle" README, 核心组件 item 1 and 技术创新点 1; "EAGLE代码实现原理",
+ * 树结构缓冲: each prefix K/V tile is read once and serves every node and every
+ * query head of its KV head; "P-EAGLE", 技术原理和实现方式 step 3.)
+ *
+ * For sequence b, node i, query head h, KV head kh = h / (Hq/Hkv), the visible
+ * keys are prefix positions [0, P_b) and tree positions P_b + j for every j
+ * whose bit is set in mask[b][i]:
+ *   out[b][i][h] = sum_t softmax_t(scale * <q[b][i][h], k[t][kh]>) * v[t][kh].
+ *
+ *   q            [B][N][Hq][D], dtype, device, 16-byte aligned.
+ *   k_cache, v_cache  [num_blocks][block_size][Hkv][D], dtype, device, 16-byte
+ *                aligned; read only.
+ *   block_table  [B][max_blocks] int32, device.
+ *   prefix_lens  [B] int32, device; every entry <= max_prefix_len (host int).
+ *   mask         [B][N][W] uint64, device (as written by tv_build_tree_mask).
+ *   out          [B][N][Hq][D], dtype, device, 16-byte aligned, written.
+ *   scale        softmax scale; <= 0 selects 1/sqrt(D).
+ *   dtype        TV_BF16 (fp32 accumulation, bf16 output rounded to nearest
+ *                even) or TV_F32 (fp32 throughout).
+ *   workspace    device buffer of at least
+ *                tv_tree_attention_workspace_size(...) bytes (may be NULL if
+ *                that size is 0).
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_DTYPE, TV_ERR_UNSUPPORTED,
+ * TV_ERR_ALIGN, TV_ERR_WORKSPACE, TV_ERR_LAUNCH.  Device: TV_DEV_BAD_CACHE.
+ */
+TV_API tv_status tv_tree_attention(const void* q, const void* k_cache, const void* v_cache,
+                            int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                            int32_t block_size, const int32_t* prefix_lens, int32_t max_prefix_len,
+                            const uint64_t* mask, void* out, int32_t B, int32_t N, int32_t Hq,
+                            int32_t Hkv, int32_t D, float scale, tv_dtype dtype, void* workspace,
+                            size_t workspace_bytes, int32_t* dev_status, hipStream_t stream);
+
+/*
+ * Workspace bytes tv_accept_greedy needs.  The workspace must be zero-filled
+ * before its first use; every call leaves it zero-filled again when its
+ * kernel ends.  Calls that share one workspace must be ordered (same stream).
+ */
+TV_API size_t tv_accept_greedy_workspace_size(int32_t B, int32_t N, int32_t V);
+
+/*
+ * tv_accept_greedy -- target argmax of every tree node and the longest
+ * accepted path.
+ * ("P-EAGLE", 技术原理和实现方式 steps 3-4; "vLLM EAGLE 投机解码实战", 无损性保障.)
+ *
+ * am[b][i] = lowest v with logits[b][i][v] == max_u logits[b][i][u] (-0.0 and
+ * +0.0 compare equal; NaN rows are unspecified).  An edge parent(c) -> c is
+ * accepted iff draft_tokens[b][c] == am[b][parent(c)].  The accepted path is
+ * the longest root-started path of accepted edges, the smallest node-index
+ * sequence among equally long ones.
+ *
+ *   logits          [B][N][V] fp32, device, 16-byte aligned; row i holds the
+ *                   target's next-token scores after node i.
+ *   draft_tokens    [B][N] int32, device (entry 0, the root, is not compared).
+ *   parents         [B][N] int32, device.
+ *   accept_len      [B] int32, written: accepted draft tokens (root and bonus
+ *                   excluded).
+ *   accepted_nodes  [B][N] int32, written: the path from the root (node 0
+ *                   first), padded with -1.
+ *   bonus_token     [B] int32, written: am at the path's last node.
+ *   target_argmax   [B][N] int32, written (may be NULL): am.
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_ALIGN, TV_ERR_WORKSPACE,
+ * TV_ERR_LAUNCH.  Device: TV_DEV_BAD_TREE, TV_DEV_BAD_TOKEN (the sequence then
+ * reports accept_len 0, path [0] and bonus am[b][0]).
+ */
+TV_API tv_status tv_accept_greedy(const float* logits, const int32_t* draft_tokens, const int32_t* parents,
+                           int32_t B, int32_t N, int32_t V, int32_t* accept_len,
+                           int32_t* accepted_nodes, int32_t* bonus_token, int32_t* target_argmax,
+                           void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                           hipStream_t stream);
+
+/*
+ * tv_kv_compact -- move the accepted path's K/V rows into the contiguous
+ * positions right after the prefix, in place.
+ * ("EAGLE代码实现原理", KV缓存优化: copy(indices, prev_length) selects the
+ * indexed rows and then copies them to the rows starting at prev_length;
+ * "P-EAGLE", 技术难点和解决方案: the cache is rolled back to the accepted
+ * tokens.)
+ *
+ * With L = accept_len[b] + 1 and path = accepted_nodes[b][0 .. L-1], the rows
+ * at logical positions P_b + path[j] are gathered and written to positions
+ * P_b + j (j < L), for every KV head, in both caches, with the result of
+ * gathering all sources before writing any destination.  All other rows keep
+ * their bytes.  The path must be strictly increasing and start at node 0 (as
+ * tv_accept_greedy writes it).
+ *
+ *   k_cache, v_cache  [num_blocks][block_size][Hkv][D], dtype, device, 16-byte
+ *                     aligned, updated in place.
+ *   new_lens          [B] int32, written (may be NULL): P_b + L.
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_DTYPE, TV_ERR_UNSUPPORTED,
+ * TV_ERR_ALIGN, TV_ERR_LAUNCH.  Device: TV_DEV_BAD_CACHE (block id out of
+ * range), TV_DEV_BAD_TREE (a path that is not strictly increasing from node 0
+ * or an accept_len outside [0, N-1]); the sequence is then left untouched.
+ */
+TV_API tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks, const int32_t* block_table,
+                        int32_t max_blocks, int32_t block_size, const int32_t* prefix_lens,
+                        const int32_t* accepted_nodes, const int32_t* accept_len, int32_t B,
+                        int32_t N, int32_t Hkv, int32_t D, tv_dtype dtype, int32_t* new_lens,
+                        int32_t* dev_status, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TV_H */

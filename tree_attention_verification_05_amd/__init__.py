@@ -1,0 +1,29 @@
+"""Single-pass verification of a draft token tree on AMD Instinct MI355X.
+
+The four calls of libtv (hand-written HIP kernels for gfx950) with the same
+names as the C ABI in ``include/tv.h``:
+
+* ``tv_build_tree_mask``  -- ancestor-or-self bitmask of every tree node
+* ``tv_tree_attention``   -- tree-masked attention over the paged prefix
+* ``tv_accept_greedy``    -- target argmax and the longest accepted path
+* ``tv_kv_compact``       -- move the accepted path's K/V after the prefix
+
+Importing the package loads libtv.so and raises if it has not been built.
+"""
+from ._lib import (  # noqa: F401
+    BLOCK_SIZE,
+    TV_BF16,
+    TV_DEV_BAD_CACHE,
+    TV_DEV_BAD_TOKEN,
+    TV_DEV_BAD_TREE,
+    TV_F32,
+    TV_MAX_NODES,
+    TVError,
+    header_functions,
+    lib,
+    tv_accept_greedy,
+    tv_build_tree_mask,
+    tv_kv_compact,
+    tv_tree_attention,
+    tv_tree_attention_workspace_size,
+)

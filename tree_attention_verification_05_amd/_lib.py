@@ -1,0 +1,258 @@
+"""ctypes binding of libtv.so: the same four calls, argument marshalling only.
+
+Every function takes torch tensors that live on an AMD GPU, checks dtype,
+shape, contiguity and device, and passes raw device pointers plus the current
+HIP stream of that device to the library.  All computation happens in the
+library's kernels; there is no fallback of any kind: if libtv.so is missing
+or a tensor is on the CPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtv.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "tv.h")
+
+TV_OK = 0
+TV_F32, TV_BF16 = 0, 1
+TV_DEV_BAD_TREE, TV_DEV_BAD_CACHE, TV_DEV_BAD_TOKEN = 1, 2, 4
+TV_MAX_NODES = 256
+BLOCK_SIZE = 16
+
+_c_i32 = ctypes.c_int32
+_c_ptr = ctypes.c_void_p
+_c_size = ctypes.c_size_t
+
+
+class TVError(RuntimeError):
+    """A libtv call returned a status other than TV_OK."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {text} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m tree_attention_verification_05_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "tv_status_string": (ctypes.c_char_p, [_c_i32]),
+        "tv_version": (ctypes.c_int, []),
+        "tv_build_tree_mask": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+        "tv_tree_attention_workspace_size": (_c_size, [_c_i32] * 6 + [_c_i32]),
+        "tv_tree_attention": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_ptr, _c_i32, _c_i32,
+                                       _c_ptr, _c_i32, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32,
+                                       _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_ptr, _c_size,
+                                       _c_ptr, _c_ptr]),
+        "tv_accept_greedy_workspace_size": (_c_size, [_c_i32] * 3),
+        "tv_accept_greedy": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_ptr,
+                                      _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr, _c_ptr]),
+        "tv_kv_compact": (_c_i32, [_c_ptr, _c_ptr, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr, _c_ptr,
+                                   _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
+                                   _c_ptr]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def header_functions() -> list:
+    """Names of the functions tv.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"TV_API\s+[\w\s\*]*?\b(tv_\w+)\s*\(", text)))
+
+
+# ------------------------------------------------------------------ helpers
+
+def _check(fn: str, st: int) -> None:
+    if st != TV_OK:
+        raise TVError(fn, st, lib.tv_status_string(st).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name}: dtype {t.dtype} not allowed")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _tv_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TV_BF16
+    if t.dtype == torch.float32:
+        return TV_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+_accept_ws: Dict[Tuple[int, int], torch.Tensor] = {}
+
+
+def accept_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A zero-filled workspace for tv_accept_greedy, kept per device (the
+    library leaves it zero-filled after every call on its stream)."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    key = (idx, 0)
+    ws = _accept_ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        _accept_ws[key] = ws
+    return ws
+
+
+# ------------------------------------------------------------------ calls
+
+def tv_build_tree_mask(parents: torch.Tensor, mask: Optional[torch.Tensor] = None,
+                       depth: Optional[torch.Tensor] = None,
+                       dev_status: Optional[torch.Tensor] = None):
+    """parents int32 [B, N] -> (mask int64 [B, N, W] holding the uint64 words,
+    depth int32 [B, N])."""
+    _dev(parents, "parents", torch.int32)
+    B, N = parents.shape
+    W = (N + 63) // 64
+    if mask is None:
+        mask = torch.empty((B, N, W), dtype=torch.int64, device=parents.device)
+    _dev(mask, "mask", (torch.int64, torch.uint64), (B, N, W))
+    if depth is None:
+        depth = torch.empty((B, N), dtype=torch.int32, device=parents.device)
+    _dev(depth, "depth", torch.int32, (B, N))
+    if dev_status is not None:
+        _dev(dev_status, "dev_status", torch.int32)
+    _check("tv_build_tree_mask", lib.tv_build_tree_mask(
+        _ptr(parents), B, N, _ptr(mask), _ptr(depth), _ptr(dev_status), _stream(parents)))
+    return mask, depth
+
+
+def tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len, dtype) -> int:
+    return int(lib.tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len, dtype))
+
+
+def tv_tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_table: torch.Tensor, prefix_lens: torch.Tensor, max_prefix_len: int,
+                      mask: torch.Tensor, out: Optional[torch.Tensor] = None, scale: float = 0.0,
+                      workspace: Optional[torch.Tensor] = None,
+                      dev_status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q [B, N, Hq, D]; caches [num_blocks, 16, Hkv, D] (bf16 or fp32, same as
+    q); block_table int32 [B, max_blocks]; prefix_lens int32 [B]; mask from
+    tv_build_tree_mask.  Returns out [B, N, Hq, D] in q's dtype."""
+    dt = _tv_dtype(q)
+    _dev(q, "q", q.dtype)
+    B, N, Hq, D = q.shape
+    nb, bs, Hkv, D2 = k_cache.shape
+    _dev(k_cache, "k_cache", q.dtype, (nb, bs, Hkv, D))
+    _dev(v_cache, "v_cache", q.dtype, (nb, bs, Hkv, D))
+    _dev(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _dev(prefix_lens, "prefix_lens", torch.int32, (B,))
+    _dev(mask, "mask", (torch.int64, torch.uint64), (B, N, (N + 63) // 64))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype, q.shape)
+    need = tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len, dt)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if dev_status is not None:
+        _dev(dev_status, "dev_status", torch.int32)
+    _check("tv_tree_attention", lib.tv_tree_attention(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_table), block_table.shape[1], bs,
+        _ptr(prefix_lens), int(max_prefix_len), _ptr(mask), _ptr(out), B, N, Hq, Hkv, D,
+        float(scale), dt, _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(q)))
+    return out
+
+
+def tv_accept_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, parents: torch.Tensor,
+                     accept_len: Optional[torch.Tensor] = None,
+                     accepted_nodes: Optional[torch.Tensor] = None,
+                     bonus_token: Optional[torch.Tensor] = None,
+                     target_argmax: Optional[torch.Tensor] = None, want_argmax: bool = True,
+                     workspace: Optional[torch.Tensor] = None,
+                     dev_status: Optional[torch.Tensor] = None):
+    """logits fp32 [B, N, V]; draft_tokens, parents int32 [B, N].  Returns
+    (accept_len [B], accepted_nodes [B, N], bonus_token [B], target_argmax
+    [B, N] or None), all int32."""
+    _dev(logits, "logits", torch.float32)
+    B, N, V = logits.shape
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, N))
+    _dev(parents, "parents", torch.int32, (B, N))
+    dev = logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if accepted_nodes is None:
+        accepted_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if bonus_token is None:
+        bonus_token = torch.empty(B, dtype=torch.int32, device=dev)
+    if target_argmax is None and want_argmax:
+        target_argmax = torch.empty((B, N), dtype=torch.int32, device=dev)
+    _dev(accept_len, "accept_len", torch.int32, (B,))
+    _dev(accepted_nodes, "accepted_nodes", torch.int32, (B, N))
+    _dev(bonus_token, "bonus_token", torch.int32, (B,))
+    if target_argmax is not None:
+        _dev(target_argmax, "target_argmax", torch.int32, (B, N))
+    need = int(lib.tv_accept_greedy_workspace_size(B, N, V))
+    if workspace is None:
+        workspace = accept_workspace(dev, need)
+    if dev_status is not None:
+        _dev(dev_status, "dev_status", torch.int32)
+    _check("tv_accept_greedy", lib.tv_accept_greedy(
+        _ptr(logits), _ptr(draft_tokens), _ptr(parents), B, N, V, _ptr(accept_len),
+        _ptr(accepted_nodes), _ptr(bonus_token), _ptr(target_argmax), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(dev_status), _stream(logits)))
+    return accept_len, accepted_nodes, bonus_token, target_argmax
+
+
+def tv_kv_compact(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                  prefix_lens: torch.Tensor, accepted_nodes: torch.Tensor,
+                  accept_len: torch.Tensor, new_lens: Optional[torch.Tensor] = None,
+                  dev_status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Compacts the accepted path's K/V in place; returns new_lens int32 [B]."""
+    dt = _tv_dtype(k_cache)
+    nb, bs, Hkv, D = k_cache.shape
+    _dev(k_cache, "k_cache", k_cache.dtype)
+    _dev(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
+    _dev(accepted_nodes, "accepted_nodes", torch.int32)
+    B, N = accepted_nodes.shape
+    _dev(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _dev(prefix_lens, "prefix_lens", torch.int32, (B,))
+    _dev(accept_len, "accept_len", torch.int32, (B,))
+    if new_lens is None:
+        new_lens = torch.empty(B, dtype=torch.int32, device=k_cache.device)
+    _dev(new_lens, "new_lens", torch.int32, (B,))
+    if dev_status is not None:
+        _dev(dev_status, "dev_status", torch.int32)
+    _check("tv_kv_compact", lib.tv_kv_compact(
+        _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_table), block_table.shape[1], bs,
+        _ptr(prefix_lens), _ptr(accepted_nodes), _ptr(accept_len), B, N, Hkv, D, dt,
+        _ptr(new_lens), _ptr(dev_status), _stream(k_cache)))
+    return new_lens

@@ -1,0 +1,232 @@
+// Greedy verification of a draft tree against the target logits, one launch.
+// ("P-EAGLE", 技术原理和实现方式 steps 3-4: the target scores every proposed
+// token at once, drafts are accepted while they agree with it; "vLLM EAGLE
+// 投机解码实战", 无损性保障: greedy speculative decoding equals greedy decoding.)
+//
+// Phase 1 (every workgroup): one chunk of one logits row is scanned with
+// 16-byte loads; the chunk's best (value, index) is packed into a 64-bit key
+// that orders by value and then by lower index, and stored in the workspace.
+// Phase 2 (the last workgroup of each sequence to finish, found with a
+// per-sequence arrival counter): reduce the chunk keys of the sequence's N
+// rows to the target argmax, validate the tree and draft tokens, and find the
+// longest accepted path (smallest node sequence among equals).  That
+// workgroup also resets the counter and the chunk keys it consumed, so the
+// whole workspace is zero again on exit, whatever sizes the next call uses.
+#include "tv_internal.h"
+
+namespace tv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMinChunk = 4096;      // floats per workgroup at least
+constexpr int kTargetBlocks = 2048;  // enough workgroups to keep HBM busy
+
+struct Split {
+  int chunk;   // floats per chunk (multiple of 4)
+  int chunks;  // chunks per row
+};
+
+Split split_for(int B, int N, int V) {
+  const long rows = static_cast<long>(B) * N;
+  long c = (kTargetBlocks + rows - 1) / rows;
+  const long cmax = (V + kMinChunk - 1) / kMinChunk;
+  if (c > cmax) c = cmax;
+  if (c < 1) c = 1;
+  int chunk = static_cast<int>((V + c - 1) / c);
+  chunk = (chunk + 3) & ~3;
+  Split s;
+  s.chunk = chunk;
+  s.chunks = (V + chunk - 1) / chunk;
+  return s;
+}
+
+// Orders floats as unsigned integers; -0.0 and +0.0 map to the same value.
+__device__ __forceinline__ uint32_t ordered(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// Larger key = larger value, then lower index.
+__device__ __forceinline__ uint64_t make_key(float v, int idx) {
+  return (static_cast<uint64_t>(ordered(v)) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(idx));
+}
+__device__ __forceinline__ int key_index(uint64_t k) {
+  return static_cast<int>(~static_cast<uint32_t>(k & 0xFFFFFFFFu));
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t w = __shfl_xor(v, o, 64);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads) void accept_kernel(AcceptArgs a, int chunk, int chunks) {
+  __shared__ uint64_t wbest[kThreads / 64];
+  __shared__ int s_last;
+  __shared__ int s_par[TV_MAX_NODES], s_tok[TV_MAX_NODES], s_am[TV_MAX_NODES];
+  __shared__ int s_ok[TV_MAX_NODES], s_dep[TV_MAX_NODES], s_on[TV_MAX_NODES];
+  __shared__ int s_bad, s_dmax, s_path[TV_MAX_NODES];
+
+  const int N = a.N, V = a.V;
+  const long row = blockIdx.x / chunks;  // global row b*N + i
+  const int ch = blockIdx.x % chunks;
+  const int b = static_cast<int>(row / N);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  uint32_t* counters = static_cast<uint32_t*>(a.workspace);
+  uint64_t* keys = reinterpret_cast<uint64_t*>(static_cast<char*>(a.workspace) +
+                                               ((static_cast<size_t>(a.B) * 4 + 255) & ~size_t(255)));
+
+  // ---- phase 1: best (value, lowest index) of this chunk ----
+  const int lo = ch * chunk;
+  const int hi = min(V, lo + chunk);
+  const float* x = a.logits + row * V;
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  if ((V & 3) == 0) {
+    // 16-byte loads; each thread visits increasing indices, so strict '>'
+    // keeps the first occurrence of its maximum
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
+    for (int j = lo / 4 + tid; j < hi / 4; j += kThreads) {
+      const f32x4 v = __builtin_nontemporal_load(x4 + j);
+      if (v.x > bv || bi == 0x7FFFFFFF) { bv = v.x; bi = 4 * j; }
+      if (v.y > bv) { bv = v.y; bi = 4 * j + 1; }
+      if (v.z > bv) { bv = v.z; bi = 4 * j + 2; }
+      if (v.w > bv) { bv = v.w; bi = 4 * j + 3; }
+    }
+  } else {
+    for (int j = lo + tid; j < hi; j += kThreads) {
+      const float v = x[j];
+      if (v > bv || bi == 0x7FFFFFFF) { bv = v; bi = j; }
+    }
+  }
+  uint64_t key = (bi == 0x7FFFFFFF) ? 0ull : make_key(bv, bi);
+  key = wave_max_u64(key);
+  if (lane == 0) wbest[wave] = key;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t k = wbest[0];
+    for (int w = 1; w < kThreads / 64; ++w) k = wbest[w] > k ? wbest[w] : k;
+    keys[row * chunks + ch] = k;
+    __threadfence();
+    const uint32_t arrived = atomicAdd(&counters[b], 1u);
+    s_last = (arrived == static_cast<uint32_t>(N) * chunks - 1u);
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- phase 2: this workgroup is the last of sequence b ----
+  __threadfence();
+  if (tid == 0) {
+    s_bad = 0;
+    s_dmax = 0;
+  }
+  const size_t base = static_cast<size_t>(b) * N;
+  for (int i = tid; i < N; i += kThreads) {
+    uint64_t* kr = keys + (base + i) * chunks;
+    uint64_t k = __builtin_nontemporal_load(kr);
+    for (int c = 1; c < chunks; ++c) {
+      const uint64_t w = __builtin_nontemporal_load(kr + c);
+      k = w > k ? w : k;
+    }
+    // leave the workspace zero-filled for the next call, whatever its sizes
+    for (int c = 0; c < chunks; ++c) kr[c] = 0ull;
+    const int am = key_index(k);
+    s_am[i] = am;
+    if (a.target_argmax) a.target_argmax[base + i] = am;
+    s_par[i] = a.parents[base + i];
+    s_tok[i] = a.draft_tokens[base + i];
+    s_on[i] = 0;
+  }
+  __syncthreads();
+  if (tid == 0) counters[b] = 0u;  // every workgroup of this call has arrived
+
+  int bad = 0;
+  for (int i = tid; i < N; i += kThreads) {
+    const int p = s_par[i];
+    if (i == 0 ? p != -1 : (p < 0 || p >= i)) bad |= TV_DEV_BAD_TREE;
+    if (i > 0 && (s_tok[i] < 0 || s_tok[i] >= V)) bad |= TV_DEV_BAD_TOKEN;
+  }
+  if (bad) atomicOr(&s_bad, bad);
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0) report(a.dev_status, s_bad);
+    for (int i = tid; i < N; i += kThreads) a.accepted_nodes[base + i] = (i == 0) ? 0 : -1;
+    if (tid == 0) {
+      a.accept_len[b] = 0;
+      a.bonus_token[b] = s_am[0];
+    }
+    return;
+  }
+
+  // node i is reachable iff every edge on its root path is accepted
+  for (int i = tid; i < N; i += kThreads) {
+    int c = i, d = 0, ok = 1;
+    while (c != 0) {
+      const int p = s_par[c];
+      if (s_tok[c] != s_am[p]) { ok = 0; break; }
+      c = p;
+      ++d;
+    }
+    s_ok[i] = ok;
+    s_dep[i] = d;
+    if (ok) atomicMax(&s_dmax, d);
+  }
+  __syncthreads();
+  const int dmax = s_dmax;
+  // mark every node on some deepest accepted path
+  for (int i = tid; i < N; i += kThreads) {
+    if (s_ok[i] && s_dep[i] == dmax) {
+      int c = i;
+      s_on[c] = 1;
+      while (c != 0) {
+        c = s_par[c];
+        s_on[c] = 1;
+      }
+    }
+  }
+  __syncthreads();
+  // descend from the root, taking the lowest-index marked child each step
+  if (wave == 0) {
+    int cur = 0;
+    if (lane == 0) s_path[0] = 0;
+    for (int k = 1; k <= dmax; ++k) {
+      int next = -1;
+      for (int c0 = cur + 1; c0 < N && next < 0; c0 += 64) {
+        const int c = c0 + lane;
+        const bool hit = c < N && s_par[c] == cur && s_on[c];
+        const uint64_t m = __ballot(hit);
+        if (m) next = c0 + __builtin_ctzll(m);
+      }
+      if (next >= 0) cur = next;  // always found: a marked node's parent is marked
+      if (lane == 0) s_path[k] = cur;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < N; i += kThreads) a.accepted_nodes[base + i] = (i <= dmax) ? s_path[i] : -1;
+  if (tid == 0) {
+    a.accept_len[b] = dmax;
+    a.bonus_token[b] = s_am[s_path[dmax]];
+  }
+}
+
+}  // namespace
+
+size_t accept_workspace_bytes(int B, int N, int V) {
+  const Split s = split_for(B, N, V);
+  const size_t head = (static_cast<size_t>(B) * 4 + 255) & ~size_t(255);
+  return head + static_cast<size_t>(B) * N * s.chunks * sizeof(uint64_t);
+}
+
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
+  const Split s = split_for(a.B, a.N, a.V);
+  const long blocks = static_cast<long>(a.B) * a.N * s.chunks;
+  hipLaunchKernelGGL(accept_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, a,
+                     s.chunk, s.chunks);
+  return hipGetLastError();
+}
+
+}  // namespace tv

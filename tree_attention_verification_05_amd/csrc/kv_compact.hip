@@ -1,0 +1,86 @@
+// In-place compaction of the accepted path's K/V rows ("EAGLE代码实现原理",
+// KV缓存优化: copy(indices, prev_length) selects the indexed rows and copies
+// them to the rows from prev_length; "P-EAGLE", 技术难点和解决方案: the cache is
+// rolled back to the accepted tokens).
+//
+// One workgroup per sequence.  Each thread owns 16-byte columns of a cache row
+// (K and V, every KV head) and walks the path in ascending order, reading the
+// source row before writing the destination.  For a strictly increasing path
+// with path[j] >= j, a destination j is never the source of a later step, and
+// the source path[j] of step j is rewritten (as destination) only by the later
+// step j' = path[j], whose store follows this thread's load of it; so the
+// in-order walk gives the same bytes as gathering every source first.
+#include "tv_internal.h"
+
+namespace tv {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void kv_compact_kernel(CompactArgs a) {
+  __shared__ int s_src[TV_MAX_NODES];  // cache row of the source of step j
+  __shared__ int s_dst[TV_MAX_NODES];  // cache row of the destination of step j
+  __shared__ int s_bad, s_L;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int N = a.N;
+  const int32_t* table = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+  const int32_t* path = a.accepted_nodes + static_cast<size_t>(b) * N;
+  const int P = a.prefix_lens[b];
+  const int L = a.accept_len[b] + 1;
+  if (tid == 0) {
+    s_bad = 0;
+    s_L = L;
+  }
+  __syncthreads();
+  int bad = 0;
+  if (L < 1 || L > N) bad |= TV_DEV_BAD_TREE;
+  if (P < 0 || static_cast<long>(P) + N > static_cast<long>(a.max_blocks) * kBlockSize) bad |= TV_DEV_BAD_CACHE;
+  if (!bad) {
+    for (int j = tid; j < L; j += kThreads) {
+      const int pj = path[j];
+      const bool inc = (j == 0) ? (pj == 0) : (pj > path[j - 1] && pj < N);
+      if (!inc) {
+        bad |= TV_DEV_BAD_TREE;
+        continue;
+      }
+      const int ts = P + pj, td = P + j;
+      const int bs = table[ts / kBlockSize], bd = table[td / kBlockSize];
+      if (bs < 0 || bs >= a.num_blocks || bd < 0 || bd >= a.num_blocks) {
+        bad |= TV_DEV_BAD_CACHE;
+        continue;
+      }
+      s_src[j] = bs * kBlockSize + ts % kBlockSize;
+      s_dst[j] = bd * kBlockSize + td % kBlockSize;
+    }
+  }
+  if (bad) atomicOr(&s_bad, bad);
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0) report(a.dev_status, s_bad);
+    return;
+  }
+  if (tid == 0 && a.new_lens) a.new_lens[b] = P + L;
+
+  // 16-byte columns per cache row (one row = Hkv * D elements)
+  const int cols = a.Hkv * a.D * a.elt_bytes / 16;
+  for (int c = tid; c < 2 * cols; c += kThreads) {
+    int4* base = reinterpret_cast<int4*>(c < cols ? a.k_cache : a.v_cache);
+    const int col = c < cols ? c : c - cols;
+    for (int j = 1; j < s_L; ++j) {
+      const int sr = s_src[j], dr = s_dst[j];
+      if (sr == dr) continue;
+      const int4 v = base[static_cast<size_t>(sr) * cols + col];
+      base[static_cast<size_t>(dr) * cols + col] = v;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_compact(const CompactArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(kv_compact_kernel, dim3(a.B), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tv

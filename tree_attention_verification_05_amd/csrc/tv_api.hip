@@ -1,0 +1,157 @@
+// Host side of the C ABI declared in tv.h: argument checks, workspace sizing
+// and kernel launches on the caller's stream.  Nothing here allocates or
+// keeps state between calls.
+#include <math.h>
+
+#include "tv_internal.h"
+
+using namespace tv;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+tv_status launched(hipError_t e) { return e == hipSuccess ? TV_OK : TV_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tv_status_string(tv_status s) {
+  switch (s) {
+    case TV_OK: return "TV_OK";
+    case TV_ERR_NULL: return "TV_ERR_NULL: a required pointer is NULL";
+    case TV_ERR_SHAPE: return "TV_ERR_SHAPE: sizes are inconsistent or out of range";
+    case TV_ERR_DTYPE: return "TV_ERR_DTYPE: dtype must be TV_F32 or TV_BF16";
+    case TV_ERR_UNSUPPORTED: return "TV_ERR_UNSUPPORTED: D must be 64 or 128 and block_size 16";
+    case TV_ERR_ALIGN: return "TV_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    case TV_ERR_WORKSPACE: return "TV_ERR_WORKSPACE: workspace missing or too small";
+    case TV_ERR_LAUNCH: return "TV_ERR_LAUNCH: kernel launch failed";
+  }
+  return "unknown tv_status";
+}
+
+int tv_version(void) { return 100; }
+
+tv_status tv_build_tree_mask(const int32_t* parents, int32_t B, int32_t N, uint64_t* mask,
+                             int32_t* depth, int32_t* dev_status, hipStream_t stream) {
+  if (!parents || !mask) return TV_ERR_NULL;
+  if (B <= 0 || N <= 0 || N > TV_MAX_NODES) return TV_ERR_SHAPE;
+  return launched(launch_tree_mask(parents, B, N, mask, depth, dev_status, stream));
+}
+
+size_t tv_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t max_prefix_len, tv_dtype dtype) {
+  if (dtype != TV_BF16 || B <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
+      max_prefix_len < 0 || (D != 64 && D != 128))
+    return 0;
+  return attention_mfma_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len);
+}
+
+tv_status tv_tree_attention(const void* q, const void* k_cache, const void* v_cache,
+                            int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                            int32_t block_size, const int32_t* prefix_lens, int32_t max_prefix_len,
+                            const uint64_t* mask, void* out, int32_t B, int32_t N, int32_t Hq,
+                            int32_t Hkv, int32_t D, float scale, tv_dtype dtype, void* workspace,
+                            size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !prefix_lens || !mask || !out) return TV_ERR_NULL;
+  if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
+  if (B <= 0 || N <= 0 || N > TV_MAX_NODES || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
+      num_blocks <= 0 || max_blocks <= 0 || max_prefix_len < 0)
+    return TV_ERR_SHAPE;
+  if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
+  if (block_size != kBlockSize) return TV_ERR_UNSUPPORTED;
+  if (static_cast<long>(max_prefix_len) + N > static_cast<long>(max_blocks) * block_size)
+    return TV_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return TV_ERR_ALIGN;
+  const size_t need = tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return TV_ERR_WORKSPACE;
+
+  AttnArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = num_blocks;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.prefix_lens = prefix_lens;
+  a.max_prefix_len = max_prefix_len;
+  a.mask = mask;
+  a.out = out;
+  a.B = B;
+  a.N = N;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.scale = scale > 0.f ? scale : 1.f / sqrtf(static_cast<float>(D));
+  a.workspace = workspace;
+  a.dev_status = dev_status;
+  if (dtype == TV_BF16) return launched(launch_attention_mfma(a, stream));
+  return launched(launch_attention_rowwave(a, dtype, stream));
+}
+
+size_t tv_accept_greedy_workspace_size(int32_t B, int32_t N, int32_t V) {
+  if (B <= 0 || N <= 0 || V <= 0) return 0;
+  return accept_workspace_bytes(B, N, V);
+}
+
+tv_status tv_accept_greedy(const float* logits, const int32_t* draft_tokens, const int32_t* parents,
+                           int32_t B, int32_t N, int32_t V, int32_t* accept_len,
+                           int32_t* accepted_nodes, int32_t* bonus_token, int32_t* target_argmax,
+                           void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                           hipStream_t stream) {
+  if (!logits || !draft_tokens || !parents || !accept_len || !accepted_nodes || !bonus_token)
+    return TV_ERR_NULL;
+  if (B <= 0 || N <= 0 || N > TV_MAX_NODES || V <= 0) return TV_ERR_SHAPE;
+  if (!aligned16(logits)) return TV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < accept_workspace_bytes(B, N, V)) return TV_ERR_WORKSPACE;
+  AcceptArgs a;
+  a.logits = logits;
+  a.draft_tokens = draft_tokens;
+  a.parents = parents;
+  a.B = B;
+  a.N = N;
+  a.V = V;
+  a.accept_len = accept_len;
+  a.accepted_nodes = accepted_nodes;
+  a.bonus_token = bonus_token;
+  a.target_argmax = target_argmax;
+  a.workspace = workspace;
+  a.dev_status = dev_status;
+  return launched(launch_accept(a, stream));
+}
+
+tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks, const int32_t* block_table,
+                        int32_t max_blocks, int32_t block_size, const int32_t* prefix_lens,
+                        const int32_t* accepted_nodes, const int32_t* accept_len, int32_t B,
+                        int32_t N, int32_t Hkv, int32_t D, tv_dtype dtype, int32_t* new_lens,
+                        int32_t* dev_status, hipStream_t stream) {
+  if (!k_cache || !v_cache || !block_table || !prefix_lens || !accepted_nodes || !accept_len)
+    return TV_ERR_NULL;
+  if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
+  if (B <= 0 || N <= 0 || N > TV_MAX_NODES || Hkv <= 0 || num_blocks <= 0 || max_blocks <= 0)
+    return TV_ERR_SHAPE;
+  if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
+  if (block_size != kBlockSize) return TV_ERR_UNSUPPORTED;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return TV_ERR_ALIGN;
+  CompactArgs a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = num_blocks;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.prefix_lens = prefix_lens;
+  a.accepted_nodes = accepted_nodes;
+  a.accept_len = accept_len;
+  a.B = B;
+  a.N = N;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.elt_bytes = dtype == TV_F32 ? 4 : 2;
+  a.new_lens = new_lens;
+  a.dev_status = dev_status;
+  return launched(launch_kv_compact(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of libtv (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tv.h"
+
+namespace tv {
+
+constexpr int kBlockSize = 16;   // tokens per paged-cache block
+
+// ---- bf16 helpers (storage is the raw 16-bit pattern) ----
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+// round to nearest even; inputs are finite
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
+};
+template <> struct Elt<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+__device__ __forceinline__ void report(int32_t* dev_status, int bits) {
+  if (dev_status) atomicOr(dev_status, bits);
+}
+
+// ---- launchers (each defined in its kernel translation unit) ----
+hipError_t launch_tree_mask(const int32_t* parents, int B, int N, uint64_t* mask, int32_t* depth,
+                            int32_t* dev_status, hipStream_t stream);
+
+struct AttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  int num_blocks;
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* prefix_lens;
+  int max_prefix_len;
+  const uint64_t* mask;
+  void* out;
+  int B, N, Hq, Hkv, D;
+  float scale;
+  void* workspace;
+  int32_t* dev_status;
+};
+
+// fp32 path: one wavefront per (sequence, node, query head) row.
+hipError_t launch_attention_rowwave(const AttnArgs& a, tv_dtype dtype, hipStream_t stream);
+
+// bf16 path: matrix-core split-KV kernel (+ split merge when the key range is split).
+size_t attention_mfma_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int max_prefix_len);
+hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
+
+struct AcceptArgs {
+  const float* logits;
+  const int32_t* draft_tokens;
+  const int32_t* parents;
+  int B, N, V;
+  int32_t* accept_len;
+  int32_t* accepted_nodes;
+  int32_t* bonus_token;
+  int32_t* target_argmax;
+  void* workspace;
+  int32_t* dev_status;
+};
+size_t accept_workspace_bytes(int B, int N, int V);
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+
+struct CompactArgs {
+  void* k_cache;
+  void* v_cache;
+  int num_blocks;
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* prefix_lens;
+  const int32_t* accepted_nodes;
+  const int32_t* accept_len;
+  int B, N, Hkv, D;
+  int elt_bytes;
+  int32_t* new_lens;
+  int32_t* dev_status;
+};
+hipError_t launch_kv_compact(const CompactArgs& a, hipStream_t stream);
+
+}  // namespace tv
