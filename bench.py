@@ -1,0 +1,320 @@
+"""Throughput of one verification step on one GPU.
+
+A step is one pass of the whole path over one batch: tree mask, tree-masked
+attention over the paged prefix, greedy acceptance over the target logits,
+and KV compaction of the accepted paths, each one libtv call on the current
+stream.  Inputs are synthetic (seeded) and resident in HBM before timing.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+Prints ONE JSON line.  `value` is verified tree tokens per second
+(B * N / mean step time).  Before every timed step a 1 GiB read+write flush
+evicts the 256 MB Infinity Cache and the L2 (outside the step's events), so
+every step reads its inputs from HBM.  Compaction rewrites the tree slots in
+place; later steps move the same number of rows, so the work per step is
+unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified tree-tokens/s + achieved HBM GB/s / MFMA util, Llama-3-8B-shape layer"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "tree_attention_verification_05_amd", "csrc")
+KERNEL_SOURCES = {
+    "tv_tree_attention": ["attn_mfma.hip"],
+    "tv_accept_greedy": ["accept.hip"],
+    "tv_kv_compact": ["kv_compact.hip"],
+    "tv_build_tree_mask": ["tree_mask.hip"],
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="workload 1..5 (default 2: Llama-3-8B-shaped layer, EAGLE-2 60-node tree)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--oracle-seconds", type=float, default=12.0,
+                    help="host time budget of the CPU-oracle baseline (0 disables it)")
+    ap.add_argument("--no-flush", action="store_true", help="do not flush caches between steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (for counter calibration under a profiler)")
+    return ap.parse_args()
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+RIDGE_FLOP_PER_BYTE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+
+def step_work(w, accept_len, accepted_nodes):
+    """Algorithmic bytes (and flops) each call moves for this batch: what the
+    method must read or write at least, with every K/V row of a KV head read
+    once for all its nodes and query heads.  The compaction count comes from
+    the accepted paths of the step."""
+    import numpy as np
+    s = w.spec
+    B, N = s.B, s.N
+    elt = 2 if s.dtype == "bf16" else 4
+    Wd = (N + 63) // 64
+    P = w.prefix_lens.astype(np.int64)
+    depth = np.zeros((B, N), np.int64)
+    rows = np.arange(B)
+    for i in range(1, N):
+        depth[:, i] = depth[rows, w.parents[:, i]] + 1
+    nblk = (P + N + s.block_size - 1) // s.block_size
+    kv_bytes = int((2 * (P + N) * s.Hkv * s.D * elt).sum())
+    qo_bytes = 2 * B * N * s.Hq * s.D * elt
+    attn_bytes = kv_bytes + qo_bytes + B * N * Wd * 8 + int(nblk.sum()) * 4 + B * 4
+    attn_flops = int(4 * s.D * s.Hq * (N * P + (depth + 1).sum(axis=1)).sum())
+    moved = 0
+    for b in range(B):
+        L = int(accept_len[b]) + 1
+        path = accepted_nodes[b, :L]
+        moved += int((path != np.arange(L)).sum())
+    row_bytes = s.Hkv * s.D * elt
+    return {
+        "tv_build_tree_mask": {"bytes": B * N * (4 + 8 * Wd + 4)},
+        "tv_tree_attention": {"bytes": attn_bytes, "flops": attn_flops,
+                              "bound": "mfma" if attn_flops / attn_bytes > RIDGE_FLOP_PER_BYTE
+                              else "hbm"},
+        "tv_accept_greedy": {"bytes": B * N * s.V * 4 + B * N * 4 * 3 + B * (N + 2) * 4},
+        "tv_kv_compact": {"bytes": moved * 2 * 2 * row_bytes + B * (N + 3) * 4},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no "
+              "multi-GPU path; the per-GPU shard runs as --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tree_attention_verification_05_amd as T
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.make_config(args.config, seed=args.seed)
+    spec = w.spec
+    B, N, V = spec.B, spec.N, spec.V
+
+    q, k, v = w.q.to(dev), w.k_cache.to(dev), w.v_cache.to(dev)
+    table = torch.from_numpy(w.block_table).to(dev)
+    prefix = torch.from_numpy(w.prefix_lens).to(dev)
+    parents = torch.from_numpy(w.parents).to(dev)
+    draft = torch.from_numpy(w.draft_tokens).to(dev)
+    logits = w.logits.to(dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    Wd = (N + 63) // 64
+    mask = torch.empty((B, N, Wd), dtype=torch.int64, device=dev)
+    depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    dt = T.TV_BF16 if q.dtype == torch.bfloat16 else T.TV_F32
+    ws_bytes = T.tv_tree_attention_workspace_size(B, N, spec.Hq, spec.Hkv, spec.D,
+                                                  w.max_prefix_len, dt)
+    attn_ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    acc_len = torch.empty(B, dtype=torch.int32, device=dev)
+    acc_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+    bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    am = torch.empty((B, N), dtype=torch.int32, device=dev)
+    new_lens = torch.empty(B, dtype=torch.int32, device=dev)
+    acc_ws = torch.zeros(max(int(T.lib.tv_accept_greedy_workspace_size(B, N, V)), 16),
+                         dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else torch.empty(256 * 1024 * 1024, dtype=torch.float32,
+                                                   device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run_step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        T.tv_build_tree_mask(parents, mask=mask, depth=depth, dev_status=status)
+        if ev is not None:
+            ev[1].record(stream)
+        T.tv_tree_attention(q, k, v, table, prefix, w.max_prefix_len, mask, out=out,
+                            workspace=attn_ws, dev_status=status)
+        if ev is not None:
+            ev[2].record(stream)
+        T.tv_accept_greedy(logits, draft, parents, accept_len=acc_len, accepted_nodes=acc_nodes,
+                           bonus_token=bonus, target_argmax=am, workspace=acc_ws,
+                           dev_status=status)
+        if ev is not None:
+            ev[3].record(stream)
+        T.tv_kv_compact(k, v, table, prefix, acc_nodes, acc_len, new_lens=new_lens,
+                        dev_status=status)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())} on generated inputs")
+
+    # ---- timed region: K steps, each preceded by a cache flush outside its events ----
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for s in range(args.steps):
+        if flush is not None:
+            flush.add_(1.0)
+        run_step(evs[s])
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    per = np.array([[evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(4)]
+                    for s in range(args.steps)])  # ms
+    step_ms = np.array([evs[s][0].elapsed_time(evs[s][4]) for s in range(args.steps)])
+    ms_per_step = float(step_ms.mean())
+
+    # back-to-back steps with warm caches, for reference
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        run_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / args.steps
+
+    if args.copy_calibration:
+        src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    names = ["tv_build_tree_mask", "tv_tree_attention", "tv_accept_greedy", "tv_kv_compact"]
+    work = step_work(w, acc_len.cpu().numpy(), acc_nodes.cpu().numpy())
+    kern = {}
+    for j, n in enumerate(names):
+        t_us = float(per[:, j].mean()) * 1e3
+        byt = work[n]["bytes"]
+        kern[n] = {"us": round(t_us, 3), "bytes": int(byt),
+                   "GB_s": round(byt / (t_us * 1e-6) / 1e9, 1)}
+        if work[n].get("flops"):
+            kern[n]["flops"] = int(work[n]["flops"])
+            kern[n]["TFLOP_s"] = round(work[n]["flops"] / (t_us * 1e-6) / 1e12, 2)
+
+    # roofline of the dominant call
+    dom = max(names, key=lambda n: kern[n]["us"])
+    d_us = kern[dom]["us"]
+    bound = work[dom].get("bound", "hbm")
+    if bound == "mfma":
+        achieved = work[dom]["flops"] / (d_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    else:
+        achieved = work[dom]["bytes"] / (d_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = dom
+    roof["traffic"] = measured_traffic(dom, spec.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(B * N / (ms_per_step * 1e-3), 1),
+        "unit": "tree-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == T.TV_BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": B, "tree_nodes": N, "q_heads": spec.Hq,
+                   "kv_heads": spec.Hkv, "head_dim": spec.D, "vocab": V,
+                   "prefix_len": [int(w.prefix_lens.min()), int(w.prefix_lens.max())],
+                   "block_size": spec.block_size, "cache_flushed_between_steps": flush is not None},
+        "roofline": roof,
+        "kernels": kern,
+        "warm_cache_ms_per_step": round(warm_ms, 5),
+        "wall_s_timed_region": round(t_wall, 4),
+        "mean_accept_len": float(acc_len.float().mean().item()),
+    }
+    if args.oracle_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(w, args.oracle_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed counter runs, if they were taken on
+    the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"{kernel}__{workload}__traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_digest(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float):
+    """The CPU oracle (test infrastructure, float64 NumPy) timed on this host
+    over whole steps of the same workload, as many as fit the time budget."""
+    import numpy as np
+
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    q = w.q.float().numpy()
+    kf = w.k_cache.float().numpy()
+    vf = w.v_cache.float().numpy()
+    k16 = w.k_cache.view(dtype=__import__("torch").int16).numpy()
+    v16 = w.v_cache.view(dtype=__import__("torch").int16).numpy()
+    lg = w.logits.numpy()
+    B = w.B
+    seqs_all = list(range(B))
+    done_tokens = 0
+    done_steps = 0
+    seq_cursor = 0
+    t0 = time.perf_counter()
+    # whole steps when they fit; otherwise one sequence at a time (the oracle
+    # treats sequences independently), until the budget is spent
+    while time.perf_counter() - t0 < seconds:
+        seqs = [seqs_all[seq_cursor % B]]
+        seq_cursor += 1
+        O.build_tree_mask(w.parents[seqs])
+        O.tree_attention(q, kf, vf, w.block_table, w.prefix_lens, w.parents, seqs=seqs)
+        acc = O.accept_greedy(lg[seqs], w.draft_tokens[seqs], w.parents[seqs])
+        O.kv_compact(k16, v16, w.block_table[seqs], w.prefix_lens[seqs], acc["accepted_nodes"],
+                     acc["accept_len"])
+        done_tokens += w.N * len(seqs)
+        done_steps += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done_tokens / el, 2), "unit": "tree-tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done_steps} single-sequence passes (mask, attention, acceptance, "
+                      f"compaction) of the same workload in {el:.1f} s, float64 NumPy",
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -144,9 +144,9 @@ TV_API tv_status tv_tree_attention(const void* q, const void* k_cache, const voi
                             size_t workspace_bytes, int32_t* dev_status, hipStream_t stream);
 
 /*
- * Workspace bytes tv_accept_greedy needs.  The workspace must be zero-filled
- * before its first use; every call leaves it zero-filled again when its
- * kernel ends.  Calls that share one workspace must be ordered (same stream).
+ * Workspace bytes tv_accept_greedy needs (per-chunk partial maxima).  The
+ * workspace needs no initialisation; calls that share one workspace must be
+ * ordered (same stream).
  */
 TV_API size_t tv_accept_greedy_workspace_size(int32_t B, int32_t N, int32_t V);
 

@@ -73,7 +73,7 @@ def check_attention(gpu_out: torch.Tensor, ref: np.ndarray, seqs, dtype):
     for b in seqs:
         diff = np.abs(g[b] - ref[b])
         bound = atol + rtol * np.abs(ref[b])
-        bad = diff > bound
+        bad = ~(diff <= bound)  # NaN anywhere counts as a failure
         if bad.any():
             idx = np.argwhere(bad)[0]
             raise AssertionError(

@@ -3,15 +3,15 @@
 // token at once, drafts are accepted while they agree with it; "vLLM EAGLE
 // 投机解码实战", 无损性保障: greedy speculative decoding equals greedy decoding.)
 //
-// Phase 1 (every workgroup): one chunk of one logits row is scanned with
-// 16-byte loads; the chunk's best (value, index) is packed into a 64-bit key
-// that orders by value and then by lower index, and stored in the workspace.
-// Phase 2 (the last workgroup of each sequence to finish, found with a
-// per-sequence arrival counter): reduce the chunk keys of the sequence's N
-// rows to the target argmax, validate the tree and draft tokens, and find the
-// longest accepted path (smallest node sequence among equals).  That
-// workgroup also resets the counter and the chunk keys it consumed, so the
-// whole workspace is zero again on exit, whatever sizes the next call uses.
+// Scan kernel (rows x chunks workgroups): one chunk of one logits row is read
+// with 16-byte loads, four in flight per thread; the chunk's best (value,
+// index) is packed into a 64-bit key that orders by value and then by lower
+// index, and stored in the workspace.  No atomics and no fences: the kernel
+// boundary orders the keys before their use.
+// Walk kernel (one workgroup per sequence): reduce the chunk keys of the
+// sequence's N rows to the target argmax, validate the tree and the draft
+// tokens, and find the longest accepted path (smallest node sequence among
+// equals).  The workspace needs no initialisation.
 #include "tv_internal.h"
 
 namespace tv {
@@ -62,45 +62,51 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-__global__ __launch_bounds__(kThreads) void accept_kernel(AcceptArgs a, int chunk, int chunks) {
+__global__ __launch_bounds__(kThreads) void accept_scan_kernel(const float* __restrict__ logits,
+                                                               int V, int chunk, int chunks,
+                                                               uint64_t* __restrict__ keys) {
   __shared__ uint64_t wbest[kThreads / 64];
-  __shared__ int s_last;
-  __shared__ int s_par[TV_MAX_NODES], s_tok[TV_MAX_NODES], s_am[TV_MAX_NODES];
-  __shared__ int s_ok[TV_MAX_NODES], s_dep[TV_MAX_NODES], s_on[TV_MAX_NODES];
-  __shared__ int s_bad, s_dmax, s_path[TV_MAX_NODES];
-
-  const int N = a.N, V = a.V;
-  const long row = blockIdx.x / chunks;  // global row b*N + i
+  const long row = blockIdx.x / chunks;
   const int ch = blockIdx.x % chunks;
-  const int b = static_cast<int>(row / N);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  uint32_t* counters = static_cast<uint32_t*>(a.workspace);
-  uint64_t* keys = reinterpret_cast<uint64_t*>(static_cast<char*>(a.workspace) +
-                                               ((static_cast<size_t>(a.B) * 4 + 255) & ~size_t(255)));
-
-  // ---- phase 1: best (value, lowest index) of this chunk ----
   const int lo = ch * chunk;
   const int hi = min(V, lo + chunk);
-  const float* x = a.logits + row * V;
+  const float* x = logits + row * V;
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
   if ((V & 3) == 0) {
-    // 16-byte loads; each thread visits increasing indices, so strict '>'
-    // keeps the first occurrence of its maximum
+    // four independent 16-byte loads in flight, then compared in index order
+    // (each thread visits increasing indices, so strict '>' keeps the first
+    // occurrence of its maximum)
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
-    for (int j = lo / 4 + tid; j < hi / 4; j += kThreads) {
-      const f32x4 v = __builtin_nontemporal_load(x4 + j);
-      if (v.x > bv || bi == 0x7FFFFFFF) { bv = v.x; bi = 4 * j; }
-      if (v.y > bv) { bv = v.y; bi = 4 * j + 1; }
-      if (v.z > bv) { bv = v.z; bi = 4 * j + 2; }
-      if (v.w > bv) { bv = v.w; bi = 4 * j + 3; }
+    const int lo4 = lo / 4, hi4 = hi / 4;
+    for (int j0 = lo4 + tid; j0 < hi4; j0 += 4 * kThreads) {
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * kThreads;
+        v[u] = j < hi4 ? __builtin_nontemporal_load(x4 + j) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * kThreads;
+        if (j >= hi4) break;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (v[u][e] > bv || bi == 0x7FFFFFFF) {
+            bv = v[u][e];
+            bi = 4 * j + e;
+          }
+      }
     }
   } else {
     for (int j = lo + tid; j < hi; j += kThreads) {
       const float v = x[j];
-      if (v > bv || bi == 0x7FFFFFFF) { bv = v; bi = j; }
+      if (v > bv || bi == 0x7FFFFFFF) {
+        bv = v;
+        bi = j;
+      }
     }
   }
   uint64_t key = (bi == 0x7FFFFFFF) ? 0ull : make_key(bv, bi);
@@ -111,29 +117,30 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptArgs a, int chun
     uint64_t k = wbest[0];
     for (int w = 1; w < kThreads / 64; ++w) k = wbest[w] > k ? wbest[w] : k;
     keys[row * chunks + ch] = k;
-    __threadfence();
-    const uint32_t arrived = atomicAdd(&counters[b], 1u);
-    s_last = (arrived == static_cast<uint32_t>(N) * chunks - 1u);
   }
-  __syncthreads();
-  if (!s_last) return;
+}
 
-  // ---- phase 2: this workgroup is the last of sequence b ----
-  __threadfence();
+__global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int chunks) {
+  __shared__ int s_par[TV_MAX_NODES], s_tok[TV_MAX_NODES], s_am[TV_MAX_NODES];
+  __shared__ int s_ok[TV_MAX_NODES], s_dep[TV_MAX_NODES], s_on[TV_MAX_NODES];
+  __shared__ int s_bad, s_dmax, s_path[TV_MAX_NODES];
+
+  const int N = a.N, V = a.V;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t* keys = static_cast<const uint64_t*>(a.workspace);
   if (tid == 0) {
     s_bad = 0;
     s_dmax = 0;
   }
   const size_t base = static_cast<size_t>(b) * N;
   for (int i = tid; i < N; i += kThreads) {
-    uint64_t* kr = keys + (base + i) * chunks;
-    uint64_t k = __builtin_nontemporal_load(kr);
+    const uint64_t* kr = keys + (base + i) * chunks;
+    uint64_t k = kr[0];
     for (int c = 1; c < chunks; ++c) {
-      const uint64_t w = __builtin_nontemporal_load(kr + c);
+      const uint64_t w = kr[c];
       k = w > k ? w : k;
     }
-    // leave the workspace zero-filled for the next call, whatever its sizes
-    for (int c = 0; c < chunks; ++c) kr[c] = 0ull;
     const int am = key_index(k);
     s_am[i] = am;
     if (a.target_argmax) a.target_argmax[base + i] = am;
@@ -142,7 +149,6 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptArgs a, int chun
     s_on[i] = 0;
   }
   __syncthreads();
-  if (tid == 0) counters[b] = 0u;  // every workgroup of this call has arrived
 
   int bad = 0;
   for (int i = tid; i < N; i += kThreads) {
@@ -217,15 +223,17 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptArgs a, int chun
 
 size_t accept_workspace_bytes(int B, int N, int V) {
   const Split s = split_for(B, N, V);
-  const size_t head = (static_cast<size_t>(B) * 4 + 255) & ~size_t(255);
-  return head + static_cast<size_t>(B) * N * s.chunks * sizeof(uint64_t);
+  return static_cast<size_t>(B) * N * s.chunks * sizeof(uint64_t);
 }
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
   const Split s = split_for(a.B, a.N, a.V);
   const long blocks = static_cast<long>(a.B) * a.N * s.chunks;
-  hipLaunchKernelGGL(accept_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, a,
-                     s.chunk, s.chunks);
+  hipLaunchKernelGGL(accept_scan_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     stream, a.logits, a.V, s.chunk, s.chunks, static_cast<uint64_t*>(a.workspace));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(accept_walk_kernel, dim3(a.B), dim3(kThreads), 0, stream, a, s.chunks);
   return hipGetLastError();
 }
 

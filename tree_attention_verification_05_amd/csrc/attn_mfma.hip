@@ -7,19 +7,21 @@
 // Work unit: one workgroup per (sequence b, KV head kh, key split s, row
 // chunk).  The query rows of a KV head are its g = Hq/Hkv heads times the N
 // tree nodes (row r = node * g + head-in-group), so one K/V tile read from HBM
-// serves every node and every query head of the group.  Each wave owns QB
-// blocks of 32 rows.
+// serves every node and every query head of the group.  Each of the NW waves
+// owns 32 rows (waves past the last row only help load tiles).
 //
-// Per 64-key tile (double-buffered in LDS, next tile prefetched into
-// registers while the current one is computed):
+// Per 64-key tile (double-buffered in LDS; the next tile is prefetched into
+// registers while the current one is computed; the block ids of the tile
+// after that are already in scalar registers), one 32-key half at a time:
 //   S^T (keys x rows)   = K (keys x D)   * Q^T (D x rows)   v_mfma_f32_32x32x16_bf16
 //   O^T (D x rows)     += V^T (D x keys) * P^T (keys x rows) v_mfma_f32_32x32x16_bf16
 // In the transposed form every accumulator a lane holds belongs to one query
-// row (lane % 32), so the softmax rescaling is a per-lane scalar, and the
-// score accumulators are already in the B-operand layout of the PV product
-// (the MFMA contraction order of the keys is permuted identically in both
-// operands).  Lanes l and l+32 share a row and split its keys; they exchange
-// the tile maximum once per tile and their denominators once at the end.
+// row (lane % 32), so softmax rescaling is a per-lane scalar, and the score
+// accumulators are already in the B-operand layout of the PV product (the
+// MFMA contraction order of the keys is permuted identically in both
+// operands).  Lanes l and l+32 share a row and split its keys; they combine
+// their tile maxima with one v_permlane32_swap per tile and their
+// denominators once at the end.
 //
 // LDS layouts (bf16 elements):
 //   K  [key][D], 16-byte chunk c of key k stored at chunk c ^ (k % 8)
@@ -28,10 +30,14 @@
 // Both swizzles make the loader's writes and the MFMA operand reads free of
 // bank conflicts.
 //
-// Softmax: scores are kept raw; exponentials use exp2 with the factor
-// scale*log2(e) folded into one FMA.  Prefix tiles need no mask; tiles that
-// reach the tree slots apply the node's ancestor bitmask.  With several key
-// splits, each split writes (max, denominator, unnormalised output) in fp32
+// Softmax: scores stay raw; p = exp2(s * scale*log2(e) - m) with one FMA and
+// one v_exp_f32.  The running maximum m is only raised when a row's new tile
+// maximum exceeds it by more than 2^8 (so p <= 256 otherwise); rescaling the
+// output accumulators is then rare and happens under a wave-uniform branch.
+// The result is the same softmax: numerator and denominator use the same m.
+// Prefix tiles need no mask; tiles that reach the tree slots select -inf for
+// keys outside the row's ancestor set (branch-free).  With several key
+// splits, each split writes (m, denominator, unnormalised output) in fp32
 // and a second kernel merges them with the log-sum-exp rule.
 #include "tv_internal.h"
 
@@ -39,37 +45,57 @@ namespace tv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTile = 64;  // keys per tile
+constexpr int kTile = 64;             // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyRescale = 8.0f;  // log2 units a row maximum may grow before rescaling
 
-template <int D, int NW, int QB>
+template <int D, int NW>
 struct Cfg {
   static constexpr int kThreads = NW * 64;
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per key row
   static constexpr int kKUnits = kTile * kChunks;        // 16-byte loads of a K tile
   static constexpr int kVUnits = (kTile / 4) * kChunks;  // (4 keys x 16 bytes) loads of a V tile
-  static constexpr int kKPer = kKUnits / kThreads;
+  static constexpr int kKPer = (kKUnits + kThreads - 1) / kThreads;
   static constexpr int kVPer = (kVUnits + kThreads - 1) / kThreads;
   static constexpr int kKs = D / 16;  // k-steps of the QK product
   static constexpr int kDb = D / 32;  // 32-dim output blocks
   static constexpr int kStage = kTile * D * 2;  // K + Vt elements per stage
-  static constexpr int kRows = NW * QB * 32;    // rows per workgroup
-  static_assert(kKUnits % kThreads == 0, "K tile loads must divide evenly");
+  static constexpr int kRows = NW * 32;         // rows per workgroup
 };
 
 struct MfmaParams {
   int tiles_per_split;
   int nsplit;      // splits per (sequence, KV head); 1 = write the output directly
   int row_chunks;  // workgroups along the rows of one KV head
+  int waves;       // waves per workgroup (32 rows each)
 };
 
 __device__ __forceinline__ int vt_swz(int r) { return (r & 15) ^ ((r >> 3) & 15); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// v_cvt_pk_bf16_f32: round to nearest even
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// op(x[l], x[l ^ 32]) for every lane l, with one v_permlane32_swap
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Visibility of the 64 keys of the tile that starts at logical position tb,
 // for a row whose node has ancestor-or-self bits mw: bit k is set iff
@@ -90,19 +116,16 @@ __device__ __forceinline__ uint64_t tile_visibility(const uint64_t (&mw)[4], int
   return vis;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-}
-
-template <int D, int NW, int QB>
-__global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
-  using C = Cfg<D, NW, QB>;
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
+  using C = Cfg<D, NW>;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5;   // which half of the key set this lane holds
-  const int col = lane & 31;  // query row within a 32-row block
+  const int col = lane & 31;  // query row within the wave's 32 rows
 
   // blockIdx.x = ((b * Hkv + kh) * nsplit + s) * row_chunks + rc
   int idx = blockIdx.x;
@@ -123,93 +146,99 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a, MfmaPara
   }
   const int total = P + a.N;
   const int ntiles = (total + kTile - 1) / kTile;
+  const int nblk = (total + kBlockSize - 1) / kBlockSize;
   const int t0 = s * mp.tiles_per_split;
   const int t1 = min(ntiles, t0 + mp.tiles_per_split);
   if (t0 >= t1) return;  // whole workgroup: this split is past the sequence's end
 
-  const int32_t* table = a.block_table + static_cast<size_t>(b) * a.max_blocks;
-  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
-  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+  const int32_t* __restrict__ table = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v_cache);
   const float c = a.scale * kLog2e;
 
-  // ---------------- query rows of this wave (B operand of S^T) ----------------
-  const int row0 = rc * C::kRows + wave * QB * 32;
-  bf16x8 qreg[QB][C::kKs];
-  uint64_t mw[QB][4];
-  bool qactive[QB];
-#pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    const int r = row0 + q * 32 + col;
-    qactive[q] = (row0 + q * 32) < R;
-    const int rr = r < R ? r : R - 1;
+  // ---------------- this wave's 32 query rows (B operand of S^T) ----------------
+  const int row0 = rc * C::kRows + wave * 32;
+  const bool active = row0 < R;
+  const int r_me = row0 + col;
+  bf16x8 qreg[C::kKs];
+  uint64_t mw[4];
+  {
+    const int rr = r_me < R ? r_me : R - 1;
     const int node = rr / g, hg = rr % g;
     const u32x4* qp = reinterpret_cast<const u32x4*>(
         static_cast<const uint16_t*>(a.q) +
         ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D);
 #pragma unroll
-    for (int ks = 0; ks < C::kKs; ++ks) {
+    for (int kk = 0; kk < C::kKs; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (r < R) v = qp[ks * 2 + hh];
-      qreg[q][ks] = __builtin_bit_cast(bf16x8, v);
+      if (r_me < R) v = qp[kk * 2 + hh];
+      qreg[kk] = __builtin_bit_cast(bf16x8, v);
     }
     const uint64_t* mrow = a.mask + (static_cast<size_t>(b) * a.N + node) * W;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mw[q][w] = (w < W) ? mrow[w] : 0ull;
+    for (int w = 0; w < 4; ++w) mw[w] = (w < W) ? mrow[w] : 0ull;
   }
 
   // ---------------- tile loader ----------------
+  // Lane j < 4 of every wave holds the block id of table entry 4*tile + j
+  // (-1 past the sequence or for an out-of-range id); threads pick theirs
+  // with one cross-lane read.  The ids are fetched one tile ahead.
+  auto tile_blocks = [&](int tile) __attribute__((always_inline)) -> int {
+    const int e = tile * 4 + (lane & 3);
+    int v = -1;
+    if (e < nblk) {
+      v = table[e];
+      if (v < 0 || v >= a.num_blocks) {
+        report(a.dev_status, TV_DEV_BAD_CACHE);
+        v = -1;
+      }
+    }
+    return v;
+  };
+
   u32x4 kreg[C::kKPer];
   u32x4 vreg[C::kVPer][4];
 
-  auto cache_row = [&](int t, bool& ok) -> long {
-    ok = false;
-    if (t >= total) return 0;
-    const int blk = table[t >> 4];
-    if (blk < 0 || blk >= a.num_blocks) {
-      report(a.dev_status, TV_DEV_BAD_CACHE);
-      return 0;
-    }
-    ok = true;
-    return (static_cast<long>(blk) * kBlockSize + (t & 15)) * a.Hkv + kh;
-  };
-
-  auto load_tile = [&](int tile) {
+  auto load_tile = [&](int tile, int bids) __attribute__((always_inline)) {
     const int tb = tile * kTile;
 #pragma unroll
     for (int j = 0; j < C::kKPer; ++j) {
       const int u = tid + j * C::kThreads;
       const int key = u / C::kChunks, ch = u % C::kChunks;
-      bool ok;
-      const long cr = cache_row(tb + key, ok);
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *reinterpret_cast<const u32x4*>(kc + cr * D + ch * 8);
+      const int blk = __shfl(bids, (key >> 4) & 3, 64);
+      if (u < C::kKUnits && tb + key < total && blk >= 0)
+        v = *reinterpret_cast<const u32x4*>(
+            kc + ((static_cast<long>(blk) * kBlockSize + (key & 15)) * a.Hkv + kh) * D + ch * 8);
       kreg[j] = v;
     }
 #pragma unroll
     for (int j = 0; j < C::kVPer; ++j) {
       const int u = tid + j * C::kThreads;
       const int kg = u / C::kChunks, ch = u % C::kChunks;
+      const int blk = __shfl(bids, (kg >> 2) & 3, 64);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        const int key = kg * 4 + e;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (u < C::kVUnits) {
-          bool ok;
-          const long cr = cache_row(tb + kg * 4 + e, ok);
-          if (ok) v = *reinterpret_cast<const u32x4*>(vc + cr * D + ch * 8);
-        }
+        if (u < C::kVUnits && tb + key < total && blk >= 0)
+          v = *reinterpret_cast<const u32x4*>(
+              vc + ((static_cast<long>(blk) * kBlockSize + (key & 15)) * a.Hkv + kh) * D + ch * 8);
         vreg[j][e] = v;
       }
     }
   };
 
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](int stage) __attribute__((always_inline)) {
     uint16_t* ks = lds + stage * C::kStage;
     uint16_t* vt = ks + kTile * D;
 #pragma unroll
     for (int j = 0; j < C::kKPer; ++j) {
       const int u = tid + j * C::kThreads;
-      const int key = u / C::kChunks, ch = u % C::kChunks;
-      *reinterpret_cast<u32x4*>(ks + key * D + ((ch ^ (key & 7)) * 8)) = kreg[j];
+      if (u < C::kKUnits) {
+        const int key = u / C::kChunks, ch = u % C::kChunks;
+        *reinterpret_cast<u32x4*>(ks + key * D + ((ch ^ (key & 7)) * 8)) = kreg[j];
+      }
     }
 #pragma unroll
     for (int j = 0; j < C::kVPer; ++j) {
@@ -222,10 +251,10 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a, MfmaPara
           const uint32_t w0 = vreg[j][0][m], w1 = vreg[j][1][m];
           const uint32_t w2 = vreg[j][2][m], w3 = vreg[j][3][m];
           u32x2 even, odd;
-          even[0] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-          even[1] = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
-          odd[0] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
-          odd[1] = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
+          even[0] = (w0 & 0xFFFFu) | (w1 << 16);
+          even[1] = (w2 & 0xFFFFu) | (w3 << 16);
+          odd[0] = (w0 >> 16) | (w1 & 0xFFFF0000u);
+          odd[1] = (w2 >> 16) | (w3 & 0xFFFF0000u);
           const int r0 = ch * 8 + 2 * m, r1 = r0 + 1;
           *reinterpret_cast<u32x2*>(vt + r0 * kTile + ((kg ^ vt_swz(r0)) * 4)) = even;
           *reinterpret_cast<u32x2*>(vt + r1 * kTile + ((kg ^ vt_swz(r1)) * 4)) = odd;
@@ -234,284 +263,269 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a, MfmaPara
     }
   };
 
-  // ---------------- per-row softmax state and output accumulators ----------------
-  f32x16 acc[QB][C::kDb];
-  float m_run[QB], l_run[QB];
+  // ---------------- softmax state and output accumulators ----------------
+  f32x16 acc[C::kDb];
 #pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    m_run[q] = -INFINITY;
-    l_run[q] = 0.f;
+  for (int db = 0; db < C::kDb; ++db)
 #pragma unroll
-    for (int db = 0; db < C::kDb; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[q][db][r] = 0.f;
-  }
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m_c = -INFINITY;  // running maximum, already multiplied by c
+  float l_run = 0.f;
 
-  auto compute_tile = [&](int stage, int tile) {
-    const uint16_t* ks = lds + stage * C::kStage;
-    const uint16_t* vt = ks + kTile * D;
-    const int tb = tile * kTile;
-    const bool masked = tb + kTile > P;  // tile reaches the tree slots or the end
+  // One 32-key half (kb) of a tile: scores, mask, online-softmax update, PV.
+  auto compute_half = [&](const uint16_t* ks, const uint16_t* vt, int tb, int kb) __attribute__((always_inline)) {
+    f32x16 sc = {};
 #pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      if (!qactive[q]) continue;
-      // S^T for the two 32-key halves of the tile
-      f32x16 sc[2];
+    for (int kk = 0; kk < C::kKs; ++kk) {
+      const int ch = kk * 2 + hh;
+      const int key = kb * 32 + col;
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(ks + key * D + ((ch ^ (key & 7)) * 8));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[kk], sc, 0, 0, 0);
+    }
+    if (tb + kb * 32 + 32 > P) {  // the half reaches the tree slots or the end: mask
+      const uint64_t vis = tile_visibility(mw, tb, P) >> (kb * 32 + 4 * hh);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 sacc = {};
-        const int key = kb * 32 + col;
-#pragma unroll
-        for (int kk = 0; kk < C::kKs; ++kk) {
-          const int ch = kk * 2 + hh;
-          const bf16x8 av =
-              *reinterpret_cast<const bf16x8*>(ks + key * D + ((ch ^ (key & 7)) * 8));
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[q][kk], sacc, 0, 0, 0);
-        }
-        sc[kb] = sacc;
+      for (int r = 0; r < 16; ++r) {
+        const int bit = 8 * (r >> 2) + (r & 3);
+        sc[r] = ((vis >> bit) & 1ull) ? sc[r] : -INFINITY;
       }
-      // scores as plain floats; masked tiles select -inf without branches
-      float sv[2][16];
+    }
+    float mt = sc[0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+    mt = pair_max(mt) * c;
+    // lazy rescale: raise m only when a row's maximum grew by more than 2^8
+    const bool grow = mt > m_c + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mn = grow ? mt : m_c;
+      // rows that do not grow keep alpha = 1 (their m may still be -inf)
+      const float alpha = grow ? exp2_fast(m_c - mn) : 1.f;  // 0 on the first visible keys
+      m_c = mn;
+      l_run *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sv[kb][r] = sc[kb][r];
-      if (masked) {
-        const uint64_t vis = tile_visibility(mw[q], tb, P) >> (4 * hh);
+      for (int db = 0; db < C::kDb; ++db)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+    const float mcs = (m_c == -INFINITY) ? 0.f : m_c;  // no visible key yet: p = 0
+    u32x4 pw[2];
+    float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int bit = kb * 32 + 8 * (r >> 2) + (r & 3);
-            sv[kb][r] = ((vis >> bit) & 1ull) ? sv[kb][r] : -INFINITY;
-          }
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = exp2_fast(__builtin_fmaf(sc[r], c, -mcs));
+      const float p1 = exp2_fast(__builtin_fmaf(sc[r + 1], c, -mcs));
+      lsum0 += p0;
+      lsum1 += p1;
+      pw[r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
+    }
+    l_run += lsum0 + lsum1;
+    // O^T += V^T P^T over the two 16-key chunks of this half
+#pragma unroll
+    for (int kc2 = 0; kc2 < 2; ++kc2) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kc2]);
+      const int g1 = kb * 8 + kc2 * 4 + hh, g2 = g1 + 2;
+#pragma unroll
+      for (int db = 0; db < C::kDb; ++db) {
+        const int d = db * 32 + col;
+        const int sw = vt_swz(d);
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vt + d * kTile + ((g1 ^ sw) * 4));
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + d * kTile + ((g2 ^ sw) * 4));
+        u32x4 w;
+        w[0] = lo[0];
+        w[1] = lo[1];
+        w[2] = hi[0];
+        w[3] = hi[1];
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb,
+                                                          acc[db], 0, 0, 0);
       }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sv[kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m_run[q], mt);
-      const float ms = (mn == -INFINITY) ? 0.f : mn;  // nothing visible yet: keep zeros
-      const float alpha = exp2_fast((m_run[q] - ms) * c);
-      const float mc = ms * c;
-      m_run[q] = mn;
-      float lsum = 0.f;
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = exp2_fast(__builtin_fmaf(sv[kb][r], c, -mc));
-          lsum += p[r];
-        }
-#pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2) {
-          u32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[kc2 * 8 + 2 * e], p[kc2 * 8 + 2 * e + 1]);
-          pb[kb][kc2] = __builtin_bit_cast(bf16x8, w);
-        }
-      }
-      l_run[q] = l_run[q] * alpha + lsum;
-      // wave-uniform branch: skipped when no row's maximum moved (alpha == 1)
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-        for (int db = 0; db < C::kDb; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[q][db][r] *= alpha;
-      }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2) {
-          const int g1 = kb * 8 + kc2 * 4 + hh, g2 = g1 + 2;
-#pragma unroll
-          for (int db = 0; db < C::kDb; ++db) {
-            const int d = db * 32 + col;
-            const int sw = vt_swz(d);
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vt + d * kTile + ((g1 ^ sw) * 4));
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + d * kTile + ((g2 ^ sw) * 4));
-            u32x4 w;
-            w[0] = lo[0];
-            w[1] = lo[1];
-            w[2] = hi[0];
-            w[3] = hi[1];
-            acc[q][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
-                                                                 pb[kb][kc2], acc[q][db], 0, 0, 0);
-          }
-        }
     }
   };
 
+  auto compute_tile = [&](int stage, int tile) __attribute__((always_inline)) {
+    const uint16_t* ks = lds + stage * C::kStage;
+    const uint16_t* vt = ks + kTile * D;
+    const int tb = tile * kTile;
+#pragma unroll 1
+    for (int kb = 0; kb < 2; ++kb) compute_half(ks, vt, tb, kb);
+  };
+
   // ---------------- main loop ----------------
-  load_tile(t0);
+  int bid_next = tile_blocks(t0);
+  load_tile(t0, bid_next);
+  if (t0 + 1 < t1) bid_next = tile_blocks(t0 + 1);
   store_tile(0);
   __syncthreads();
   for (int tile = t0; tile < t1; ++tile) {
     const int stage = (tile - t0) & 1;
     const bool more = tile + 1 < t1;
-    if (more) load_tile(tile + 1);
-    compute_tile(stage, tile);
+    if (more) {
+      load_tile(tile + 1, bid_next);
+      if (tile + 2 < t1) bid_next = tile_blocks(tile + 2);
+    }
+    if (active) compute_tile(stage, tile);
     if (more) store_tile(stage ^ 1);
     __syncthreads();
   }
 
   // ---------------- epilogue ----------------
+  if (!active) return;
+  const float lt = pair_sum(l_run);
+  if (r_me >= R) return;
+  const int node = r_me / g, hg = r_me % g;
+  if (mp.nsplit == 1) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* op = static_cast<uint16_t*>(a.out) +
+                   ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D;
 #pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    if (!qactive[q]) continue;
-    const int r = row0 + q * 32 + col;
-    const float lt = l_run[q] + __shfl_xor(l_run[q], 32, 64);
-    if (r >= R) continue;
-    const int node = r / g, hg = r % g;
-    if (mp.nsplit == 1) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      uint16_t* op = static_cast<uint16_t*>(a.out) +
-                     ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D;
+    for (int db = 0; db < C::kDb; ++db)
 #pragma unroll
-      for (int db = 0; db < C::kDb; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = db * 32 + 8 * j + 4 * hh;
-          u32x2 w;
-          w[0] = pack_bf16x2(acc[q][db][4 * j] * inv, acc[q][db][4 * j + 1] * inv);
-          w[1] = pack_bf16x2(acc[q][db][4 * j + 2] * inv, acc[q][db][4 * j + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + d) = w;
-        }
-    } else {
-      // partial state of this split: [B][Hkv][nsplit][R] rows
-      const size_t prow = ((static_cast<size_t>(b) * a.Hkv + kh) * mp.nsplit + s) * R + r;
-      const size_t nprow = static_cast<size_t>(a.B) * a.Hkv * mp.nsplit * R;
-      float* po = static_cast<float*>(a.workspace) + prow * D;
-      float* pm = static_cast<float*>(a.workspace) + nprow * D;
-      float* pl = pm + nprow;
-#pragma unroll
-      for (int db = 0; db < C::kDb; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = db * 32 + 8 * j + 4 * hh;
-          float4 v;
-          v.x = acc[q][db][4 * j];
-          v.y = acc[q][db][4 * j + 1];
-          v.z = acc[q][db][4 * j + 2];
-          v.w = acc[q][db][4 * j + 3];
-          *reinterpret_cast<float4*>(po + d) = v;
-        }
-      if (hh == 0) {
-        pm[prow] = m_run[q];
-        pl[prow] = lt;
+      for (int j = 0; j < 4; ++j) {
+        const int d = db * 32 + 8 * j + 4 * hh;
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv);
+        w[1] = pack_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + d) = w;
       }
+  } else {
+    // partial state of this split: rows [B][Hkv][nsplit][R]
+    const size_t prow = ((static_cast<size_t>(b) * a.Hkv + kh) * mp.nsplit + s) * R + r_me;
+    const size_t nprow = static_cast<size_t>(a.B) * a.Hkv * mp.nsplit * R;
+    float* po = static_cast<float*>(a.workspace) + prow * D;
+    float* pm = static_cast<float*>(a.workspace) + nprow * D;
+    float* pl = pm + nprow;
+#pragma unroll
+    for (int db = 0; db < C::kDb; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = db * 32 + 8 * j + 4 * hh;
+        float4 v;
+        v.x = acc[db][4 * j];
+        v.y = acc[db][4 * j + 1];
+        v.z = acc[db][4 * j + 2];
+        v.w = acc[db][4 * j + 3];
+        *reinterpret_cast<float4*>(po + d) = v;
+      }
+    if (hh == 0) {
+      pm[prow] = m_c;
+      pl[prow] = lt;
     }
   }
 }
 
-// Merge the per-split partial states of every row (log-sum-exp rule) and
-// write the bf16 output.  One wavefront per (sequence, KV head, row).
+// Merge the per-split partial states (log-sum-exp rule) and write bf16
+// outputs.  Each thread owns 4 dims of one row: a workgroup of 256 threads
+// covers 1024 / D rows of one (sequence, KV head).
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, MfmaParams mp) {
-  const int lane = threadIdx.x & 63;
+  constexpr int kTpr = D / 4;  // threads per row
+  constexpr int kRowsPerBlock = 256 / kTpr;
   const int g = a.Hq / a.Hkv;
   const int R = g * a.N;
-  const long gw = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (gw >= static_cast<long>(a.B) * a.Hkv * R) return;
-  const int r = static_cast<int>(gw % R);
-  const int kh = static_cast<int>((gw / R) % a.Hkv);
-  const int b = static_cast<int>(gw / (static_cast<long>(R) * a.Hkv));
+  const int blocks_per_head = (R + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int bh = blockIdx.x / blocks_per_head;  // b * Hkv + kh
+  const int r = (blockIdx.x % blocks_per_head) * kRowsPerBlock + threadIdx.x / kTpr;
+  const int d = (threadIdx.x % kTpr) * 4;
+  if (r >= R) return;
+  const int kh = bh % a.Hkv;
+  const int b = bh / a.Hkv;
   int P = a.prefix_lens[b];
   P = P < 0 ? 0 : (P > a.max_prefix_len ? a.max_prefix_len : P);
   const int ntiles = (P + a.N + kTile - 1) / kTile;
   const int ns = min(mp.nsplit, (ntiles + mp.tiles_per_split - 1) / mp.tiles_per_split);
-  const float c = a.scale * kLog2e;
   const size_t nprow = static_cast<size_t>(a.B) * a.Hkv * mp.nsplit * R;
   const float* po = static_cast<const float*>(a.workspace);
   const float* pm = po + nprow * D;
   const float* pl = pm + nprow;
-  const size_t base = (static_cast<size_t>(b) * a.Hkv + kh) * mp.nsplit * R + r;
+  const size_t base = static_cast<size_t>(bh) * mp.nsplit * R + r;
 
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[base + static_cast<size_t>(s) * R]);
+  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, pm[base + static_cast<size_t>(sp) * R]);
   const float Ms = (M == -INFINITY) ? 0.f : M;
-  constexpr int PER = D / 64;
-  float o[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.f;
+  float4 o = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t pr = base + static_cast<size_t>(s) * R;
-    const float w = exp2_fast((pm[pr] - Ms) * c);
+  for (int sp = 0; sp < ns; ++sp) {
+    const size_t pr = base + static_cast<size_t>(sp) * R;
+    const float w = exp2_fast(pm[pr] - Ms);
     L += w * pl[pr];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] += w * po[pr * D + lane * PER + e];
+    const float4 v = *reinterpret_cast<const float4*>(po + pr * D + d);
+    o.x += w * v.x;
+    o.y += w * v.y;
+    o.z += w * v.z;
+    o.w += w * v.w;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   const int node = r / g, hg = r % g;
   uint16_t* op = static_cast<uint16_t*>(a.out) +
-                 ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) op[lane * PER + e] = f32_to_bf16(o[e] * inv);
+                 ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D + d;
+  u32x2 w;
+  w[0] = pack_bf16x2(o.x * inv, o.y * inv);
+  w[1] = pack_bf16x2(o.z * inv, o.w * inv);
+  *reinterpret_cast<u32x2*>(op) = w;
 }
 
-template <int D, int NW, int QB>
+template <int D, int NW>
 hipError_t launch_cfg(const AttnArgs& a, const MfmaParams& mp, hipStream_t stream) {
-  using C = Cfg<D, NW, QB>;
+  using C = Cfg<D, NW>;
   const long blocks = static_cast<long>(a.B) * a.Hkv * mp.nsplit * mp.row_chunks;
   const size_t shmem = 2 * C::kStage * sizeof(uint16_t);
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NW, QB>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NW>), dim3(static_cast<unsigned>(blocks)),
                      dim3(C::kThreads), shmem, stream, a, mp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || mp.nsplit == 1) return e;
-  const long rows = static_cast<long>(a.B) * a.Hkv * (a.Hq / a.Hkv) * a.N;
-  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(static_cast<unsigned>((rows + 3) / 4)),
-                     dim3(256), 0, stream, a, mp);
+  constexpr int kRowsPerBlock = 256 / (D / 4);
+  const int R = (a.Hq / a.Hkv) * a.N;
+  const long cblocks = static_cast<long>(a.B) * a.Hkv * ((R + kRowsPerBlock - 1) / kRowsPerBlock);
+  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(static_cast<unsigned>(cblocks)), dim3(256), 0,
+                     stream, a, mp);
   return hipGetLastError();
 }
 
-constexpr int kWaves = 4;
+template <int D>
+hipError_t launch_d(const AttnArgs& a, const MfmaParams& mp, hipStream_t stream) {
+  switch (mp.waves) {
+    case 4: return launch_cfg<D, 4>(a, mp, stream);
+    case 5: return launch_cfg<D, 5>(a, mp, stream);
+    case 6: return launch_cfg<D, 6>(a, mp, stream);
+    case 7: return launch_cfg<D, 7>(a, mp, stream);
+    default: return launch_cfg<D, 8>(a, mp, stream);
+  }
+}
+
+constexpr int kMinWaves = 4;  // the loader keeps at most a few 16-byte loads per thread
+constexpr int kMaxWaves = 8;
 constexpr int kTargetBlocks = 512;
 constexpr int kMinTilesPerSplit = 2;
 
-struct Plan {
-  int qb;
-  MfmaParams mp;
-};
-
-Plan plan_for(int B, int N, int Hq, int Hkv, int max_prefix_len) {
+MfmaParams plan_for(int B, int N, int Hq, int Hkv, int max_prefix_len) {
   const int R = (Hq / Hkv) * N;
-  Plan p;
-  p.qb = R > kWaves * 32 ? 2 : 1;
-  const int rows_per_wg = kWaves * 32 * p.qb;
-  p.mp.row_chunks = (R + rows_per_wg - 1) / rows_per_wg;
+  const int qblocks = (R + 31) / 32;
+  MfmaParams p;
+  p.row_chunks = (qblocks + kMaxWaves - 1) / kMaxWaves;
+  p.waves = (qblocks + p.row_chunks - 1) / p.row_chunks;
+  if (p.waves < kMinWaves) p.waves = kMinWaves;  // extra waves only load
   const int max_tiles = (max_prefix_len + N + kTile - 1) / kTile;
-  const long base = static_cast<long>(B) * Hkv * p.mp.row_chunks;
+  const long base = static_cast<long>(B) * Hkv * p.row_chunks;
   long want = (kTargetBlocks + base - 1) / base;
   const long cap = (max_tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
   if (want > cap) want = cap;
   if (want < 1) want = 1;
-  p.mp.tiles_per_split = static_cast<int>((max_tiles + want - 1) / want);
-  p.mp.nsplit = (max_tiles + p.mp.tiles_per_split - 1) / p.mp.tiles_per_split;
+  p.tiles_per_split = static_cast<int>((max_tiles + want - 1) / want);
+  p.nsplit = (max_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
   return p;
 }
 
 }  // namespace
 
 size_t attention_mfma_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
-  const Plan p = plan_for(B, N, Hq, Hkv, max_prefix_len);
-  if (p.mp.nsplit == 1) return 0;
-  const size_t rows = static_cast<size_t>(B) * Hkv * p.mp.nsplit * (Hq / Hkv) * N;
+  const MfmaParams p = plan_for(B, N, Hq, Hkv, max_prefix_len);
+  if (p.nsplit == 1) return 0;
+  const size_t rows = static_cast<size_t>(B) * Hkv * p.nsplit * (Hq / Hkv) * N;
   return rows * (D + 2) * sizeof(float);
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
-  const Plan p = plan_for(a.B, a.N, a.Hq, a.Hkv, a.max_prefix_len);
-  if (a.D == 128)
-    return p.qb == 2 ? launch_cfg<128, kWaves, 2>(a, p.mp, stream)
-                     : launch_cfg<128, kWaves, 1>(a, p.mp, stream);
-  return p.qb == 2 ? launch_cfg<64, kWaves, 2>(a, p.mp, stream)
-                   : launch_cfg<64, kWaves, 1>(a, p.mp, stream);
+  const MfmaParams p = plan_for(a.B, a.N, a.Hq, a.Hkv, a.max_prefix_len);
+  return a.D == 128 ? launch_d<128>(a, p, stream) : launch_d<64>(a, p, stream);
 }
 
 }  // namespace tv
