@@ -10,25 +10,33 @@
 // serves every node and every query head of the group.  Each of the NW waves
 // owns 32 rows (waves past the last row only help load tiles).
 //
-// Per 64-key tile (double-buffered in LDS; the next tile is prefetched into
-// registers while the current one is computed; the block ids of the tile
-// after that are already in scalar registers), one 32-key half at a time:
-//   S^T (keys x rows)   = K (keys x D)   * Q^T (D x rows)   v_mfma_f32_32x32x16_bf16
-//   O^T (D x rows)     += V^T (D x keys) * P^T (keys x rows) v_mfma_f32_32x32x16_bf16
-// In the transposed form every accumulator a lane holds belongs to one query
-// row (lane % 32), so softmax rescaling is a per-lane scalar, and the score
-// accumulators are already in the B-operand layout of the PV product (the
-// MFMA contraction order of the keys is permuted identically in both
-// operands).  Lanes l and l+32 share a row and split its keys; they combine
-// their tile maxima with one v_permlane32_swap per tile and their
-// denominators once at the end.
+// Memory pipeline: 32-key tiles stream from HBM straight into LDS with
+// global_load_lds_dwordx4 (each lane's 16 bytes land at the wave's LDS base +
+// 16 * lane; no registers are staged), through kStages LDS buffers, so
+// kStages - 1 tiles are in flight per workgroup.  Each wave waits only for its
+// own copies of the tile it is about to use (s_waitcnt vmcnt with the number
+// of copies it has issued since), then one s_barrier makes every wave's
+// copies visible and frees the buffer of the previous tile.  The block ids of
+// a tile are two wave-uniform table entries.
 //
-// LDS layouts (bf16 elements):
-//   K  [key][D], 16-byte chunk c of key k stored at chunk c ^ (k % 8)
-//   Vt [dim][64 keys], 8-byte key group G of dim r stored at group
-//      G ^ ((r % 16) ^ ((r / 8) % 16))
-// Both swizzles make the loader's writes and the MFMA operand reads free of
-// bank conflicts.
+// Per tile, with lanes l and l+32 sharing query row l % 32:
+//   S^T (32 keys x rows)  = K (keys x D) * Q^T (D x rows)   v_mfma_f32_32x32x16_bf16
+//   O^T (D x rows)       += V^T (D x keys) * P^T (keys x rows)
+// In the transposed form every accumulator a lane holds belongs to one row,
+// so softmax rescaling is a per-lane scalar, and the score accumulators are
+// already the B operand of the PV product.  The V^T operand is read from the
+// row-major V tile with ds_read_b64_tr_b16: in each 16-lane group, lane j
+// receives element j % 4 of the 8 bytes addressed by lanes j/4, j/4+4,
+// j/4+8 and j/4+12; pointing lanes 4k..4k+3 of a group at key k (four dims
+// each) hands every lane four keys of its own dim, in the key order of P^T.
+//
+// LDS layouts (bf16 elements, one buffer = K tile then V tile, [key][D]):
+//   K: 16-byte chunk c of key k stored at chunk c ^ (k % 8)
+//   V: 16-byte chunk c of key k stored at chunk c ^ (2 * (k % 4))
+// The K swizzle spreads the QK operand reads (8 keys, one chunk) and the V
+// swizzle the transpose reads (4 keys x 2 chunks per 16 lanes) over all
+// banks.  The copies realise a swizzle by choosing which global chunk each
+// lane fetches.
 //
 // Softmax: scores stay raw; p = exp2(s * scale*log2(e) - m) with one FMA and
 // one v_exp_f32.  The running maximum m is only raised when a row's new tile
@@ -46,26 +54,32 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+#define CONST_AS __attribute__((address_space(4)))
 
-constexpr int kTile = 64;             // keys per tile
+constexpr int kTile = 32;             // keys per tile
+constexpr int kStages = 4;            // LDS buffers; kStages - 1 tiles in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRescale = 8.0f;  // log2 units a row maximum may grow before rescaling
 
 template <int D, int NW>
 struct Cfg {
   static constexpr int kThreads = NW * 64;
-  static constexpr int kChunks = D / 8;                  // 16-byte chunks per key row
-  static constexpr int kKUnits = kTile * kChunks;        // 16-byte loads of a K tile
-  static constexpr int kVUnits = (kTile / 4) * kChunks;  // (4 keys x 16 bytes) loads of a V tile
-  static constexpr int kKPer = (kKUnits + kThreads - 1) / kThreads;
-  static constexpr int kVPer = (kVUnits + kThreads - 1) / kThreads;
+  static constexpr int kChunks = D / 8;                   // 16-byte chunks per key row
+  static constexpr int kKeysPerCopy = 64 / kChunks;       // keys one wave copy instruction covers
+  static constexpr int kCopiesPerTile = kTile / kKeysPerCopy;  // wave copies per K (or V) tile
+  static constexpr int kCopiesPerWave = kCopiesPerTile / NW;
   static constexpr int kKs = D / 16;  // k-steps of the QK product
   static constexpr int kDb = D / 32;  // 32-dim output blocks
-  static constexpr int kStage = kTile * D * 2;  // K + Vt elements per stage
-  static constexpr int kRows = NW * 32;         // rows per workgroup
+  static constexpr int kTileElems = kTile * D;             // one K (or V) tile
+  static constexpr int kStageElems = 2 * kTileElems;       // K + V
+  static constexpr int kRows = NW * 32;                    // rows per workgroup
+  static constexpr int kDmaPerTile = 2 * kCopiesPerWave;   // copies per wave per tile (K and V)
+  static_assert(kCopiesPerTile % NW == 0, "every wave issues the same number of copies");
 };
 
 struct MfmaParams {
@@ -74,8 +88,6 @@ struct MfmaParams {
   int row_chunks;  // workgroups along the rows of one KV head
   int waves;       // waves per workgroup (32 rows each)
 };
-
-__device__ __forceinline__ int vt_swz(int r) { return (r & 15) ^ ((r >> 3) & 15); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -97,17 +109,25 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Visibility of the 64 keys of the tile that starts at logical position tb,
-// for a row whose node has ancestor-or-self bits mw: bit k is set iff
-// position tb + k is in the prefix or is a tree slot of one of those nodes.
-// Bits of nodes >= N are zero in mw, so positions past the end are hidden.
-// Every condition depends only on (tb, P) and is uniform across the wave.
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Visibility of the 64 keys starting at logical position tb, for a row whose
+// node has ancestor-or-self bits mw: bit k is set iff position tb + k is in
+// the prefix or is a tree slot of one of those nodes.  Bits of nodes >= N are
+// zero in mw, so positions past the end are hidden.  Every condition depends
+// only on (tb, P) and is uniform across the wave.
 __device__ __forceinline__ uint64_t tile_visibility(const uint64_t (&mw)[4], int tb, int P) {
   const int npre = P - tb;
   uint64_t vis = npre >= 64 ? ~0ull : (npre <= 0 ? 0ull : ((1ull << npre) - 1ull));
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int pos = P + 64 * k - tb;  // tile position of tree node 64k
+    const int pos = P + 64 * k - tb;  // position (relative to tb) of tree node 64k
     if (pos >= 0 && pos < 64)
       vis |= mw[k] << pos;
     else if (pos < 0 && pos > -64)
@@ -156,6 +176,47 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v_cache);
   const float c = a.scale * kLog2e;
 
+  // every table entry this workgroup will use must name a block of the cache
+  for (int e = t0 * 2 + tid; e < min(t1 * 2, nblk); e += C::kThreads) {
+    const int v = table[e];
+    if (v < 0 || v >= a.num_blocks) report(a.dev_status, TV_DEV_BAD_CACHE);
+  }
+
+  // ---------------- tile copies: HBM -> LDS ----------------
+  // Wave copy i of a K (or V) tile covers keys i*kKeysPerCopy .. +kKeysPerCopy-1;
+  // lane l writes chunk position l % kChunks of key i*kKeysPerCopy + l / kChunks.
+  const int ckey = lane / C::kChunks, cpos = lane % C::kChunks;
+  // Block ids come through the constant address space: uniform reads become
+  // scalar loads, which never wait behind the in-flight tile copies.
+  const CONST_AS int32_t* table_s = (const CONST_AS int32_t*)table;
+  auto fetch_ids = [&](int tile, int& b0, int& b1) __attribute__((always_inline)) {
+    const int e0 = tile * 2;  // the tile spans table entries e0 and e0 + 1
+    b0 = e0 < nblk ? table_s[e0] : -1;
+    b1 = e0 + 1 < nblk ? table_s[e0 + 1] : -1;
+  };
+  auto issue_tile = [&](int tile, int stage, int b0, int b1) __attribute__((always_inline)) {
+    const int tb = tile * kTile;
+    b0 = (b0 >= 0 && b0 < a.num_blocks) ? b0 : -1;
+    b1 = (b1 >= 0 && b1 < a.num_blocks) ? b1 : -1;
+    uint16_t* kst = lds + stage * C::kStageElems;
+    uint16_t* vst = kst + C::kTileElems;
+#pragma unroll
+    for (int j = 0; j < C::kCopiesPerWave; ++j) {
+      const int copy = j * NW + wave;
+      const int key = copy * C::kKeysPerCopy + ckey;
+      const int blk = key < 16 ? b0 : b1;
+      const bool ok = tb + key < total && blk >= 0;
+      // keys past the end (masked later) read a harmless in-bounds row
+      const long row = ok ? (static_cast<long>(blk) * kBlockSize + (key & 15)) * a.Hkv + kh : 0;
+      const int ck = cpos ^ (key & 7);
+      const int cv = cpos ^ (2 * (key & 3));
+      __builtin_amdgcn_global_load_lds(kc + row * D + ck * 8,
+                                       (LDS_AS void*)(kst + copy * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vc + row * D + cv * 8,
+                                       (LDS_AS void*)(vst + copy * 512), 16, 0, 0);
+    }
+  };
+
   // ---------------- this wave's 32 query rows (B operand of S^T) ----------------
   const int row0 = rc * C::kRows + wave * 32;
   const bool active = row0 < R;
@@ -178,90 +239,15 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) mw[w] = (w < W) ? mrow[w] : 0ull;
   }
+  // the query and mask loads must not count against the copy waits below
+  wait_vmcnt<0>();
 
-  // ---------------- tile loader ----------------
-  // Lane j < 4 of every wave holds the block id of table entry 4*tile + j
-  // (-1 past the sequence or for an out-of-range id); threads pick theirs
-  // with one cross-lane read.  The ids are fetched one tile ahead.
-  auto tile_blocks = [&](int tile) __attribute__((always_inline)) -> int {
-    const int e = tile * 4 + (lane & 3);
-    int v = -1;
-    if (e < nblk) {
-      v = table[e];
-      if (v < 0 || v >= a.num_blocks) {
-        report(a.dev_status, TV_DEV_BAD_CACHE);
-        v = -1;
-      }
-    }
-    return v;
-  };
-
-  u32x4 kreg[C::kKPer];
-  u32x4 vreg[C::kVPer][4];
-
-  auto load_tile = [&](int tile, int bids) __attribute__((always_inline)) {
-    const int tb = tile * kTile;
-#pragma unroll
-    for (int j = 0; j < C::kKPer; ++j) {
-      const int u = tid + j * C::kThreads;
-      const int key = u / C::kChunks, ch = u % C::kChunks;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      const int blk = __shfl(bids, (key >> 4) & 3, 64);
-      if (u < C::kKUnits && tb + key < total && blk >= 0)
-        v = *reinterpret_cast<const u32x4*>(
-            kc + ((static_cast<long>(blk) * kBlockSize + (key & 15)) * a.Hkv + kh) * D + ch * 8);
-      kreg[j] = v;
-    }
-#pragma unroll
-    for (int j = 0; j < C::kVPer; ++j) {
-      const int u = tid + j * C::kThreads;
-      const int kg = u / C::kChunks, ch = u % C::kChunks;
-      const int blk = __shfl(bids, (kg >> 2) & 3, 64);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = kg * 4 + e;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (u < C::kVUnits && tb + key < total && blk >= 0)
-          v = *reinterpret_cast<const u32x4*>(
-              vc + ((static_cast<long>(blk) * kBlockSize + (key & 15)) * a.Hkv + kh) * D + ch * 8);
-        vreg[j][e] = v;
-      }
-    }
-  };
-
-  auto store_tile = [&](int stage) __attribute__((always_inline)) {
-    uint16_t* ks = lds + stage * C::kStage;
-    uint16_t* vt = ks + kTile * D;
-#pragma unroll
-    for (int j = 0; j < C::kKPer; ++j) {
-      const int u = tid + j * C::kThreads;
-      if (u < C::kKUnits) {
-        const int key = u / C::kChunks, ch = u % C::kChunks;
-        *reinterpret_cast<u32x4*>(ks + key * D + ((ch ^ (key & 7)) * 8)) = kreg[j];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < C::kVPer; ++j) {
-      const int u = tid + j * C::kThreads;
-      if (u < C::kVUnits) {
-        const int kg = u / C::kChunks, ch = u % C::kChunks;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          // dims 2m and 2m+1 of the 4 keys: low and high halves of word m
-          const uint32_t w0 = vreg[j][0][m], w1 = vreg[j][1][m];
-          const uint32_t w2 = vreg[j][2][m], w3 = vreg[j][3][m];
-          u32x2 even, odd;
-          even[0] = (w0 & 0xFFFFu) | (w1 << 16);
-          even[1] = (w2 & 0xFFFFu) | (w3 << 16);
-          odd[0] = (w0 >> 16) | (w1 & 0xFFFF0000u);
-          odd[1] = (w2 >> 16) | (w3 & 0xFFFF0000u);
-          const int r0 = ch * 8 + 2 * m, r1 = r0 + 1;
-          *reinterpret_cast<u32x2*>(vt + r0 * kTile + ((kg ^ vt_swz(r0)) * 4)) = even;
-          *reinterpret_cast<u32x2*>(vt + r1 * kTile + ((kg ^ vt_swz(r1)) * 4)) = odd;
-        }
-      }
-    }
-  };
+  // per-lane parts of the V^T transpose-read addresses (see the header)
+  const int tq = lane >> 4, ts = lane & 15;
+  const int tr_row = 4 * hh + (ts >> 2);                 // + 16 * chunk (+ 8 for keys 4..7)
+  const int tr_chunk = 2 * (tq & 1) + ((ts & 3) >> 1);   // + 4 * dim block
+  const int tr_half = (ts & 1) * 4;
+  const int tr_swz = 2 * ((ts >> 2) & 3);                // 2 * (row % 4)
 
   // ---------------- softmax state and output accumulators ----------------
   f32x16 acc[C::kDb];
@@ -272,18 +258,19 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   float m_c = -INFINITY;  // running maximum, already multiplied by c
   float l_run = 0.f;
 
-  // One 32-key half (kb) of a tile: scores, mask, online-softmax update, PV.
-  auto compute_half = [&](const uint16_t* ks, const uint16_t* vt, int tb, int kb) __attribute__((always_inline)) {
+  auto compute_tile = [&](int stage, int tile) __attribute__((always_inline)) {
+    const uint16_t* ks = lds + stage * C::kStageElems;
+    const uint16_t* vs = ks + C::kTileElems;
+    const int tb = tile * kTile;
     f32x16 sc = {};
 #pragma unroll
     for (int kk = 0; kk < C::kKs; ++kk) {
       const int ch = kk * 2 + hh;
-      const int key = kb * 32 + col;
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(ks + key * D + ((ch ^ (key & 7)) * 8));
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(ks + col * D + ((ch ^ (col & 7)) * 8));
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[kk], sc, 0, 0, 0);
     }
-    if (tb + kb * 32 + 32 > P) {  // the half reaches the tree slots or the end: mask
-      const uint64_t vis = tile_visibility(mw, tb, P) >> (kb * 32 + 4 * hh);
+    if (tb + kTile > P) {  // the tile reaches the tree slots or the end: mask
+      const uint64_t vis = tile_visibility(mw, tb, P) >> (4 * hh);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int bit = 8 * (r >> 2) + (r & 3);
@@ -319,52 +306,66 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
       pw[r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
     }
     l_run += lsum0 + lsum1;
-    // O^T += V^T P^T over the two 16-key chunks of this half
+    // O^T += V^T P^T over the two 16-key chunks of the tile
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; ++kc2) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kc2]);
-      const int g1 = kb * 8 + kc2 * 4 + hh, g2 = g1 + 2;
+      const int r1 = 16 * kc2 + tr_row, r2 = r1 + 8;
 #pragma unroll
       for (int db = 0; db < C::kDb; ++db) {
-        const int d = db * 32 + col;
-        const int sw = vt_swz(d);
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vt + d * kTile + ((g1 ^ sw) * 4));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + d * kTile + ((g2 ^ sw) * 4));
+        const int chk = (4 * db + tr_chunk) ^ tr_swz;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(vs + r1 * D + chk * 8 + tr_half));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(vs + r2 * D + chk * 8 + tr_half));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
         u32x4 w;
-        w[0] = lo[0];
-        w[1] = lo[1];
-        w[2] = hi[0];
-        w[3] = hi[1];
+        w[0] = lo2[0];
+        w[1] = lo2[1];
+        w[2] = hi2[0];
+        w[3] = hi2[1];
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb,
                                                           acc[db], 0, 0, 0);
       }
     }
   };
 
-  auto compute_tile = [&](int stage, int tile) __attribute__((always_inline)) {
-    const uint16_t* ks = lds + stage * C::kStage;
-    const uint16_t* vt = ks + kTile * D;
-    const int tb = tile * kTile;
-#pragma unroll 1
-    for (int kb = 0; kb < 2; ++kb) compute_half(ks, vt, tb, kb);
+  // wait until this wave's copies of the tile about to be used are done:
+  // `later` tiles (at most kStages - 2) have been issued after it
+  auto wait_tile = [&](int later) __attribute__((always_inline)) {
+    static_assert(kStages == 4, "wait_tile covers 0..2 later tiles");
+    if (later >= 2)
+      wait_vmcnt<2 * C::kDmaPerTile>();
+    else if (later == 1)
+      wait_vmcnt<C::kDmaPerTile>();
+    else
+      wait_vmcnt<0>();
   };
 
   // ---------------- main loop ----------------
-  int bid_next = tile_blocks(t0);
-  load_tile(t0, bid_next);
-  if (t0 + 1 < t1) bid_next = tile_blocks(t0 + 1);
-  store_tile(0);
-  __syncthreads();
+  int nb0, nb1;  // block ids of the next tile to issue
+  fetch_ids(t0, nb0, nb1);
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i) {
+    if (t0 + i < t1) {
+      const int b0 = nb0, b1 = nb1;
+      fetch_ids(t0 + i + 1, nb0, nb1);
+      issue_tile(t0 + i, i, b0, b1);
+    }
+  }
   for (int tile = t0; tile < t1; ++tile) {
-    const int stage = (tile - t0) & 1;
-    const bool more = tile + 1 < t1;
-    if (more) {
-      load_tile(tile + 1, bid_next);
-      if (tile + 2 < t1) bid_next = tile_blocks(tile + 2);
+    const int stage = (tile - t0) % kStages;
+    wait_tile(min(kStages - 2, t1 - 1 - tile));
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // every wave's copies landed; tile - 1 is done
+    __asm__ volatile("" ::: "memory");
+    const int nt = tile + kStages - 1;
+    if (nt < t1) {
+      const int b0 = nb0, b1 = nb1;
+      fetch_ids(nt + 1, nb0, nb1);
+      issue_tile(nt, (nt - t0) % kStages, b0, b1);
     }
     if (active) compute_tile(stage, tile);
-    if (more) store_tile(stage ^ 1);
-    __syncthreads();
   }
 
   // ---------------- epilogue ----------------
@@ -467,7 +468,7 @@ template <int D, int NW>
 hipError_t launch_cfg(const AttnArgs& a, const MfmaParams& mp, hipStream_t stream) {
   using C = Cfg<D, NW>;
   const long blocks = static_cast<long>(a.B) * a.Hkv * mp.nsplit * mp.row_chunks;
-  const size_t shmem = 2 * C::kStage * sizeof(uint16_t);
+  const size_t shmem = kStages * C::kStageElems * sizeof(uint16_t);
   hipLaunchKernelGGL((attn_mfma_kernel<D, NW>), dim3(static_cast<unsigned>(blocks)),
                      dim3(C::kThreads), shmem, stream, a, mp);
   hipError_t e = hipGetLastError();
@@ -480,29 +481,17 @@ hipError_t launch_cfg(const AttnArgs& a, const MfmaParams& mp, hipStream_t strea
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_d(const AttnArgs& a, const MfmaParams& mp, hipStream_t stream) {
-  switch (mp.waves) {
-    case 4: return launch_cfg<D, 4>(a, mp, stream);
-    case 5: return launch_cfg<D, 5>(a, mp, stream);
-    case 6: return launch_cfg<D, 6>(a, mp, stream);
-    case 7: return launch_cfg<D, 7>(a, mp, stream);
-    default: return launch_cfg<D, 8>(a, mp, stream);
-  }
-}
-
-constexpr int kMinWaves = 4;  // the loader keeps at most a few 16-byte loads per thread
-constexpr int kMaxWaves = 8;
 constexpr int kTargetBlocks = 512;
-constexpr int kMinTilesPerSplit = 2;
+constexpr int kMinTilesPerSplit = 4;
 
-MfmaParams plan_for(int B, int N, int Hq, int Hkv, int max_prefix_len) {
+// Rows of a KV head go to workgroups of 4 waves (128 rows) or, for D = 128
+// and more than 128 rows, 8 waves (256 rows); the key range is split so that
+// the grid has about kTargetBlocks workgroups.
+MfmaParams plan_for(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
   const int R = (Hq / Hkv) * N;
-  const int qblocks = (R + 31) / 32;
   MfmaParams p;
-  p.row_chunks = (qblocks + kMaxWaves - 1) / kMaxWaves;
-  p.waves = (qblocks + p.row_chunks - 1) / p.row_chunks;
-  if (p.waves < kMinWaves) p.waves = kMinWaves;  // extra waves only load
+  p.waves = (D == 128 && R > 128) ? 8 : 4;
+  p.row_chunks = (R + p.waves * 32 - 1) / (p.waves * 32);
   const int max_tiles = (max_prefix_len + N + kTile - 1) / kTile;
   const long base = static_cast<long>(B) * Hkv * p.row_chunks;
   long want = (kTargetBlocks + base - 1) / base;
@@ -517,15 +506,17 @@ MfmaParams plan_for(int B, int N, int Hq, int Hkv, int max_prefix_len) {
 }  // namespace
 
 size_t attention_mfma_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
-  const MfmaParams p = plan_for(B, N, Hq, Hkv, max_prefix_len);
+  const MfmaParams p = plan_for(B, N, Hq, Hkv, D, max_prefix_len);
   if (p.nsplit == 1) return 0;
   const size_t rows = static_cast<size_t>(B) * Hkv * p.nsplit * (Hq / Hkv) * N;
   return rows * (D + 2) * sizeof(float);
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
-  const MfmaParams p = plan_for(a.B, a.N, a.Hq, a.Hkv, a.max_prefix_len);
-  return a.D == 128 ? launch_d<128>(a, p, stream) : launch_d<64>(a, p, stream);
+  const MfmaParams p = plan_for(a.B, a.N, a.Hq, a.Hkv, a.D, a.max_prefix_len);
+  if (a.D == 128)
+    return p.waves == 8 ? launch_cfg<128, 8>(a, p, stream) : launch_cfg<128, 4>(a, p, stream);
+  return launch_cfg<64, 4>(a, p, stream);
 }
 
 }  // namespace tv
