@@ -17,7 +17,8 @@
 // own copies of the tile it is about to use (s_waitcnt vmcnt with the number
 // of copies it has issued since), then one s_barrier makes every wave's
 // copies visible and frees the buffer of the previous tile.  The block ids of
-// a tile are two wave-uniform table entries.
+// a tile are two wave-uniform table entries read with scalar loads one tile
+// ahead; a copy's source is that block's base plus a per-thread offset.
 //
 // Per tile, with lanes l and l+32 sharing query row l % 32:
 //   S^T (32 keys x rows)  = K (keys x D) * Q^T (D x rows)   v_mfma_f32_32x32x16_bf16
@@ -25,7 +26,8 @@
 // In the transposed form every accumulator a lane holds belongs to one row,
 // so softmax rescaling is a per-lane scalar, and the score accumulators are
 // already the B operand of the PV product.  The V^T operand is read from the
-// row-major V tile with ds_read_b64_tr_b16: in each 16-lane group, lane j
+// row-major V tile with ds_read_b64_tr_b16 (inline assembly, waited for
+// explicitly; see ds_read_tr16_b64): in each 16-lane group, lane j
 // receives element j % 4 of the 8 bytes addressed by lanes j/4, j/4+4,
 // j/4+8 and j/4+12; pointing lanes 4k..4k+3 of a group at key k (four dims
 // each) hands every lane four keys of its own dim, in the key order of P^T.
@@ -62,7 +64,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define CONST_AS __attribute__((address_space(4)))
 
 constexpr int kTile = 32;             // keys per tile
-constexpr int kStages = 4;            // LDS buffers; kStages - 1 tiles in flight
+#ifndef TV_ATTN_STAGES
+#define TV_ATTN_STAGES 4
+#endif
+constexpr int kStages = TV_ATTN_STAGES;  // LDS buffers; kStages - 1 tiles in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRescale = 8.0f;  // log2 units a row maximum may grow before rescaling
 
@@ -107,6 +112,29 @@ __device__ __forceinline__ float pair_max(float x) {
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ds_read_b64_tr_b16 issued as inline assembly.  The compiler cannot tell
+// this LDS read from the in-flight LDS copies and would drain them all
+// (vmcnt(0)) before it; the caller instead waits with lds_wait_operands,
+// which the copies into other buffers never block.
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(const uint16_t* p) {
+  u32x2 v;
+  const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS const void*)p));
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+
+// s_waitcnt lgkmcnt(0) taking the transpose-read results as operands, so no
+// use of them is scheduled above the wait (device-only: the register
+// constraints do not exist on the host side of the compilation).
+__device__ __forceinline__ void lds_wait_operands(u32x4 (&v)[2][4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]),
+                 "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]));
+}
+__device__ __forceinline__ void lds_wait_operands(u32x4 (&v)[2][2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]), "+v"(v[1][1]));
 }
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding:
@@ -183,37 +211,43 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   }
 
   // ---------------- tile copies: HBM -> LDS ----------------
-  // Wave copy i of a K (or V) tile covers keys i*kKeysPerCopy .. +kKeysPerCopy-1;
-  // lane l writes chunk position l % kChunks of key i*kKeysPerCopy + l / kChunks.
+  // Wave copy i of a K (or V) tile covers keys i*kKeysPerCopy .. +kKeysPerCopy-1
+  // (all in one 16-token block); lane l writes chunk position l % kChunks of
+  // key i*kKeysPerCopy + l / kChunks.  The source address is a wave-uniform
+  // block base plus a per-thread offset fixed for the whole kernel.
   const int ckey = lane / C::kChunks, cpos = lane % C::kChunks;
+  const long block_stride = static_cast<long>(kBlockSize) * a.Hkv * D;  // elements per block
+  int off_k[C::kCopiesPerWave], off_v[C::kCopiesPerWave];
+#pragma unroll
+  for (int j = 0; j < C::kCopiesPerWave; ++j) {
+    const int key = (j * NW + wave) * C::kKeysPerCopy + ckey;
+    const int row = ((key & 15) * a.Hkv + kh) * D;
+    off_k[j] = row + (cpos ^ (key & 7)) * 8;
+    off_v[j] = row + (cpos ^ (2 * (key & 3))) * 8;
+  }
   // Block ids come through the constant address space: uniform reads become
   // scalar loads, which never wait behind the in-flight tile copies.
   const CONST_AS int32_t* table_s = (const CONST_AS int32_t*)table;
   auto fetch_ids = [&](int tile, int& b0, int& b1) __attribute__((always_inline)) {
     const int e0 = tile * 2;  // the tile spans table entries e0 and e0 + 1
-    b0 = e0 < nblk ? table_s[e0] : -1;
-    b1 = e0 + 1 < nblk ? table_s[e0 + 1] : -1;
+    b0 = e0 < nblk ? table_s[e0] : 0;
+    b1 = e0 + 1 < nblk ? table_s[e0 + 1] : 0;
   };
-  auto issue_tile = [&](int tile, int stage, int b0, int b1) __attribute__((always_inline)) {
-    const int tb = tile * kTile;
-    b0 = (b0 >= 0 && b0 < a.num_blocks) ? b0 : -1;
-    b1 = (b1 >= 0 && b1 < a.num_blocks) ? b1 : -1;
+  auto issue_tile = [&](int stage, int b0, int b1) __attribute__((always_inline)) {
+    // ids past the end or out of range (reported above) read block 0; those
+    // keys are masked, and block 0 holds finite values like any other
+    b0 = (b0 >= 0 && b0 < a.num_blocks) ? b0 : 0;
+    b1 = (b1 >= 0 && b1 < a.num_blocks) ? b1 : 0;
     uint16_t* kst = lds + stage * C::kStageElems;
     uint16_t* vst = kst + C::kTileElems;
 #pragma unroll
     for (int j = 0; j < C::kCopiesPerWave; ++j) {
       const int copy = j * NW + wave;
-      const int key = copy * C::kKeysPerCopy + ckey;
-      const int blk = key < 16 ? b0 : b1;
-      const bool ok = tb + key < total && blk >= 0;
-      // keys past the end (masked later) read a harmless in-bounds row
-      const long row = ok ? (static_cast<long>(blk) * kBlockSize + (key & 15)) * a.Hkv + kh : 0;
-      const int ck = cpos ^ (key & 7);
-      const int cv = cpos ^ (2 * (key & 3));
-      __builtin_amdgcn_global_load_lds(kc + row * D + ck * 8,
-                                       (LDS_AS void*)(kst + copy * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vc + row * D + cv * 8,
-                                       (LDS_AS void*)(vst + copy * 512), 16, 0, 0);
+      const long base = static_cast<long>(copy * C::kKeysPerCopy < kBlockSize ? b0 : b1) * block_stride;
+      __builtin_amdgcn_global_load_lds((const void*)(kc + base + off_k[j]), (LDS_AS void*)(kst + copy * 512), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vc + base + off_v[j]), (LDS_AS void*)(vst + copy * 512), 16,
+                                       0, 0);
     }
   };
 
@@ -269,6 +303,22 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
       const bf16x8 av = *reinterpret_cast<const bf16x8*>(ks + col * D + ((ch ^ (col & 7)) * 8));
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[kk], sc, 0, 0, 0);
     }
+    // V^T operands of the whole tile, read now so the reads overlap the softmax
+    u32x4 vop[2][C::kDb];
+#pragma unroll
+    for (int kc2 = 0; kc2 < 2; ++kc2) {
+      const int r1 = 16 * kc2 + tr_row, r2 = r1 + 8;
+#pragma unroll
+      for (int db = 0; db < C::kDb; ++db) {
+        const int chk = (4 * db + tr_chunk) ^ tr_swz;
+        const u32x2 lo = ds_read_tr16_b64(vs + r1 * D + chk * 8 + tr_half);
+        const u32x2 hi = ds_read_tr16_b64(vs + r2 * D + chk * 8 + tr_half);
+        vop[kc2][db][0] = lo[0];
+        vop[kc2][db][1] = lo[1];
+        vop[kc2][db][2] = hi[0];
+        vop[kc2][db][3] = hi[1];
+      }
+    }
     if (tb + kTile > P) {  // the tile reaches the tree slots or the end: mask
       const uint64_t vis = tile_visibility(mw, tb, P) >> (4 * hh);
 #pragma unroll
@@ -306,35 +356,30 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
       pw[r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
     }
     l_run += lsum0 + lsum1;
+    // the transpose reads above are invisible to the compiler's wait
+    // tracking: wait for them here, with their results as operands so that
+    // no use can be scheduled above the wait
+    lds_wait_operands(vop);
     // O^T += V^T P^T over the two 16-key chunks of the tile
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; ++kc2) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kc2]);
-      const int r1 = 16 * kc2 + tr_row, r2 = r1 + 8;
 #pragma unroll
-      for (int db = 0; db < C::kDb; ++db) {
-        const int chk = (4 * db + tr_chunk) ^ tr_swz;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4*)(vs + r1 * D + chk * 8 + tr_half));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4*)(vs + r2 * D + chk * 8 + tr_half));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-        u32x4 w;
-        w[0] = lo2[0];
-        w[1] = lo2[1];
-        w[2] = hi2[0];
-        w[3] = hi2[1];
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb,
+      for (int db = 0; db < C::kDb; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[kc2][db]), pb,
                                                           acc[db], 0, 0, 0);
-      }
     }
   };
 
   // wait until this wave's copies of the tile about to be used are done:
   // `later` tiles (at most kStages - 2) have been issued after it
   auto wait_tile = [&](int later) __attribute__((always_inline)) {
-    static_assert(kStages == 4, "wait_tile covers 0..2 later tiles");
-    if (later >= 2)
+    static_assert(kStages >= 2 && kStages <= 6, "wait_tile covers 0..4 later tiles");
+    if (later >= 4)
+      wait_vmcnt<4 * C::kDmaPerTile>();
+    else if (later == 3)
+      wait_vmcnt<3 * C::kDmaPerTile>();
+    else if (later == 2)
       wait_vmcnt<2 * C::kDmaPerTile>();
     else if (later == 1)
       wait_vmcnt<C::kDmaPerTile>();
@@ -350,7 +395,7 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     if (t0 + i < t1) {
       const int b0 = nb0, b1 = nb1;
       fetch_ids(t0 + i + 1, nb0, nb1);
-      issue_tile(t0 + i, i, b0, b1);
+      issue_tile(i, b0, b1);
     }
   }
   for (int tile = t0; tile < t1; ++tile) {
@@ -360,12 +405,9 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     __builtin_amdgcn_s_barrier();  // every wave's copies landed; tile - 1 is done
     __asm__ volatile("" ::: "memory");
     const int nt = tile + kStages - 1;
-    if (nt < t1) {
-      const int b0 = nb0, b1 = nb1;
-      fetch_ids(nt + 1, nb0, nb1);
-      issue_tile(nt, (nt - t0) % kStages, b0, b1);
-    }
+    if (nt < t1) issue_tile((nt - t0) % kStages, nb0, nb1);
     if (active) compute_tile(stage, tile);
+    if (nt < t1) fetch_ids(nt + 1, nb0, nb1);  // ready by the next issue
   }
 
   // ---------------- epilogue ----------------
