@@ -1,0 +1,87 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of the oracle's source (a dropped or
+transposed mask term, a wrong GQA index, an off-by-one prefix, a missing
+scale, the wrong argmax tie rule, a greedy instead of longest path, the bonus
+taken at the wrong node, compaction without gather-before-write, a wrong new
+length) and runs the pin suite against that copy in a separate process, on
+the CPU.  The suite must fail for every one of them.
+"""
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "ancestor_mask_transposed": ("visible[:, P:] = anc", "visible[:, P:] = anc.T"),
+    "node_does_not_see_itself": ("        anc[i, i] = True\n", ""),
+    "gqa_interleaved_heads": (
+        "Qg = q[b, :, kh * g:(kh + 1) * g, :].reshape(N * g, D)",
+        "Qg = q[b, :, kh::Hkv, :].reshape(N * g, D)"),
+    "prefix_off_by_one": ("visible[:, :P] = True", "visible[:, :P-1] = True"),
+    "scale_missing": ("s = scale * (Qg @ K[:, kh, :].T)", "s = (Qg @ K[:, kh, :].T)"),
+    "argmax_highest_index_on_ties": (
+        "return np.argmax(np.asarray(logits), axis=-1).astype(np.int64)",
+        "a = np.asarray(logits); "
+        "return (a.shape[-1] - 1 - np.argmax(a[..., ::-1], axis=-1)).astype(np.int64)"),
+    "first_child_instead_of_longest": ("                if len(cand) > len(best):",
+                                       "                if len(best) == 1:"),
+    "bonus_at_root": ("return path, int(am[path[-1]])", "return path, int(am[0])"),
+    "compaction_in_descending_order": (
+        "        ks = kf[src].copy()\n        vs = vf[src].copy()\n"
+        "        kf[dst] = ks\n        vf[dst] = vs",
+        "        for s_, d_ in zip(src[::-1], dst[::-1]):\n"
+        "            kf[d_] = kf[s_]; vf[d_] = vf[s_]"),
+    "new_length_without_root": ("new_lens[b] = P + L", "new_lens[b] = P + L - 1"),
+}
+
+COPY = ["pytest.ini", "workloads", os.path.join("tests", "conftest.py"),
+        os.path.join("tests", "test_oracle.py"), os.path.join("tests", "golden")]
+
+
+def _run_mutant(base, name, old, new):
+    src = open(os.path.join(ROOT, "oracle", "__init__.py")).read()
+    assert src.count(old) == 1, f"{name}: the planted site is not unique in the oracle"
+    d = os.path.join(base, name)
+    os.makedirs(os.path.join(d, "tests"))
+    os.makedirs(os.path.join(d, "oracle"))
+    for rel in COPY:
+        s = os.path.join(ROOT, rel)
+        if os.path.isdir(s):
+            shutil.copytree(s, os.path.join(d, rel), ignore=shutil.ignore_patterns("__pycache__"))
+        else:
+            shutil.copy(s, os.path.join(d, rel))
+    with open(os.path.join(d, "oracle", "__init__.py"), "w") as f:
+        f.write(src.replace(old, new))
+    env = dict(os.environ, OMP_NUM_THREADS="2", OPENBLAS_NUM_THREADS="2", MKL_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        "tests/test_oracle.py"], cwd=d, capture_output=True, text=True, env=env,
+                       timeout=600)
+    tail = (r.stdout.strip().splitlines() or [""])[-1]
+    return name, r.returncode, tail
+
+
+def test_every_planted_mistake_fails_a_pin(tmp_path):
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = list(ex.map(lambda kv: _run_mutant(str(tmp_path), kv[0], *kv[1]),
+                              MUTANTS.items()))
+    survived = [(n, tail) for n, rc, tail in results if rc == 0]
+    broken = [(n, rc, tail) for n, rc, tail in results if rc not in (0, 1)]
+    assert not broken, f"mutant runs that did not complete: {broken}"
+    assert not survived, f"planted mistakes that no pin caught: {survived}"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """Control: the same copy procedure with no mistake planted passes."""
+    name, rc, tail = _run_mutant(str(tmp_path), "control", "import numpy as np",
+                                 "import numpy as np")
+    assert rc == 0, tail
+
+
+if __name__ == "__main__":
+    sys.exit(pytest.main([__file__, "-q"]))
