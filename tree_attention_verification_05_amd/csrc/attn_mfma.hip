@@ -4,16 +4,19 @@
 // "EAGLE代码实现原理", 树结构缓冲: the common prefix is shared; "P-EAGLE",
 // 技术原理和实现方式 step 3.)
 //
-// Work unit: one workgroup per (sequence b, KV head kh, key split s, row
-// chunk).  The query rows of a KV head are its g = Hq/Hkv heads times the N
-// tree nodes (row r = node * g + head-in-group), so one K/V tile read from HBM
-// serves every node and every query head of the group.  Each of the NW waves
-// owns 32 rows (waves past the last row only help load tiles).
+// Work unit: a segment is (sequence b, KV head kh, row chunk).  The query
+// rows of a KV head are its g = Hq/Hkv heads times the N tree nodes (row r =
+// node * g + head-in-group), so one K/V tile read from HBM serves every node
+// and every query head of the group.  Each of the NW waves owns 32 rows
+// (waves past the last row only help load tiles).  Sequences differ in
+// length, so the tiles of all segments are laid end to end and every
+// workgroup takes an equal share of that flat range (see make_schedule);
+// a segment cut between workgroups is merged by a second kernel.
 //
 // Memory pipeline: 32-key tiles stream from HBM straight into LDS with
 // global_load_lds_dwordx4 (each lane's 16 bytes land at the wave's LDS base +
-// 16 * lane; no registers are staged), through kStages LDS buffers, so
-// kStages - 1 tiles are in flight per workgroup.  Each wave waits only for its
+// 16 * lane; no registers are staged), through a ring of kStages LDS
+// buffers, so kStages - 1 tiles are in flight per workgroup.  Each wave waits only for its
 // own copies of the tile it is about to use (s_waitcnt vmcnt with the number
 // of copies it has issued since), then one s_barrier makes every wave's
 // copies visible and frees the buffer of the previous tile.  The block ids of
@@ -46,9 +49,9 @@
 // output accumulators is then rare and happens under a wave-uniform branch.
 // The result is the same softmax: numerator and denominator use the same m.
 // Prefix tiles need no mask; tiles that reach the tree slots select -inf for
-// keys outside the row's ancestor set (branch-free).  With several key
-// splits, each split writes (m, denominator, unnormalised output) in fp32
-// and a second kernel merges them with the log-sum-exp rule.
+// keys outside the row's ancestor set (branch-free).  A segment shared by
+// several workgroups leaves (m, denominator, unnormalised output) in fp32 per
+// piece, merged with the log-sum-exp rule.
 #include "tv_internal.h"
 
 namespace tv {
@@ -64,10 +67,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define CONST_AS __attribute__((address_space(4)))
 
 constexpr int kTile = 32;             // keys per tile
-#ifndef TV_ATTN_STAGES
-#define TV_ATTN_STAGES 4
-#endif
-constexpr int kStages = TV_ATTN_STAGES;  // LDS buffers; kStages - 1 tiles in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRescale = 8.0f;  // log2 units a row maximum may grow before rescaling
 
@@ -84,15 +83,28 @@ struct Cfg {
   static constexpr int kStageElems = 2 * kTileElems;       // K + V
   static constexpr int kRows = NW * 32;                    // rows per workgroup
   static constexpr int kDmaPerTile = 2 * kCopiesPerWave;   // copies per wave per tile (K and V)
+  // LDS buffers (kStages - 1 tiles in flight): 4 (64 KB at D = 128) lets two
+  // 4-wave workgroups share a compute unit; an 8-wave workgroup has the unit
+  // to itself and takes 6 (96 KB)
+  static constexpr int kStages = NW == 8 ? 6 : 4;
   static_assert(kCopiesPerTile % NW == 0, "every wave issues the same number of copies");
 };
 
 struct MfmaParams {
-  int tiles_per_split;
-  int nsplit;      // splits per (sequence, KV head); 1 = write the output directly
-  int row_chunks;  // workgroups along the rows of one KV head
+  int grid;        // workgroups launched (G)
+  int balanced;    // 1: equal shares of the flat tile range; 0: fixed pieces per segment
+  int T;           // fixed: tiles per piece; balanced: smallest share
+  int pieces;      // fixed: pieces per segment
+  int row_chunks;  // row chunks per KV head
   int waves;       // waves per workgroup (32 rows each)
 };
+
+// workspace: a header written by the attention kernel for the merge (lane
+// tiles S, share length T, then the first lane tile of every sequence), then
+// the partial slots (2G balanced, G fixed) of kRows rows: unnormalised
+// outputs [slot][row][D], then running maxima and denominators [slot][row]
+// each, all fp32
+__host__ __device__ constexpr size_t header_bytes(int B) { return (8 + 4 * static_cast<size_t>(B) + 255) / 256 * 256; }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -164,118 +176,148 @@ __device__ __forceinline__ uint64_t tile_visibility(const uint64_t (&mw)[4], int
   return vis;
 }
 
+// ---------------- block-wide integer helpers ----------------
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int w = __shfl_up(v, o, 64);
+    if (lane >= o) v += w;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int clamp_prefix(const AttnArgs& a, int P) {
+  return P < 0 ? 0 : (P > a.max_prefix_len ? a.max_prefix_len : P);
+}
+// tiles of a sequence with prefix length P: prefix plus tree slots, 32 keys each
+__device__ __forceinline__ int tiles_of(const AttnArgs& a, int P) { return (P + a.N + kTile - 1) / kTile; }
+
+// Work decomposition.  A segment is (sequence b, KV head kh, row chunk rc),
+// numbered ((b * Hkv) + kh) * row_chunks + rc; a segment of sequence b has
+// tiles_of(P_b) tiles.
+//
+// Fixed pieces (one sequence): every segment is cut into `pieces` pieces of
+// T tiles (sized for the longest prefix); workgroup u runs piece u % pieces
+// of segment u / pieces and, unless that piece is the whole segment, leaves
+// its partial state in slot u.
+//
+// Balanced shares (several sequences, whose lengths only the device knows):
+// a lane is (KV head kh, row chunk rc), and the G workgroups split into
+// G / lanes shares per lane, workgroup u taking lane u % lanes and share
+// v = u / lanes, so the workgroups that run at the same time stream the same
+// blocks for every head.  Within a lane the tiles of all sequences, in order,
+// form one flat range of S tiles, cut into shares of T = max(minimum,
+// ceil(S / shares)) tiles.  Workgroup u runs every sequence its share
+// [v T, v T + T) touches: a sequence inside the share is written straight to
+// `out`, and one cut by a share boundary leaves its partial state in slot u
+// (the share's first sequence) or G + u (its last).  Workgroup 0 stores S and
+// T in the workspace header.
+struct Start {
+  int S, T;        // flat tiles, share length
+  int b, base;     // sequence holding the share's first tile (-1: none), and its first lane tile
+};
+
+template <int NW>
+__device__ Start balanced_start(const AttnArgs& a, int shares, int share_idx, int min_tiles, int* red,
+                               int* found) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  Start st;
+  // pass 1: tiles of one lane (and the prefix-length check)
+  int local = 0;
+  for (int b = tid; b < a.B; b += NW * 64) {
+    const int P = a.prefix_lens[b];
+    if (P < 0 || P > a.max_prefix_len) report(a.dev_status, TV_DEV_BAD_CACHE);
+    local += tiles_of(a, clamp_prefix(a, P));
+  }
+  local = wave_sum(local);
+  if (lane == 0) red[wave] = local;
+  __syncthreads();
+  int tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tot += red[w];
+  __syncthreads();
+  st.S = tot;
+  const int even = (st.S + shares - 1) / shares;
+  st.T = even > min_tiles ? even : min_tiles;
+  const int j0 = share_idx * st.T;
+  const bool write_starts = blockIdx.x == 0;  // the merge reads them from the header
+  if (j0 >= st.S && !write_starts) {
+    st.b = -1;
+    return st;
+  }
+  // pass 2: the sequence whose tiles hold j0
+  int running = 0;
+  for (int c = 0; c < a.B; c += NW * 64) {
+    const int b = c + tid;
+    const int v = b < a.B ? tiles_of(a, clamp_prefix(a, a.prefix_lens[b])) : 0;
+    const int incl = wave_inclusive_scan(v, lane);
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    int before = 0, chunk = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int x = red[w];
+      before += w < wave ? x : 0;
+      chunk += x;
+    }
+    const int start = running + before + incl - v;
+    if (write_starts && b < a.B) static_cast<int*>(a.workspace)[2 + b] = start;
+    if (b < a.B && start <= j0 && j0 < start + v) {
+      found[0] = b;
+      found[1] = start;
+    }
+    running += chunk;
+    __syncthreads();
+  }
+  st.b = j0 < st.S ? found[0] : -1;
+  st.base = found[1];
+  return st;
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   using C = Cfg<D, NW>;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  __shared__ int red[NW];
+  __shared__ int found[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5;   // which half of the key set this lane holds
   const int col = lane & 31;  // query row within the wave's 32 rows
-
-  // blockIdx.x = ((b * Hkv + kh) * nsplit + s) * row_chunks + rc
-  int idx = blockIdx.x;
-  const int rc = idx % mp.row_chunks;
-  idx /= mp.row_chunks;
-  const int s = idx % mp.nsplit;
-  idx /= mp.nsplit;
-  const int kh = idx % a.Hkv;
-  const int b = idx / a.Hkv;
-
   const int g = a.Hq / a.Hkv;
   const int R = g * a.N;
   const int W = (a.N + 63) >> 6;
-  int P = a.prefix_lens[b];
-  if (P < 0 || P > a.max_prefix_len) {
-    if (tid == 0) report(a.dev_status, TV_DEV_BAD_CACHE);
-    P = P < 0 ? 0 : a.max_prefix_len;
-  }
-  const int total = P + a.N;
-  const int ntiles = (total + kTile - 1) / kTile;
-  const int nblk = (total + kBlockSize - 1) / kBlockSize;
-  const int t0 = s * mp.tiles_per_split;
-  const int t1 = min(ntiles, t0 + mp.tiles_per_split);
-  if (t0 >= t1) return;  // whole workgroup: this split is past the sequence's end
-
-  const int32_t* __restrict__ table = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+  const int segs = a.Hkv * mp.row_chunks;  // segments per sequence
+  const int G = static_cast<int>(gridDim.x);
+  const int u = blockIdx.x;
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v_cache);
   const float c = a.scale * kLog2e;
+  const long block_stride = static_cast<long>(kBlockSize) * a.Hkv * D;  // elements per block
 
-  // every table entry this workgroup will use must name a block of the cache
-  for (int e = t0 * 2 + tid; e < min(t1 * 2, nblk); e += C::kThreads) {
-    const int v = table[e];
-    if (v < 0 || v >= a.num_blocks) report(a.dev_status, TV_DEV_BAD_CACHE);
-  }
-
-  // ---------------- tile copies: HBM -> LDS ----------------
+  // ---------------- per-thread parts of the copy and read addresses ----------------
   // Wave copy i of a K (or V) tile covers keys i*kKeysPerCopy .. +kKeysPerCopy-1
   // (all in one 16-token block); lane l writes chunk position l % kChunks of
   // key i*kKeysPerCopy + l / kChunks.  The source address is a wave-uniform
-  // block base plus a per-thread offset fixed for the whole kernel.
-  const int ckey = lane / C::kChunks, cpos = lane % C::kChunks;
-  const long block_stride = static_cast<long>(kBlockSize) * a.Hkv * D;  // elements per block
+  // block-and-head base plus a per-thread offset fixed for the whole kernel.
   int off_k[C::kCopiesPerWave], off_v[C::kCopiesPerWave];
-#pragma unroll
-  for (int j = 0; j < C::kCopiesPerWave; ++j) {
-    const int key = (j * NW + wave) * C::kKeysPerCopy + ckey;
-    const int row = ((key & 15) * a.Hkv + kh) * D;
-    off_k[j] = row + (cpos ^ (key & 7)) * 8;
-    off_v[j] = row + (cpos ^ (2 * (key & 3))) * 8;
-  }
-  // Block ids come through the constant address space: uniform reads become
-  // scalar loads, which never wait behind the in-flight tile copies.
-  const CONST_AS int32_t* table_s = (const CONST_AS int32_t*)table;
-  auto fetch_ids = [&](int tile, int& b0, int& b1) __attribute__((always_inline)) {
-    const int e0 = tile * 2;  // the tile spans table entries e0 and e0 + 1
-    b0 = e0 < nblk ? table_s[e0] : 0;
-    b1 = e0 + 1 < nblk ? table_s[e0 + 1] : 0;
-  };
-  auto issue_tile = [&](int stage, int b0, int b1) __attribute__((always_inline)) {
-    // ids past the end or out of range (reported above) read block 0; those
-    // keys are masked, and block 0 holds finite values like any other
-    b0 = (b0 >= 0 && b0 < a.num_blocks) ? b0 : 0;
-    b1 = (b1 >= 0 && b1 < a.num_blocks) ? b1 : 0;
-    uint16_t* kst = lds + stage * C::kStageElems;
-    uint16_t* vst = kst + C::kTileElems;
-#pragma unroll
-    for (int j = 0; j < C::kCopiesPerWave; ++j) {
-      const int copy = j * NW + wave;
-      const long base = static_cast<long>(copy * C::kKeysPerCopy < kBlockSize ? b0 : b1) * block_stride;
-      __builtin_amdgcn_global_load_lds((const void*)(kc + base + off_k[j]), (LDS_AS void*)(kst + copy * 512), 16,
-                                       0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vc + base + off_v[j]), (LDS_AS void*)(vst + copy * 512), 16,
-                                       0, 0);
-    }
-  };
-
-  // ---------------- this wave's 32 query rows (B operand of S^T) ----------------
-  const int row0 = rc * C::kRows + wave * 32;
-  const bool active = row0 < R;
-  const int r_me = row0 + col;
-  bf16x8 qreg[C::kKs];
-  uint64_t mw[4];
   {
-    const int rr = r_me < R ? r_me : R - 1;
-    const int node = rr / g, hg = rr % g;
-    const u32x4* qp = reinterpret_cast<const u32x4*>(
-        static_cast<const uint16_t*>(a.q) +
-        ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D);
+    const int ckey = lane / C::kChunks, cpos = lane % C::kChunks;
 #pragma unroll
-    for (int kk = 0; kk < C::kKs; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (r_me < R) v = qp[kk * 2 + hh];
-      qreg[kk] = __builtin_bit_cast(bf16x8, v);
+    for (int jj = 0; jj < C::kCopiesPerWave; ++jj) {
+      const int key = (jj * NW + wave) * C::kKeysPerCopy + ckey;
+      const int row = (key & 15) * a.Hkv * D;
+      off_k[jj] = row + (cpos ^ (key & 7)) * 8;
+      off_v[jj] = row + (cpos ^ (2 * (key & 3))) * 8;
     }
-    const uint64_t* mrow = a.mask + (static_cast<size_t>(b) * a.N + node) * W;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) mw[w] = (w < W) ? mrow[w] : 0ull;
   }
-  // the query and mask loads must not count against the copy waits below
-  wait_vmcnt<0>();
-
   // per-lane parts of the V^T transpose-read addresses (see the header)
   const int tq = lane >> 4, ts = lane & 15;
   const int tr_row = 4 * hh + (ts >> 2);                 // + 16 * chunk (+ 8 for keys 4..7)
@@ -283,223 +325,376 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   const int tr_half = (ts & 1) * 4;
   const int tr_swz = 2 * ((ts >> 2) & 3);                // 2 * (row % 4)
 
-  // ---------------- softmax state and output accumulators ----------------
-  f32x16 acc[C::kDb];
+  // One piece: tiles [t0, t1) of segment (b, kh, rc) whose sequence has
+  // prefix length P (raw, checked here).  `whole` pieces write bf16 outputs,
+  // the others their partial state into `slot`.
+  auto run_piece = [&](int b, int kh, int rc, int Praw, int t0, int t1, bool whole,
+                       int slot) __attribute__((always_inline)) {
+    // ---- this wave's 32 query rows and their mask words (issued first) ----
+    const int rl = wave * 32 + col;  // row within the chunk
+    const int row0 = rc * C::kRows + wave * 32;
+    const bool active = row0 < R;
+    const int r_me = row0 + col;
+    bf16x8 qreg[C::kKs];
+    uint64_t mw[4];
+    {
+      const int rr = r_me < R ? r_me : R - 1;
+      const int node = rr / g, hg = rr % g;
+      const u32x4* qp = reinterpret_cast<const u32x4*>(
+          static_cast<const uint16_t*>(a.q) +
+          ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D);
 #pragma unroll
-  for (int db = 0; db < C::kDb; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  float m_c = -INFINITY;  // running maximum, already multiplied by c
-  float l_run = 0.f;
-
-  auto compute_tile = [&](int stage, int tile) __attribute__((always_inline)) {
-    const uint16_t* ks = lds + stage * C::kStageElems;
-    const uint16_t* vs = ks + C::kTileElems;
-    const int tb = tile * kTile;
-    f32x16 sc = {};
-#pragma unroll
-    for (int kk = 0; kk < C::kKs; ++kk) {
-      const int ch = kk * 2 + hh;
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(ks + col * D + ((ch ^ (col & 7)) * 8));
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[kk], sc, 0, 0, 0);
-    }
-    // V^T operands of the whole tile, read now so the reads overlap the softmax
-    u32x4 vop[2][C::kDb];
-#pragma unroll
-    for (int kc2 = 0; kc2 < 2; ++kc2) {
-      const int r1 = 16 * kc2 + tr_row, r2 = r1 + 8;
-#pragma unroll
-      for (int db = 0; db < C::kDb; ++db) {
-        const int chk = (4 * db + tr_chunk) ^ tr_swz;
-        const u32x2 lo = ds_read_tr16_b64(vs + r1 * D + chk * 8 + tr_half);
-        const u32x2 hi = ds_read_tr16_b64(vs + r2 * D + chk * 8 + tr_half);
-        vop[kc2][db][0] = lo[0];
-        vop[kc2][db][1] = lo[1];
-        vop[kc2][db][2] = hi[0];
-        vop[kc2][db][3] = hi[1];
+      for (int kk = 0; kk < C::kKs; ++kk) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r_me < R) v = qp[kk * 2 + hh];
+        qreg[kk] = __builtin_bit_cast(bf16x8, v);
       }
-    }
-    if (tb + kTile > P) {  // the tile reaches the tree slots or the end: mask
-      const uint64_t vis = tile_visibility(mw, tb, P) >> (4 * hh);
+      const uint64_t* mrow = a.mask + (static_cast<size_t>(b) * a.N + node) * W;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int bit = 8 * (r >> 2) + (r & 3);
-        sc[r] = ((vis >> bit) & 1ull) ? sc[r] : -INFINITY;
+      for (int w = 0; w < 4; ++w) mw[w] = (w < W) ? mrow[w] : 0ull;
+    }
+
+    // ---- block ids: scalar loads through the constant address space, which
+    // never wait behind the in-flight tile copies; reads stop at the table
+    // row's end, and entries past the sequence's blocks are replaced by 0 ----
+    const int32_t* table = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+    const CONST_AS int32_t* table_s = (const CONST_AS int32_t*)table;
+    const int maxb = a.max_blocks;
+    auto fetch_ids = [&](int tile, int& b0, int& b1) __attribute__((always_inline)) {
+      const int e0 = tile * 2;  // the tile spans table entries e0 and e0 + 1
+      b0 = e0 < maxb ? table_s[e0] : 0;
+      b1 = e0 + 1 < maxb ? table_s[e0 + 1] : 0;
+    };
+    int nb0, nb1;  // block ids of the next tile to issue
+    fetch_ids(t0, nb0, nb1);
+
+    const bool bad_len = Praw < 0 || Praw > a.max_prefix_len;
+    const int P = clamp_prefix(a, Praw);
+    const int nblk = (P + a.N + kBlockSize - 1) / kBlockSize;
+    const long head_off = static_cast<long>(kh) * D;
+    auto issue_tile = [&](int stage, int tile, int b0, int b1) __attribute__((always_inline)) {
+      const int e0 = tile * 2;
+      b0 = e0 < nblk ? b0 : 0;
+      b1 = e0 + 1 < nblk ? b1 : 0;
+      // an id outside the cache is reported and replaced by block 0 (finite values)
+      if (b0 < 0 || b0 >= a.num_blocks || b1 < 0 || b1 >= a.num_blocks) {
+        if (tid == 0) report(a.dev_status, TV_DEV_BAD_CACHE);
+        b0 = (b0 >= 0 && b0 < a.num_blocks) ? b0 : 0;
+        b1 = (b1 >= 0 && b1 < a.num_blocks) ? b1 : 0;
       }
-    }
-    float mt = sc[0];
+      uint16_t* kst = lds + stage * C::kStageElems;
+      uint16_t* vst = kst + C::kTileElems;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
-    mt = pair_max(mt) * c;
-    // lazy rescale: raise m only when a row's maximum grew by more than 2^8
-    const bool grow = mt > m_c + kLazyRescale;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float mn = grow ? mt : m_c;
-      // rows that do not grow keep alpha = 1 (their m may still be -inf)
-      const float alpha = grow ? exp2_fast(m_c - mn) : 1.f;  // 0 on the first visible keys
-      m_c = mn;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::kDb; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-    }
-    const float mcs = (m_c == -INFINITY) ? 0.f : m_c;  // no visible key yet: p = 0
-    u32x4 pw[2];
-    float lsum0 = 0.f, lsum1 = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = exp2_fast(__builtin_fmaf(sc[r], c, -mcs));
-      const float p1 = exp2_fast(__builtin_fmaf(sc[r + 1], c, -mcs));
-      lsum0 += p0;
-      lsum1 += p1;
-      pw[r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
-    }
-    l_run += lsum0 + lsum1;
-    // the transpose reads above are invisible to the compiler's wait
-    // tracking: wait for them here, with their results as operands so that
-    // no use can be scheduled above the wait
-    lds_wait_operands(vop);
-    // O^T += V^T P^T over the two 16-key chunks of the tile
-#pragma unroll
-    for (int kc2 = 0; kc2 < 2; ++kc2) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kc2]);
-#pragma unroll
-      for (int db = 0; db < C::kDb; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[kc2][db]), pb,
-                                                          acc[db], 0, 0, 0);
-    }
-  };
+      for (int jj = 0; jj < C::kCopiesPerWave; ++jj) {
+        const int copy = jj * NW + wave;
+        const long base = static_cast<long>(copy * C::kKeysPerCopy < kBlockSize ? b0 : b1) * block_stride + head_off;
+        __builtin_amdgcn_global_load_lds((const void*)(kc + base + off_k[jj]), (LDS_AS void*)(kst + copy * 512),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vc + base + off_v[jj]), (LDS_AS void*)(vst + copy * 512),
+                                         16, 0, 0);
+      }
+    };
 
-  // wait until this wave's copies of the tile about to be used are done:
-  // `later` tiles (at most kStages - 2) have been issued after it
-  auto wait_tile = [&](int later) __attribute__((always_inline)) {
-    static_assert(kStages >= 2 && kStages <= 6, "wait_tile covers 0..4 later tiles");
-    if (later >= 4)
-      wait_vmcnt<4 * C::kDmaPerTile>();
-    else if (later == 3)
-      wait_vmcnt<3 * C::kDmaPerTile>();
-    else if (later == 2)
-      wait_vmcnt<2 * C::kDmaPerTile>();
-    else if (later == 1)
-      wait_vmcnt<C::kDmaPerTile>();
-    else
-      wait_vmcnt<0>();
-  };
-
-  // ---------------- main loop ----------------
-  int nb0, nb1;  // block ids of the next tile to issue
-  fetch_ids(t0, nb0, nb1);
-#pragma unroll
-  for (int i = 0; i < kStages - 1; ++i) {
-    if (t0 + i < t1) {
-      const int b0 = nb0, b1 = nb1;
-      fetch_ids(t0 + i + 1, nb0, nb1);
-      issue_tile(i, b0, b1);
-    }
-  }
-  for (int tile = t0; tile < t1; ++tile) {
-    const int stage = (tile - t0) % kStages;
-    wait_tile(min(kStages - 2, t1 - 1 - tile));
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // every wave's copies landed; tile - 1 is done
-    __asm__ volatile("" ::: "memory");
-    const int nt = tile + kStages - 1;
-    if (nt < t1) issue_tile((nt - t0) % kStages, nb0, nb1);
-    if (active) compute_tile(stage, tile);
-    if (nt < t1) fetch_ids(nt + 1, nb0, nb1);  // ready by the next issue
-  }
-
-  // ---------------- epilogue ----------------
-  if (!active) return;
-  const float lt = pair_sum(l_run);
-  if (r_me >= R) return;
-  const int node = r_me / g, hg = r_me % g;
-  if (mp.nsplit == 1) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* op = static_cast<uint16_t*>(a.out) +
-                   ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D;
+    f32x16 acc[C::kDb];
 #pragma unroll
     for (int db = 0; db < C::kDb; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = db * 32 + 8 * j + 4 * hh;
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv);
-        w[1] = pack_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + d) = w;
-      }
-  } else {
-    // partial state of this split: rows [B][Hkv][nsplit][R]
-    const size_t prow = ((static_cast<size_t>(b) * a.Hkv + kh) * mp.nsplit + s) * R + r_me;
-    const size_t nprow = static_cast<size_t>(a.B) * a.Hkv * mp.nsplit * R;
-    float* po = static_cast<float*>(a.workspace) + prow * D;
-    float* pm = static_cast<float*>(a.workspace) + nprow * D;
-    float* pl = pm + nprow;
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    float m_c = -INFINITY;  // running maximum, already multiplied by c
+    float l_run = 0.f;
+
+    auto compute_tile = [&](int stage, int tile) __attribute__((always_inline)) {
+        const uint16_t* ks = lds + stage * C::kStageElems;
+        const uint16_t* vs = ks + C::kTileElems;
+        const int tb = tile * kTile;
+        f32x16 sc = {};
+    #pragma unroll
+        for (int kk = 0; kk < C::kKs; ++kk) {
+          const int ch = kk * 2 + hh;
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(ks + col * D + ((ch ^ (col & 7)) * 8));
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[kk], sc, 0, 0, 0);
+        }
+        // V^T operands of the whole tile, read now so the reads overlap the softmax
+        u32x4 vop[2][C::kDb];
+    #pragma unroll
+        for (int kc2 = 0; kc2 < 2; ++kc2) {
+          const int r1 = 16 * kc2 + tr_row, r2 = r1 + 8;
+    #pragma unroll
+          for (int db = 0; db < C::kDb; ++db) {
+            const int chk = (4 * db + tr_chunk) ^ tr_swz;
+            const u32x2 lo = ds_read_tr16_b64(vs + r1 * D + chk * 8 + tr_half);
+            const u32x2 hi = ds_read_tr16_b64(vs + r2 * D + chk * 8 + tr_half);
+            vop[kc2][db][0] = lo[0];
+            vop[kc2][db][1] = lo[1];
+            vop[kc2][db][2] = hi[0];
+            vop[kc2][db][3] = hi[1];
+          }
+        }
+        if (tb + kTile > P) {  // the tile reaches the tree slots or the end: mask
+          const uint64_t vis = tile_visibility(mw, tb, P) >> (4 * hh);
+    #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int bit = 8 * (r >> 2) + (r & 3);
+            sc[r] = ((vis >> bit) & 1ull) ? sc[r] : -INFINITY;
+          }
+        }
+        float mt = sc[0];
+    #pragma unroll
+        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+        mt = pair_max(mt) * c;
+        // lazy rescale: raise m only when a row's maximum grew by more than 2^8
+        const bool grow = mt > m_c + kLazyRescale;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float mn = grow ? mt : m_c;
+          // rows that do not grow keep alpha = 1 (their m may still be -inf)
+          const float alpha = grow ? exp2_fast(m_c - mn) : 1.f;  // 0 on the first visible keys
+          m_c = mn;
+          l_run *= alpha;
+    #pragma unroll
+          for (int db = 0; db < C::kDb; ++db)
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        }
+        const float mcs = (m_c == -INFINITY) ? 0.f : m_c;  // no visible key yet: p = 0
+        u32x4 pw[2];
+        float lsum0 = 0.f, lsum1 = 0.f;
+    #pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = exp2_fast(__builtin_fmaf(sc[r], c, -mcs));
+          const float p1 = exp2_fast(__builtin_fmaf(sc[r + 1], c, -mcs));
+          lsum0 += p0;
+          lsum1 += p1;
+          pw[r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
+        }
+        l_run += lsum0 + lsum1;
+        // the transpose reads above are invisible to the compiler's wait
+        // tracking: wait for them here, with their results as operands so that
+        // no use can be scheduled above the wait
+        lds_wait_operands(vop);
+        // O^T += V^T P^T over the two 16-key chunks of the tile
+    #pragma unroll
+        for (int kc2 = 0; kc2 < 2; ++kc2) {
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kc2]);
+    #pragma unroll
+          for (int db = 0; db < C::kDb; ++db)
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[kc2][db]), pb,
+                                                              acc[db], 0, 0, 0);
+        }
+    };
+
+    // wait until this wave's copies of the tile about to be used are done:
+    // `later` tiles (at most C::kStages - 2) have been issued after it
+    auto wait_tile = [&](int later) __attribute__((always_inline)) {
+      static_assert(C::kStages >= 2 && C::kStages <= 6, "wait_tile covers 0..4 later tiles");
+      if (later >= 4)
+        wait_vmcnt<4 * C::kDmaPerTile>();
+      else if (later == 3)
+        wait_vmcnt<3 * C::kDmaPerTile>();
+      else if (later == 2)
+        wait_vmcnt<2 * C::kDmaPerTile>();
+      else if (later == 1)
+        wait_vmcnt<C::kDmaPerTile>();
+      else
+        wait_vmcnt<0>();
+    };
+
+    // ---- tile pipeline ----
+    // the ring may still be read by the previous piece's last tile (every
+    // wave's LDS reads of it completed before its last MFMAs)
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    if (bad_len && tid == 0) report(a.dev_status, TV_DEV_BAD_CACHE);
 #pragma unroll
-    for (int db = 0; db < C::kDb; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = db * 32 + 8 * j + 4 * hh;
-        float4 v;
-        v.x = acc[db][4 * j];
-        v.y = acc[db][4 * j + 1];
-        v.z = acc[db][4 * j + 2];
-        v.w = acc[db][4 * j + 3];
-        *reinterpret_cast<float4*>(po + d) = v;
+    for (int i = 0; i < C::kStages - 1; ++i) {
+      if (t0 + i < t1) {
+        const int b0 = nb0, b1 = nb1;
+        fetch_ids(t0 + i + 1, nb0, nb1);
+        issue_tile(i, t0 + i, b0, b1);
       }
-    if (hh == 0) {
-      pm[prow] = m_c;
-      pl[prow] = lt;
     }
+    // the query and mask loads went out before these copies; draining here
+    // keeps them out of the per-tile copy waits
+    wait_vmcnt<0>();
+    for (int tile = t0; tile < t1; ++tile) {
+      const int stage = (tile - t0) % C::kStages;
+      wait_tile(min(C::kStages - 2, t1 - 1 - tile));
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();  // every wave's copies landed; tile - 1 is done
+      __asm__ volatile("" ::: "memory");
+      const int nt = tile + C::kStages - 1;
+      if (nt < t1) issue_tile((nt - t0) % C::kStages, nt, nb0, nb1);
+      if (active) compute_tile(stage, tile);
+      if (nt < t1) fetch_ids(nt + 1, nb0, nb1);  // ready by the next issue
+    }
+
+    // ---- piece epilogue ----
+    if (!active) return;
+    const float lt = pair_sum(l_run);
+    if (r_me >= R) return;
+    if (whole) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int node = r_me / g, hg = r_me % g;
+      uint16_t* op = static_cast<uint16_t*>(a.out) +
+                     ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D;
+#pragma unroll
+      for (int db = 0; db < C::kDb; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = db * 32 + 8 * jj + 4 * hh;
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[db][4 * jj] * inv, acc[db][4 * jj + 1] * inv);
+          w[1] = pack_bf16x2(acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + d) = w;
+        }
+    } else {
+      // output partials are [slot][D/4][row] float4, so that one store
+      // instruction writes two runs of 32 consecutive rows (whole lines)
+      const size_t nslots = static_cast<size_t>(mp.balanced ? 2 * G : G) * C::kRows;
+      const size_t prow = static_cast<size_t>(slot) * C::kRows + rl;
+      float* ws = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + header_bytes(a.B));
+      float4* po = reinterpret_cast<float4*>(ws) + static_cast<size_t>(slot) * (D / 4) * C::kRows + rl;
+      float* pm = ws + nslots * D;
+      float* pl = pm + nslots;
+#pragma unroll
+      for (int db = 0; db < C::kDb; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int q = db * 8 + 2 * jj + hh;  // dims 4q .. 4q + 3
+          float4 v;
+          v.x = acc[db][4 * jj];
+          v.y = acc[db][4 * jj + 1];
+          v.z = acc[db][4 * jj + 2];
+          v.w = acc[db][4 * jj + 3];
+          po[static_cast<size_t>(q) * C::kRows] = v;
+        }
+      if (hh == 0) {
+        pm[prow] = m_c;
+        pl[prow] = lt;
+      }
+    }
+  };
+
+  if (!mp.balanced) {
+    // ---------------- fixed pieces ----------------
+    const int seg_id = u / mp.pieces, piece = u % mp.pieces;
+    const int b = seg_id / segs, seg = seg_id % segs;
+    const int Praw = a.prefix_lens[b];
+    const int ntiles = tiles_of(a, clamp_prefix(a, Praw));
+    const int t0 = piece * mp.T;
+    if (t0 >= ntiles) return;  // whole workgroup: the sequence is shorter than the longest
+    const int t1 = min(ntiles, t0 + mp.T);
+    run_piece(b, seg / mp.row_chunks, seg % mp.row_chunks, Praw, t0, t1, t0 == 0 && t1 == ntiles, u);
+    return;
+  }
+
+  // ---------------- balanced shares ----------------
+  const int lanes = a.Hkv * mp.row_chunks;
+  const int lane_id = u % lanes, share = u / lanes;
+  const int kh = lane_id / mp.row_chunks, rc = lane_id % mp.row_chunks;
+  const Start st = balanced_start<NW>(a, G / lanes, share, mp.T, red, found);
+  if (u == 0 && tid == 0) {
+    int* hdr = static_cast<int*>(a.workspace);
+    hdr[0] = st.S;
+    hdr[1] = st.T;
+  }
+  if (st.b < 0) return;  // whole workgroup: the lane's tiles ended before this share
+  const int j1 = min(st.S, share * st.T + st.T);
+  int j = share * st.T;
+  int b = st.b, seq_base = st.base;
+  int Praw = a.prefix_lens[b];
+  int ntiles = tiles_of(a, clamp_prefix(a, Praw));
+  bool first = true;
+  while (j < j1) {
+    while (j >= seq_base + ntiles) {  // the share continues into the next sequence
+      seq_base += ntiles;
+      ++b;
+      Praw = a.prefix_lens[b];
+      ntiles = tiles_of(a, clamp_prefix(a, Praw));
+    }
+    const int t0 = j - seq_base;
+    const int t1 = min(ntiles, t0 + (j1 - j));
+    run_piece(b, kh, rc, Praw, t0, t1, t0 == 0 && t1 == ntiles, first ? u : G + u);
+    j += t1 - t0;
+    first = false;
   }
 }
 
-// Merge the per-split partial states (log-sum-exp rule) and write bf16
-// outputs.  Each thread owns 4 dims of one row: a workgroup of 256 threads
-// covers 1024 / D rows of one (sequence, KV head).
-template <int D>
+// Merge the partial states of segments that several workgroups shared
+// (log-sum-exp rule) and write bf16 outputs.  Workgroup (segment, block of
+// 32 rows x 8 four-dim chunks): each thread owns 4 dims of one row (threads
+// of a wave take consecutive rows, matching the partial layout) and walks
+// the segment's pieces.
+template <int D, int NW>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, MfmaParams mp) {
-  constexpr int kTpr = D / 4;  // threads per row
-  constexpr int kRowsPerBlock = 256 / kTpr;
+  using C = Cfg<D, NW>;
+  constexpr int kQBlocks = D / 4 / 8;                  // 8 chunks of 4 dims per workgroup
+  constexpr int kBlocksPerSeg = C::kRows / 32 * kQBlocks;
+  const int tid = threadIdx.x;
+  const int segs = a.Hkv * mp.row_chunks;
+  const int seg_id = blockIdx.x / kBlocksPerSeg;  // ((b * Hkv) + kh) * row_chunks + rc
+  const int blk = blockIdx.x % kBlocksPerSeg;
+  const int b = seg_id / segs, seg = seg_id % segs;
+  const int kh = seg / mp.row_chunks, rc = seg % mp.row_chunks;
   const int g = a.Hq / a.Hkv;
   const int R = g * a.N;
-  const int blocks_per_head = (R + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int bh = blockIdx.x / blocks_per_head;  // b * Hkv + kh
-  const int r = (blockIdx.x % blocks_per_head) * kRowsPerBlock + threadIdx.x / kTpr;
-  const int d = (threadIdx.x % kTpr) * 4;
-  if (r >= R) return;
-  const int kh = bh % a.Hkv;
-  const int b = bh / a.Hkv;
-  int P = a.prefix_lens[b];
-  P = P < 0 ? 0 : (P > a.max_prefix_len ? a.max_prefix_len : P);
-  const int ntiles = (P + a.N + kTile - 1) / kTile;
-  const int ns = min(mp.nsplit, (ntiles + mp.tiles_per_split - 1) / mp.tiles_per_split);
-  const size_t nprow = static_cast<size_t>(a.B) * a.Hkv * mp.nsplit * R;
-  const float* po = static_cast<const float*>(a.workspace);
-  const float* pm = po + nprow * D;
-  const float* pl = pm + nprow;
-  const size_t base = static_cast<size_t>(bh) * mp.nsplit * R + r;
+  const int G = mp.grid;
+  const int rows = min(C::kRows, R - rc * C::kRows);
+  const int rl = (blk / kQBlocks) * 32 + (tid & 31);
+  const int q = (blk % kQBlocks) * 8 + (tid >> 5);
+  if ((blk / kQBlocks) * 32 >= rows) return;  // whole workgroup: rows past the chunk's end
+  const int ntiles = tiles_of(a, clamp_prefix(a, a.prefix_lens[b]));
 
+  int first_slot_lo, npieces, T;  // pieces are slots first_slot_lo.. (see below)
+  int f = 0, F = 0;
+  if (!mp.balanced) {
+    T = mp.T;
+    npieces = (ntiles + T - 1) / T;
+    first_slot_lo = seg_id * mp.pieces;
+  } else {
+    const int* hdr = static_cast<const int*>(a.workspace);
+    T = hdr[1];
+    F = hdr[2 + b];  // index of this sequence's first tile in its lane
+    f = F / T;
+    npieces = (F + ntiles - 1) / T - f + 1;
+    first_slot_lo = seg;  // the lane: workgroup of share v is v * lanes + lane
+  }
+  if (npieces <= 1) return;  // one workgroup ran the whole segment and wrote it
+  if (rl >= rows) return;
+
+  const size_t nslots = static_cast<size_t>(mp.balanced ? 2 * G : G) * C::kRows;
+  const float* ws = reinterpret_cast<const float*>(static_cast<const char*>(a.workspace) + header_bytes(a.B));
+  const float4* po = reinterpret_cast<const float4*>(ws);
+  const float* pm = ws + nslots * D;
+  const float* pl = pm + nslots;
+  auto slot_of = [&](int k) __attribute__((always_inline)) {
+    if (!mp.balanced) return first_slot_lo + k;
+    const int uu = (f + k) * segs + first_slot_lo;  // workgroup of share f + k in this lane
+    return (k == 0 && F != f * T) ? G + uu : uu;
+  };
   float M = -INFINITY;
-  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, pm[base + static_cast<size_t>(sp) * R]);
+#pragma unroll 8
+  for (int k = 0; k < npieces; ++k) M = fmaxf(M, pm[static_cast<size_t>(slot_of(k)) * C::kRows + rl]);
   const float Ms = (M == -INFINITY) ? 0.f : M;
   float4 o = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  for (int sp = 0; sp < ns; ++sp) {
-    const size_t pr = base + static_cast<size_t>(sp) * R;
+#pragma unroll 8
+  for (int k = 0; k < npieces; ++k) {
+    const size_t sl = static_cast<size_t>(slot_of(k));
+    const size_t pr = sl * C::kRows + rl;
     const float w = exp2_fast(pm[pr] - Ms);
     L += w * pl[pr];
-    const float4 v = *reinterpret_cast<const float4*>(po + pr * D + d);
+    const float4 v = po[(sl * (D / 4) + q) * C::kRows + rl];
     o.x += w * v.x;
     o.y += w * v.y;
     o.z += w * v.z;
     o.w += w * v.w;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int r = rc * C::kRows + rl;
   const int node = r / g, hg = r % g;
   uint16_t* op = static_cast<uint16_t*>(a.out) +
-                 ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D + d;
+                 ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D + 4 * q;
   u32x2 w;
   w[0] = pack_bf16x2(o.x * inv, o.y * inv);
   w[1] = pack_bf16x2(o.z * inv, o.w * inv);
@@ -509,39 +704,57 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, MfmaParam
 template <int D, int NW>
 hipError_t launch_cfg(const AttnArgs& a, const MfmaParams& mp, hipStream_t stream) {
   using C = Cfg<D, NW>;
-  const long blocks = static_cast<long>(a.B) * a.Hkv * mp.nsplit * mp.row_chunks;
-  const size_t shmem = kStages * C::kStageElems * sizeof(uint16_t);
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NW>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(C::kThreads), shmem, stream, a, mp);
+  const size_t shmem = C::kStages * C::kStageElems * sizeof(uint16_t);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NW>), dim3(static_cast<unsigned>(mp.grid)), dim3(C::kThreads),
+                     shmem, stream, a, mp);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || mp.nsplit == 1) return e;
-  constexpr int kRowsPerBlock = 256 / (D / 4);
-  const int R = (a.Hq / a.Hkv) * a.N;
-  const long cblocks = static_cast<long>(a.B) * a.Hkv * ((R + kRowsPerBlock - 1) / kRowsPerBlock);
-  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(static_cast<unsigned>(cblocks)), dim3(256), 0,
-                     stream, a, mp);
+  if (e != hipSuccess) return e;
+  if (!mp.balanced ? mp.pieces == 1 : mp.grid == a.Hkv * mp.row_chunks) return e;  // no segment is ever shared
+  constexpr int kBlocksPerSeg = C::kRows / 32 * (D / 4 / 8);
+  const long blocks = static_cast<long>(a.B) * a.Hkv * mp.row_chunks * kBlocksPerSeg;
+  hipLaunchKernelGGL((attn_combine_kernel<D, NW>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     a, mp);
   return hipGetLastError();
 }
 
-constexpr int kTargetBlocks = 512;
-constexpr int kMinTilesPerSplit = 4;
+// MI355X: 256 compute units.  A 4-wave workgroup takes 64 KB of LDS, so two
+// fit on a compute unit (two waves per SIMD); an 8-wave workgroup fills the
+// SIMDs at two waves each by itself.
+constexpr int kComputeUnits = 256;
+constexpr int kMinTilesPerPiece = 4;
 
 // Rows of a KV head go to workgroups of 4 waves (128 rows) or, for D = 128
-// and more than 128 rows, 8 waves (256 rows); the key range is split so that
-// the grid has about kTargetBlocks workgroups.
+// and more than 128 rows, 8 waves (256 rows).  One sequence: fixed pieces,
+// about one round of resident workgroups.  Several sequences: balanced
+// shares over one round of resident workgroups, or fewer when the work
+// (bounded by max_prefix_len) would give shares under kMinTilesPerPiece.
 MfmaParams plan_for(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
   const int R = (Hq / Hkv) * N;
   MfmaParams p;
   p.waves = (D == 128 && R > 128) ? 8 : 4;
   p.row_chunks = (R + p.waves * 32 - 1) / (p.waves * 32);
-  const int max_tiles = (max_prefix_len + N + kTile - 1) / kTile;
-  const long base = static_cast<long>(B) * Hkv * p.row_chunks;
-  long want = (kTargetBlocks + base - 1) / base;
-  const long cap = (max_tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
-  if (want > cap) want = cap;
-  if (want < 1) want = 1;
-  p.tiles_per_split = static_cast<int>((max_tiles + want - 1) / want);
-  p.nsplit = (max_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  const long max_tiles = (static_cast<long>(max_prefix_len) + N + kTile - 1) / kTile;
+  const long segments = static_cast<long>(B) * Hkv * p.row_chunks;
+  const long resident = static_cast<long>(kComputeUnits) * (p.waves == 8 ? 1 : 2);
+  if (B == 1) {
+    long pieces = (resident + segments - 1) / segments;
+    const long cap = (max_tiles + kMinTilesPerPiece - 1) / kMinTilesPerPiece;
+    if (pieces > cap) pieces = cap;
+    if (pieces < 1) pieces = 1;
+    p.balanced = 0;
+    p.T = static_cast<int>((max_tiles + pieces - 1) / pieces);
+    p.pieces = static_cast<int>((max_tiles + p.T - 1) / p.T);
+    p.grid = static_cast<int>(segments * p.pieces);
+  } else {
+    const long lanes = static_cast<long>(Hkv) * p.row_chunks;
+    long shares = (B * max_tiles + kMinTilesPerPiece - 1) / kMinTilesPerPiece;
+    if (shares > resident / lanes) shares = resident / lanes;
+    if (shares < 1) shares = 1;
+    p.balanced = 1;
+    p.T = kMinTilesPerPiece;
+    p.pieces = 0;
+    p.grid = static_cast<int>(shares * lanes);
+  }
   return p;
 }
 
@@ -549,9 +762,8 @@ MfmaParams plan_for(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
 
 size_t attention_mfma_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
   const MfmaParams p = plan_for(B, N, Hq, Hkv, D, max_prefix_len);
-  if (p.nsplit == 1) return 0;
-  const size_t rows = static_cast<size_t>(B) * Hkv * p.nsplit * (Hq / Hkv) * N;
-  return rows * (D + 2) * sizeof(float);
+  const size_t slots = static_cast<size_t>(p.balanced ? 2 * p.grid : p.grid) * p.waves * 32;
+  return header_bytes(B) + slots * (D + 2) * sizeof(float);
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
