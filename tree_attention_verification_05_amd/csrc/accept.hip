@@ -124,29 +124,48 @@ __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int
   __shared__ int s_par[TV_MAX_NODES], s_tok[TV_MAX_NODES], s_am[TV_MAX_NODES];
   __shared__ int s_ok[TV_MAX_NODES], s_dep[TV_MAX_NODES], s_on[TV_MAX_NODES];
   __shared__ int s_bad, s_dmax, s_path[TV_MAX_NODES];
+  __shared__ unsigned long long s_key[TV_MAX_NODES];
 
   const int N = a.N, V = a.V;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t* keys = static_cast<const uint64_t*>(a.workspace);
+  const size_t base = static_cast<size_t>(b) * N;
+  // the tree and the draft tokens are loaded first; their latency overlaps
+  // the chunk keys below
+  for (int i = tid; i < N; i += kThreads) {
+    s_par[i] = a.parents[base + i];
+    s_tok[i] = a.draft_tokens[base + i];
+    s_on[i] = 0;
+    s_key[i] = 0ull;
+  }
   if (tid == 0) {
     s_bad = 0;
     s_dmax = 0;
   }
-  const size_t base = static_cast<size_t>(b) * N;
-  for (int i = tid; i < N; i += kThreads) {
-    const uint64_t* kr = keys + (base + i) * chunks;
-    uint64_t k = kr[0];
-    for (int c = 1; c < chunks; ++c) {
-      const uint64_t w = kr[c];
-      k = w > k ? w : k;
+  __syncthreads();
+  // every (node, chunk) key of the sequence, contiguous in the workspace:
+  // eight loads in flight per thread, then folded per node with LDS max
+  const uint64_t* kb = keys + base * chunks;
+  const int nk = N * chunks;
+  for (int k0 = tid; k0 < nk; k0 += 8 * kThreads) {
+    uint64_t kv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u * kThreads;
+      kv[u] = k < nk ? kb[k] : 0ull;
     }
-    const int am = key_index(k);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u * kThreads;
+      if (k < nk) atomicMax(&s_key[k / chunks], static_cast<unsigned long long>(kv[u]));
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < N; i += kThreads) {
+    const int am = key_index(s_key[i]);
     s_am[i] = am;
     if (a.target_argmax) a.target_argmax[base + i] = am;
-    s_par[i] = a.parents[base + i];
-    s_tok[i] = a.draft_tokens[base + i];
-    s_on[i] = 0;
   }
   __syncthreads();
 

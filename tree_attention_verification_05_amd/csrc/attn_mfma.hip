@@ -52,6 +52,8 @@
 // keys outside the row's ancestor set (branch-free).  A segment shared by
 // several workgroups leaves (m, denominator, unnormalised output) in fp32 per
 // piece, merged with the log-sum-exp rule.
+#include <type_traits>
+
 #include "tv_internal.h"
 
 namespace tv {
@@ -126,15 +128,35 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// ds_read_b64_tr_b16 issued as inline assembly.  The compiler cannot tell
-// this LDS read from the in-flight LDS copies and would drain them all
-// (vmcnt(0)) before it; the caller instead waits with lds_wait_operands,
-// which the copies into other buffers never block.
-__device__ __forceinline__ u32x2 ds_read_tr16_b64(const uint16_t* p) {
+// ds_read_b64_tr_b16 issued as inline assembly, at a byte address plus an
+// immediate offset.  The compiler cannot tell this LDS read from the
+// in-flight LDS copies and would drain them all (vmcnt(0)) before it; the
+// caller instead waits with lds_wait_operands, which the copies into other
+// buffers never block.
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
   u32x2 v;
-  const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS const void*)p));
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
   return v;
+}
+
+// One wave copies 64 x 16 bytes from a buffer (base, range in bytes;
+// per-lane byte offset) into LDS: lane l's bytes land at dst + 16 l.  Reads
+// past the range return zeros.  (A plain device function: lambdas would also
+// be compiled for the host, which has no buffer resources.)
+__device__ __forceinline__ void copy_to_lds(const char* base, int range, int voff, uint16_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, range, 0x00020000),
+      (LDS_AS void*)dst, 16, voff, 0, 0, 0);
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 // s_waitcnt lgkmcnt(0) taking the transpose-read results as operands, so no
@@ -288,7 +310,10 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   __shared__ int found[2];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // the wave index is uniform across the wave; saying so keeps block bases,
+  // buffer descriptors and LDS destinations in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;   // which half of the key set this lane holds
   const int col = lane & 31;  // query row within the wave's 32 rows
   const int g = a.Hq / a.Hkv;
@@ -297,8 +322,8 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   const int segs = a.Hkv * mp.row_chunks;  // segments per sequence
   const int G = static_cast<int>(gridDim.x);
   const int u = blockIdx.x;
-  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k_cache);
-  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v_cache);
+  const char* kcb = static_cast<const char*>(a.k_cache);
+  const char* vcb = static_cast<const char*>(a.v_cache);
   const float c = a.scale * kLog2e;
   const long block_stride = static_cast<long>(kBlockSize) * a.Hkv * D;  // elements per block
 
@@ -307,6 +332,8 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   // (all in one 16-token block); lane l writes chunk position l % kChunks of
   // key i*kKeysPerCopy + l / kChunks.  The source address is a wave-uniform
   // block-and-head base plus a per-thread offset fixed for the whole kernel.
+  // (byte offsets within one block of one head; the block and head go into
+  // the buffer descriptor)
   int off_k[C::kCopiesPerWave], off_v[C::kCopiesPerWave];
   {
     const int ckey = lane / C::kChunks, cpos = lane % C::kChunks;
@@ -314,16 +341,31 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     for (int jj = 0; jj < C::kCopiesPerWave; ++jj) {
       const int key = (jj * NW + wave) * C::kKeysPerCopy + ckey;
       const int row = (key & 15) * a.Hkv * D;
-      off_k[jj] = row + (cpos ^ (key & 7)) * 8;
-      off_v[jj] = row + (cpos ^ (2 * (key & 3))) * 8;
+      off_k[jj] = (row + (cpos ^ (key & 7)) * 8) * 2;
+      off_v[jj] = (row + (cpos ^ (2 * (key & 3))) * 8) * 2;
     }
   }
-  // per-lane parts of the V^T transpose-read addresses (see the header)
-  const int tq = lane >> 4, ts = lane & 15;
-  const int tr_row = 4 * hh + (ts >> 2);                 // + 16 * chunk (+ 8 for keys 4..7)
-  const int tr_chunk = 2 * (tq & 1) + ((ts & 3) >> 1);   // + 4 * dim block
-  const int tr_half = (ts & 1) * 4;
-  const int tr_swz = 2 * ((ts >> 2) & 3);                // 2 * (row % 4)
+  // LDS read addresses: a per-lane base plus a compile-time offset (stage,
+  // k-step, key chunk, dim block).  K: chunk c = 2 kk + hh of key `col` sits at
+  // c ^ (col % 8), which is (2 (kk % 4) + hh) ^ (col % 8) plus 8 (kk / 4).
+  // V^T: in each 16-lane group, lanes 4k..4k+3 point at key row
+  // 4 hh + k (+ 16 per key chunk, + 8 for its upper 8 keys), dims
+  // 8 ((4 db + 2 (lane/16 % 2) + lane/2 % 2) ^ 2 (k % 4)) + 4 (lane % 2);
+  // (4 db + x) ^ y with x, y < 8 is (4 (db % 2) + x) ^ y plus 8 (db / 2).
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS const void*)lds));
+  uint32_t kaddr[4], vaddr[2];
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) kaddr[k4] = lds0 + 2 * (col * D + (((2 * k4 + hh) ^ (col & 7)) * 8));
+  {
+    const int tq = lane >> 4, ts = lane & 15;
+    const int tr_row = 4 * hh + (ts >> 2);
+    const int tr_chunk = 2 * (tq & 1) + ((ts & 3) >> 1);
+    const int tr_half = (ts & 1) * 4;
+    const int tr_swz = 2 * ((ts >> 2) & 3);
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2)
+      vaddr[d2] = lds0 + 2 * (C::kTileElems + tr_row * D + (((4 * d2 + tr_chunk) ^ tr_swz) * 8) + tr_half);
+  }
 
   // One piece: tiles [t0, t1) of segment (b, kh, rc) whose sequence has
   // prefix length P (raw, checked here).  `whole` pieces write bf16 outputs,
@@ -371,7 +413,11 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     const bool bad_len = Praw < 0 || Praw > a.max_prefix_len;
     const int P = clamp_prefix(a, Praw);
     const int nblk = (P + a.N + kBlockSize - 1) / kBlockSize;
-    const long head_off = static_cast<long>(kh) * D;
+    // buffer descriptors per (cache, block): base = the block's first row of
+    // head kh; the range ends with the block, so a stray offset reads zeros
+    const long block_bytes = block_stride * 2;
+    const long head_bytes = static_cast<long>(kh) * D * 2;
+    const int range = static_cast<int>(block_bytes - head_bytes);
     auto issue_tile = [&](int stage, int tile, int b0, int b1) __attribute__((always_inline)) {
       const int e0 = tile * 2;
       b0 = e0 < nblk ? b0 : 0;
@@ -387,11 +433,10 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
 #pragma unroll
       for (int jj = 0; jj < C::kCopiesPerWave; ++jj) {
         const int copy = jj * NW + wave;
-        const long base = static_cast<long>(copy * C::kKeysPerCopy < kBlockSize ? b0 : b1) * block_stride + head_off;
-        __builtin_amdgcn_global_load_lds((const void*)(kc + base + off_k[jj]), (LDS_AS void*)(kst + copy * 512),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vc + base + off_v[jj]), (LDS_AS void*)(vst + copy * 512),
-                                         16, 0, 0);
+        const int blk = copy * C::kKeysPerCopy < kBlockSize ? b0 : b1;
+        const long src = blk * block_bytes + head_bytes;
+        copy_to_lds(kcb + src, range, off_k[jj], kst + copy * 512);
+        copy_to_lds(vcb + src, range, off_v[jj], vst + copy * 512);
       }
     };
 
@@ -403,33 +448,36 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     float m_c = -INFINITY;  // running maximum, already multiplied by c
     float l_run = 0.f;
 
-    auto compute_tile = [&](int stage, int tile) __attribute__((always_inline)) {
-        const uint16_t* ks = lds + stage * C::kStageElems;
-        const uint16_t* vs = ks + C::kTileElems;
+    auto compute_tile = [&](auto stage_c, int tile) __attribute__((always_inline)) {
+        constexpr int kStage = decltype(stage_c)::value;
+        constexpr int kStageBytes = kStage * C::kStageElems * 2;
         const int tb = tile * kTile;
         f32x16 sc = {};
     #pragma unroll
         for (int kk = 0; kk < C::kKs; ++kk) {
-          const int ch = kk * 2 + hh;
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(ks + col * D + ((ch ^ (col & 7)) * 8));
+          const bf16x8 av = *reinterpret_cast<const LDS_AS bf16x8*>(
+              static_cast<uintptr_t>(kaddr[kk & 3] + kStageBytes + (kk >> 2) * 128));
           sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[kk], sc, 0, 0, 0);
         }
         // V^T operands of the whole tile, read now so the reads overlap the softmax
         u32x4 vop[2][C::kDb];
-    #pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2) {
-          const int r1 = 16 * kc2 + tr_row, r2 = r1 + 8;
-    #pragma unroll
-          for (int db = 0; db < C::kDb; ++db) {
-            const int chk = (4 * db + tr_chunk) ^ tr_swz;
-            const u32x2 lo = ds_read_tr16_b64(vs + r1 * D + chk * 8 + tr_half);
-            const u32x2 hi = ds_read_tr16_b64(vs + r2 * D + chk * 8 + tr_half);
+        static_for<0, 2>([&](auto kc2_c) {
+          constexpr int kc2 = decltype(kc2_c)::value;
+          static_for<0, C::kDb>([&](auto db_c) {
+            constexpr int db = decltype(db_c)::value;
+            // bytes past vaddr: stage, key rows 16 kc2 (+ 8), dim blocks 2 (db / 2)
+            constexpr int kLo = kStageBytes + 2 * (16 * kc2 * D + (db >> 1) * 64);
+            constexpr int kHi = kLo + 2 * 8 * D;
+            // the offset field holds 16 bits: far stages step the base by 64 KB
+            constexpr int kLoB = kLo >= 65536 ? 65536 : 0, kHiB = kHi >= 65536 ? 65536 : 0;
+            const u32x2 lo = ds_read_tr16_b64<kLo - kLoB>(vaddr[db & 1] + kLoB);
+            const u32x2 hi = ds_read_tr16_b64<kHi - kHiB>(vaddr[db & 1] + kHiB);
             vop[kc2][db][0] = lo[0];
             vop[kc2][db][1] = lo[1];
             vop[kc2][db][2] = hi[0];
             vop[kc2][db][3] = hi[1];
-          }
-        }
+          });
+        });
         if (tb + kTile > P) {  // the tile reaches the tree slots or the end: mask
           const uint64_t vis = tile_visibility(mw, tb, P) >> (4 * hh);
     #pragma unroll
@@ -516,16 +564,23 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     // the query and mask loads went out before these copies; draining here
     // keeps them out of the per-tile copy waits
     wait_vmcnt<0>();
-    for (int tile = t0; tile < t1; ++tile) {
-      const int stage = (tile - t0) % C::kStages;
-      wait_tile(min(C::kStages - 2, t1 - 1 - tile));
-      __asm__ volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();  // every wave's copies landed; tile - 1 is done
-      __asm__ volatile("" ::: "memory");
-      const int nt = tile + C::kStages - 1;
-      if (nt < t1) issue_tile((nt - t0) % C::kStages, nt, nb0, nb1);
-      if (active) compute_tile(stage, tile);
-      if (nt < t1) fetch_ids(nt + 1, nb0, nb1);  // ready by the next issue
+    // the loop body is unrolled over the ring, so that every LDS address is a
+    // per-lane base plus a constant
+    for (int tile = t0; tile < t1;) {
+      static_for<0, C::kStages>([&](auto stage_c) {
+        constexpr int kStage = decltype(stage_c)::value;
+        if (tile < t1) {
+          wait_tile(min(C::kStages - 2, t1 - 1 - tile));
+          __asm__ volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();  // every wave's copies landed; tile - 1 is done
+          __asm__ volatile("" ::: "memory");
+          const int nt = tile + C::kStages - 1;
+          if (nt < t1) issue_tile((kStage + C::kStages - 1) % C::kStages, nt, nb0, nb1);
+          if (active) compute_tile(stage_c, tile);
+          if (nt < t1) fetch_ids(nt + 1, nb0, nb1);  // ready by the next issue
+          ++tile;
+        }
+      });
     }
 
     // ---- piece epilogue ----
@@ -721,24 +776,31 @@ hipError_t launch_cfg(const AttnArgs& a, const MfmaParams& mp, hipStream_t strea
 // fit on a compute unit (two waves per SIMD); an 8-wave workgroup fills the
 // SIMDs at two waves each by itself.
 constexpr int kComputeUnits = 256;
-constexpr int kMinTilesPerPiece = 4;
+constexpr int kMinTilesPerPiece = 4;  // balanced shares
+// fixed pieces: each cut adds a partial state of kRows x (D + 2) floats,
+// written and merged; 8 tiles per piece is the measured sweet spot for one
+// Llama-3-8B-shaped sequence (2k prefix, 60 nodes)
+constexpr int kMinTilesFixed = 8;
 
-// Rows of a KV head go to workgroups of 4 waves (128 rows) or, for D = 128
-// and more than 128 rows, 8 waves (256 rows).  One sequence: fixed pieces,
-// about one round of resident workgroups.  Several sequences: balanced
+// Rows of a KV head go to workgroups of 4 waves (128 rows) or, for D = 128,
+// more than 128 rows and several sequences, 8 waves (256 rows).  One
+// sequence: fixed pieces of at least kMinTilesFixed tiles, up to one round of
+// resident workgroups.  Several sequences: balanced
 // shares over one round of resident workgroups, or fewer when the work
 // (bounded by max_prefix_len) would give shares under kMinTilesPerPiece.
 MfmaParams plan_for(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
   const int R = (Hq / Hkv) * N;
   MfmaParams p;
-  p.waves = (D == 128 && R > 128) ? 8 : 4;
+  // one sequence is latency-bound: 4-wave workgroups spread its rows over
+  // twice the compute units (the row chunks share K/V tiles through L2)
+  p.waves = (D == 128 && R > 128 && B > 1) ? 8 : 4;
   p.row_chunks = (R + p.waves * 32 - 1) / (p.waves * 32);
   const long max_tiles = (static_cast<long>(max_prefix_len) + N + kTile - 1) / kTile;
   const long segments = static_cast<long>(B) * Hkv * p.row_chunks;
   const long resident = static_cast<long>(kComputeUnits) * (p.waves == 8 ? 1 : 2);
   if (B == 1) {
     long pieces = (resident + segments - 1) / segments;
-    const long cap = (max_tiles + kMinTilesPerPiece - 1) / kMinTilesPerPiece;
+    const long cap = (max_tiles + kMinTilesFixed - 1) / kMinTilesFixed;
     if (pieces > cap) pieces = cap;
     if (pieces < 1) pieces = 1;
     p.balanced = 0;

@@ -4,8 +4,8 @@
 // rolled back to the accepted tokens).
 //
 // One workgroup per sequence.  Each thread owns 16-byte columns of a cache row
-// (K and V, every KV head) and walks the path in ascending order, reading the
-// source row before writing the destination.  For a strictly increasing path
+// (K and V, every KV head) and walks the path in ascending order, reading
+// source rows before writing destinations.  For a strictly increasing path
 // with path[j] >= j, a destination j is never the source of a later step, and
 // the source path[j] of step j is rewritten (as destination) only by the later
 // step j' = path[j], whose store follows this thread's load of it; so the
@@ -62,16 +62,27 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CompactArgs a) {
   }
   if (tid == 0 && a.new_lens) a.new_lens[b] = P + L;
 
-  // 16-byte columns per cache row (one row = Hkv * D elements)
+  // 16-byte columns per cache row (one row = Hkv * D elements).  Steps go in
+  // batches of 8: all sources of a batch are loaded before its stores.  A
+  // batch's sources path[j] >= j are never an earlier destination, and a
+  // destination j that is the source of an earlier step of the batch is
+  // stored after that load, so batches keep gather-before-write.
   const int cols = a.Hkv * a.D * a.elt_bytes / 16;
   for (int c = tid; c < 2 * cols; c += kThreads) {
     int4* base = reinterpret_cast<int4*>(c < cols ? a.k_cache : a.v_cache);
     const int col = c < cols ? c : c - cols;
-    for (int j = 1; j < s_L; ++j) {
-      const int sr = s_src[j], dr = s_dst[j];
-      if (sr == dr) continue;
-      const int4 v = base[static_cast<size_t>(sr) * cols + col];
-      base[static_cast<size_t>(dr) * cols + col] = v;
+    for (int j0 = 1; j0 < s_L; j0 += 8) {
+      int4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        if (j < s_L && s_src[j] != s_dst[j]) v[u] = base[static_cast<size_t>(s_src[j]) * cols + col];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        if (j < s_L && s_src[j] != s_dst[j]) base[static_cast<size_t>(s_dst[j]) * cols + col] = v[u];
+      }
     }
   }
 }

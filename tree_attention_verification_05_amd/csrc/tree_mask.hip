@@ -19,13 +19,16 @@ __global__ __launch_bounds__(kThreads) void tree_mask_kernel(const int32_t* __re
   const int b = blockIdx.x;
   const int W = (N + 63) >> 6;
   const int32_t* par = parents + static_cast<size_t>(b) * N;
+  __shared__ int s_par[TV_MAX_NODES];
   __shared__ int bad;
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
 
-  // validity of the whole tree first, so that every row is either exact or zero
+  // validity of the whole tree first, so that every row is either exact or
+  // zero; the parents stay in LDS for the walks
   for (int i = threadIdx.x; i < N; i += kThreads) {
     const int p = par[i];
+    s_par[i] = p;
     if (i == 0 ? p != -1 : (p < 0 || p >= i)) bad = 1;
   }
   __syncthreads();
@@ -38,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void tree_mask_kernel(const int32_t* __re
       int c = i;
       bits[c >> 6] |= 1ull << (c & 63);
       while (c != 0) {
-        c = par[c];
+        c = s_par[c];
         bits[c >> 6] |= 1ull << (c & 63);
         ++d;
       }
