@@ -122,6 +122,45 @@ def test_all_match_and_all_miss():
     assert (aref["accept_len"] == 0).all()
 
 
+def test_many_sequences_four_wave_schedule():
+    """More sequences than one workgroup scans at once (the share schedule's
+    prefix sum runs over several chunks), most shares spanning many short
+    sequences, some prefixes empty."""
+    w = _variant(3, name="many-seq", tag=108, B=600, prefix=(0, 200), V=1000)
+    assert (w.prefix_lens == 0).any()
+    verify(w, label="B=600 4-wave")
+
+
+def test_many_sequences_eight_wave_schedule():
+    """The eight-wave, two-row-chunk layout with more sequences than one
+    eight-wave workgroup scans at once."""
+    w = _variant(4, name="many-seq-8w", tag=109, B=520, prefix=(0, 120), V=1000)
+    verify(w, label="B=520 8-wave")
+
+
+def test_mixed_empty_short_and_long_prefixes():
+    """One long prefix among empty and short ones: the long sequence is split
+    over many shares while single shares cover several short sequences, and
+    the batch's total is far below its upper bound so that many workgroups
+    find no tiles at all."""
+    lengths = (0, 0, 5000, 1, 0, 17, 31, 32, 33, 63, 64, 65, 0, 2047, 3, 0, 511, 0, 1, 700)
+    w = _variant(3, name="mixed", tag=110, B=len(lengths), prefix_lengths=lengths, V=1000)
+    verify(w, label="mixed lengths")
+    w = _variant(4, name="mixed-8w", tag=111, B=6, prefix_lengths=(0, 4100, 0, 5, 0, 1500),
+                 V=1000)
+    verify(w, label="mixed lengths 8-wave")
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_largest_tree(batch):
+    """N at its maximum of 256 nodes (four 64-bit mask words per row, eight
+    (one sequence) or four (batched) row chunks per KV head)."""
+    w = _variant(3, name=f"n256-b{batch}", tag=112 + batch, B=batch, tree=("uniform", 256, 9),
+                 prefix=(100, 400), V=1000)
+    assert w.N == 256
+    verify(w, label=f"N=256 B={batch}")
+
+
 def test_argmax_ties_and_signed_zero():
     """Exact ties (lowest index wins), maxima at index 0 and V-1, and rows
     whose maximum is a mix of -0.0 and +0.0."""
@@ -221,7 +260,8 @@ def test_python_binding_rejects_host_tensors():
 
 def test_accept_workspace_reused_across_batch_sizes():
     """One cached workspace serves calls of growing and shrinking batch size:
-    each call leaves it zero-filled, so no stale state leaks into the next."""
+    every key a call reads was written by the same call, so nothing stale
+    from a larger earlier call leaks into a smaller later one."""
     for i, seed in ((5, 1), (3, 2), (5, 3), (1, 4)):
         w = W.make_small(i, seed=seed, dense=False)
         d = {"logits": w.logits.cuda(), "draft": torch.from_numpy(w.draft_tokens).cuda(),

@@ -68,6 +68,8 @@ class Spec:
     logit_std: float
     match: Union[float, Tuple[float, float]]  # per-node plant probability, or a range per sequence
     block_size: int = BLOCK_SIZE
+    prefix_lengths: Optional[Tuple[int, ...]] = None  # explicit per-sequence lengths (B of them);
+                                                      # when given, ``prefix`` is not used
 
     @property
     def N(self) -> int:
@@ -279,7 +281,11 @@ def build(spec: Spec, seed: int = 0, dense: bool = True, logits: bool = True) ->
     bs = spec.block_size
 
     r = _rng(seed, spec.tag, _C_PREFIX)
-    if isinstance(spec.prefix, tuple):
+    if spec.prefix_lengths is not None:
+        if len(spec.prefix_lengths) != B:
+            raise ValueError("prefix_lengths needs one length per sequence")
+        prefix_lens = np.asarray(spec.prefix_lengths, dtype=np.int32)
+    elif isinstance(spec.prefix, tuple):
         lo, hi = spec.prefix
         prefix_lens = r.integers(lo, hi + 1, size=B).astype(np.int32)
     else:
