@@ -66,7 +66,7 @@ typedef enum {
                              block table cannot hold max_prefix_len + N positions */
   TV_ERR_DTYPE = 3,       /* dtype is neither TV_F32 nor TV_BF16 */
   TV_ERR_UNSUPPORTED = 4, /* D not in {64, 128} or block_size != 16 */
-  TV_ERR_ALIGN = 5,       /* q, out, cache or logits pointer not 16-byte aligned */
+  TV_ERR_ALIGN = 5,       /* q, out, cache, logits or workspace pointer not 16-byte aligned */
   TV_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the queried size */
   TV_ERR_LAUNCH = 7       /* the HIP runtime reported an error at launch */
 } tv_status;
@@ -102,8 +102,9 @@ TV_API tv_status tv_build_tree_mask(const int32_t* parents, int32_t B, int32_t N
 
 /*
  * Workspace bytes tv_tree_attention needs for these sizes (0 when the key
- * range is not split).  The workspace holds per-split partial softmax state
- * and needs no initialisation.
+ * range is not split).  The workspace holds the split schedule and the
+ * partial softmax state of every split (row maxima and sums in fp32, the
+ * normalised partial outputs in bf16), and needs no initialisation.
  */
 TV_API size_t tv_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
                                         int32_t max_prefix_len, tv_dtype dtype);
@@ -131,8 +132,8 @@ TV_API size_t tv_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq,
  *   dtype        TV_BF16 (fp32 accumulation, bf16 output rounded to nearest
  *                even) or TV_F32 (fp32 throughout).
  *   workspace    device buffer of at least
- *                tv_tree_attention_workspace_size(...) bytes (may be NULL if
- *                that size is 0).
+ *                tv_tree_attention_workspace_size(...) bytes, 16-byte aligned
+ *                (may be NULL if that size is 0).
  * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_DTYPE, TV_ERR_UNSUPPORTED,
  * TV_ERR_ALIGN, TV_ERR_WORKSPACE, TV_ERR_LAUNCH.  Device: TV_DEV_BAD_CACHE.
  */

@@ -10,18 +10,20 @@
 // and every query head of the group.  Each of the NW waves owns 32 rows
 // (waves past the last row only help load tiles).  Sequences differ in
 // length, so the tiles of all segments are laid end to end and every
-// workgroup takes an equal share of that flat range (see make_schedule);
+// workgroup takes an equal share of that flat range (see balanced_start);
 // a segment cut between workgroups is merged by a second kernel.
 //
 // Memory pipeline: 32-key tiles stream from HBM straight into LDS with
-// global_load_lds_dwordx4 (each lane's 16 bytes land at the wave's LDS base +
-// 16 * lane; no registers are staged), through a ring of kStages LDS
-// buffers, so kStages - 1 tiles are in flight per workgroup.  Each wave waits only for its
-// own copies of the tile it is about to use (s_waitcnt vmcnt with the number
-// of copies it has issued since), then one s_barrier makes every wave's
-// copies visible and frees the buffer of the previous tile.  The block ids of
-// a tile are two wave-uniform table entries read with scalar loads one tile
-// ahead; a copy's source is that block's base plus a per-thread offset.
+// buffer_load_dwordx4 ... lds (each lane's 16 bytes land at the wave's LDS
+// base + 16 * lane; no registers are staged), through a ring of kStages LDS
+// buffers.  Iteration t computes the scores of tile t + 1 while it runs the
+// softmax and the PV product of tile t, so two buffers are being read and
+// kStages - 2 tiles are in flight.  Each wave waits only for its own copies
+// of tile t + 1 (s_waitcnt vmcnt with the number of copies it has issued
+// since), then one s_barrier makes every wave's copies visible and frees the
+// buffer of tile t - 1.  The block ids of a tile are two wave-uniform table
+// entries read with scalar loads one tile ahead; a copy's source is that
+// block's base plus a per-thread offset.
 //
 // Per tile, with lanes l and l+32 sharing query row l % 32:
 //   S^T (32 keys x rows)  = K (keys x D) * Q^T (D x rows)   v_mfma_f32_32x32x16_bf16
@@ -50,8 +52,9 @@
 // The result is the same softmax: numerator and denominator use the same m.
 // Prefix tiles need no mask; tiles that reach the tree slots select -inf for
 // keys outside the row's ancestor set (branch-free).  A segment shared by
-// several workgroups leaves (m, denominator, unnormalised output) in fp32 per
-// piece, merged with the log-sum-exp rule.
+// several workgroups leaves per piece its row maxima and sums (fp32) and its
+// normalised output (bf16: the final output is bf16, and the merge is a
+// convex combination of these), merged with the log-sum-exp rule.
 #include <type_traits>
 
 #include "tv_internal.h"
@@ -71,6 +74,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kTile = 32;             // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRescale = 8.0f;  // log2 units a row maximum may grow before rescaling
+constexpr int kSoftmaxPerMfma = 4;   // vector instructions scheduled after each score MFMA
 
 template <int D, int NW>
 struct Cfg {
@@ -85,7 +89,7 @@ struct Cfg {
   static constexpr int kStageElems = 2 * kTileElems;       // K + V
   static constexpr int kRows = NW * 32;                    // rows per workgroup
   static constexpr int kDmaPerTile = 2 * kCopiesPerWave;   // copies per wave per tile (K and V)
-  // LDS buffers (kStages - 1 tiles in flight): 4 (64 KB at D = 128) lets two
+  // LDS buffers (kStages - 2 tiles in flight): 4 (64 KB at D = 128) lets two
   // 4-wave workgroups share a compute unit; an 8-wave workgroup has the unit
   // to itself and takes 6 (96 KB)
   static constexpr int kStages = NW == 8 ? 6 : 4;
@@ -102,13 +106,36 @@ struct MfmaParams {
 };
 
 // workspace: a header written by the attention kernel for the merge (lane
-// tiles S, share length T, then the first lane tile of every sequence), then
-// the partial slots (2G balanced, G fixed) of kRows rows: unnormalised
-// outputs [slot][row][D], then running maxima and denominators [slot][row]
-// each, all fp32
-__host__ __device__ constexpr size_t header_bytes(int B) { return (8 + 4 * static_cast<size_t>(B) + 255) / 256 * 256; }
+// tiles S and share length T, then one cut record of four int32 per share),
+// then the partial slots (2G balanced, G fixed) of kRows rows each
+__host__ __device__ constexpr size_t header_bytes(int shares) {
+  return (16 + 16 * static_cast<size_t>(shares) + 255) / 256 * 256;
+}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Partial states after the header: normalised outputs O / l as bf16,
+// [slot][D/4][row] with 8 bytes per four dims, then the row maxima m (log2
+// units, scaled) and row sums l, [slot][row] fp32.  nslots counts slot rows.
+struct PartialView {
+  u32x2* o;
+  float* m;
+  float* l;
+};
+template <int D>
+__device__ __forceinline__ PartialView partial_view_at(void* ws, size_t hbytes, size_t nslots) {
+  char* base = static_cast<char*>(ws) + hbytes;
+  PartialView v;
+  v.o = reinterpret_cast<u32x2*>(base);
+  v.m = reinterpret_cast<float*>(base + nslots * D * 2);
+  v.l = v.m + nslots;
+  return v;
+}
+template <int D>
+__device__ __forceinline__ PartialView partial_view(const AttnArgs& a, const MfmaParams& mp, int G) {
+  const size_t nslots = static_cast<size_t>(mp.balanced ? 2 * G : G) * (mp.waves * 32);
+  return partial_view_at<D>(a.workspace, header_bytes(mp.balanced ? G / (a.Hkv * mp.row_chunks) : 0), nslots);
+}
 
 // v_cvt_pk_bf16_f32: round to nearest even
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -238,10 +265,16 @@ __device__ __forceinline__ int tiles_of(const AttnArgs& a, int P) { return (P + 
 // [v T, v T + T) touches: a sequence inside the share is written straight to
 // `out`, and one cut by a share boundary leaves its partial state in slot u
 // (the share's first sequence) or G + u (its last).  Workgroup 0 stores S and
-// T in the workspace header.
+// T in the workspace header, and lane 0 of every share the cut at its start.
+//
+// Workgroup placement: the hardware hands workgroups to the 8 XCDs round
+// robin (u % 8).  With several row chunks per KV head, the chunks of one
+// (share, KV head) are given to workgroups u, u + 8, ... of one XCD, which
+// start together and share the K/V tiles through that XCD's L2.
 struct Start {
   int S, T;        // flat tiles, share length
   int b, base;     // sequence holding the share's first tile (-1: none), and its first lane tile
+  int ntiles;      // tiles of sequence b
 };
 
 template <int NW>
@@ -267,8 +300,7 @@ __device__ Start balanced_start(const AttnArgs& a, int shares, int share_idx, in
   const int even = (st.S + shares - 1) / shares;
   st.T = even > min_tiles ? even : min_tiles;
   const int j0 = share_idx * st.T;
-  const bool write_starts = blockIdx.x == 0;  // the merge reads them from the header
-  if (j0 >= st.S && !write_starts) {
+  if (j0 >= st.S) {
     st.b = -1;
     return st;
   }
@@ -288,16 +320,17 @@ __device__ Start balanced_start(const AttnArgs& a, int shares, int share_idx, in
       chunk += x;
     }
     const int start = running + before + incl - v;
-    if (write_starts && b < a.B) static_cast<int*>(a.workspace)[2 + b] = start;
     if (b < a.B && start <= j0 && j0 < start + v) {
       found[0] = b;
       found[1] = start;
+      found[2] = v;
     }
     running += chunk;
     __syncthreads();
   }
-  st.b = j0 < st.S ? found[0] : -1;
+  st.b = found[0];
   st.base = found[1];
+  st.ntiles = found[2];
   return st;
 }
 
@@ -307,7 +340,7 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   using C = Cfg<D, NW>;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ int red[NW];
-  __shared__ int found[2];
+  __shared__ int found[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -448,18 +481,22 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     float m_c = -INFINITY;  // running maximum, already multiplied by c
     float l_run = 0.f;
 
-    auto compute_tile = [&](auto stage_c, int tile) __attribute__((always_inline)) {
+    // One tile: softmax of this tile's scores `sc` and O^T += V^T P^T, with
+    // the next tile's scores S^T = K Q^T computed into `sn` in the same
+    // straight-line block as the exponentials, so that the matrix cores work
+    // while the vector unit runs the softmax.
+    auto tile_body = [&](auto stage_c, int tile, f32x16 sc, f32x16& sn) __attribute__((always_inline)) {
         constexpr int kStage = decltype(stage_c)::value;
         constexpr int kStageBytes = kStage * C::kStageElems * 2;
+        constexpr int kNextBytes = ((kStage + 1) % C::kStages) * C::kStageElems * 2;
         const int tb = tile * kTile;
-        f32x16 sc = {};
+        // K operands of the next tile
+        bf16x8 kop[C::kKs];
     #pragma unroll
-        for (int kk = 0; kk < C::kKs; ++kk) {
-          const bf16x8 av = *reinterpret_cast<const LDS_AS bf16x8*>(
-              static_cast<uintptr_t>(kaddr[kk & 3] + kStageBytes + (kk >> 2) * 128));
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[kk], sc, 0, 0, 0);
-        }
-        // V^T operands of the whole tile, read now so the reads overlap the softmax
+        for (int kk = 0; kk < C::kKs; ++kk)
+          kop[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(
+              static_cast<uintptr_t>(kaddr[kk & 3] + kNextBytes + (kk >> 2) * 128));
+        // V^T operands of this tile, read now so the reads overlap the softmax
         u32x4 vop[2][C::kDb];
         static_for<0, 2>([&](auto kc2_c) {
           constexpr int kc2 = decltype(kc2_c)::value;
@@ -504,6 +541,9 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
             for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
         }
         const float mcs = (m_c == -INFINITY) ? 0.f : m_c;  // no visible key yet: p = 0
+        f32x16 s2 = {};
+    #pragma unroll
+        for (int kk = 0; kk < C::kKs; ++kk) s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qreg[kk], s2, 0, 0, 0);
         u32x4 pw[2];
         float lsum0 = 0.f, lsum1 = 0.f;
     #pragma unroll
@@ -515,6 +555,13 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
           pw[r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
         }
         l_run += lsum0 + lsum1;
+        // one score MFMA, then a share of the softmax arithmetic, repeated
+    #pragma unroll
+        for (int kk = 0; kk < C::kKs; ++kk) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, kSoftmaxPerMfma, 0);
+        }
+        sn = s2;
         // the transpose reads above are invisible to the compiler's wait
         // tracking: wait for them here, with their results as operands so that
         // no use can be scheduled above the wait
@@ -529,14 +576,24 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
                                                               acc[db], 0, 0, 0);
         }
     };
+    // S^T of the piece's first tile
+    auto compute_s = [&](auto stage_c, f32x16& sc) __attribute__((always_inline)) {
+        constexpr int kStage = decltype(stage_c)::value;
+        constexpr int kStageBytes = kStage * C::kStageElems * 2;
+        sc = f32x16{};
+    #pragma unroll
+        for (int kk = 0; kk < C::kKs; ++kk) {
+          const bf16x8 av = *reinterpret_cast<const LDS_AS bf16x8*>(
+              static_cast<uintptr_t>(kaddr[kk & 3] + kStageBytes + (kk >> 2) * 128));
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[kk], sc, 0, 0, 0);
+        }
+    };
 
-    // wait until this wave's copies of the tile about to be used are done:
-    // `later` tiles (at most C::kStages - 2) have been issued after it
+    // wait until this wave's copies of a tile are done: `later` tiles (at
+    // most C::kStages - 3) have been issued after it
     auto wait_tile = [&](int later) __attribute__((always_inline)) {
-      static_assert(C::kStages >= 2 && C::kStages <= 6, "wait_tile covers 0..4 later tiles");
-      if (later >= 4)
-        wait_vmcnt<4 * C::kDmaPerTile>();
-      else if (later == 3)
+      static_assert(C::kStages >= 3 && C::kStages <= 6, "wait_tile covers 0..3 later tiles");
+      if (later >= 3)
         wait_vmcnt<3 * C::kDmaPerTile>();
       else if (later == 2)
         wait_vmcnt<2 * C::kDmaPerTile>();
@@ -547,6 +604,9 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     };
 
     // ---- tile pipeline ----
+    // Iteration `tile` reads K of tile + 1 (its scores are computed ahead,
+    // overlapping this tile's softmax) and V of tile, and refills the buffer
+    // of tile - 1, so kStages - 2 tiles stay in flight.
     // the ring may still be read by the previous piece's last tile (every
     // wave's LDS reads of it completed before its last MFMAs)
     __asm__ volatile("" ::: "memory");
@@ -564,19 +624,33 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     // the query and mask loads went out before these copies; draining here
     // keeps them out of the per-tile copy waits
     wait_vmcnt<0>();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    f32x16 s_cur = {};
+    if (active) compute_s(std::integral_constant<int, 0>{}, s_cur);
     // the loop body is unrolled over the ring, so that every LDS address is a
     // per-lane base plus a constant
-    for (int tile = t0; tile < t1;) {
+    int tile = t0;
+    while (tile < t1) {
       static_for<0, C::kStages>([&](auto stage_c) {
         constexpr int kStage = decltype(stage_c)::value;
         if (tile < t1) {
-          wait_tile(min(C::kStages - 2, t1 - 1 - tile));
-          __asm__ volatile("" ::: "memory");
-          __builtin_amdgcn_s_barrier();  // every wave's copies landed; tile - 1 is done
-          __asm__ volatile("" ::: "memory");
+          const bool has_next = tile + 1 < t1;
           const int nt = tile + C::kStages - 1;
-          if (nt < t1) issue_tile((kStage + C::kStages - 1) % C::kStages, nt, nb0, nb1);
-          if (active) compute_tile(stage_c, tile);
+          if (has_next) {
+            wait_tile(min(C::kStages - 3, t1 - 2 - tile));
+            __asm__ volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();  // tile + 1 landed everywhere; tile - 1 is free
+            __asm__ volatile("" ::: "memory");
+            if (nt < t1) issue_tile((kStage + C::kStages - 1) % C::kStages, nt, nb0, nb1);
+          }
+          if (active) {
+            // the last tile's "next" scores read a stale buffer and are dropped
+            f32x16 s_next;
+            tile_body(stage_c, tile, s_cur, s_next);
+            s_cur = s_next;
+          }
           if (nt < t1) fetch_ids(nt + 1, nb0, nb1);  // ready by the next issue
           ++tile;
         }
@@ -603,55 +677,87 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
           *reinterpret_cast<u32x2*>(op + d) = w;
         }
     } else {
-      // output partials are [slot][D/4][row] float4, so that one store
-      // instruction writes two runs of 32 consecutive rows (whole lines)
+      // the piece's normalised output O / l in bf16 (the merge weighs it by
+      // l and the maximum m), [slot][D/4][row] with 8 bytes per four dims so
+      // that one store instruction writes two runs of 32 consecutive rows
       const size_t nslots = static_cast<size_t>(mp.balanced ? 2 * G : G) * C::kRows;
       const size_t prow = static_cast<size_t>(slot) * C::kRows + rl;
-      float* ws = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + header_bytes(a.B));
-      float4* po = reinterpret_cast<float4*>(ws) + static_cast<size_t>(slot) * (D / 4) * C::kRows + rl;
-      float* pm = ws + nslots * D;
-      float* pl = pm + nslots;
+      const PartialView pv = partial_view<D>(a, mp, G);
+      u32x2* po = pv.o + static_cast<size_t>(slot) * (D / 4) * C::kRows + rl;
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
       for (int db = 0; db < C::kDb; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int q = db * 8 + 2 * jj + hh;  // dims 4q .. 4q + 3
-          float4 v;
-          v.x = acc[db][4 * jj];
-          v.y = acc[db][4 * jj + 1];
-          v.z = acc[db][4 * jj + 2];
-          v.w = acc[db][4 * jj + 3];
-          po[static_cast<size_t>(q) * C::kRows] = v;
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[db][4 * jj] * inv, acc[db][4 * jj + 1] * inv);
+          w[1] = pack_bf16x2(acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv);
+          po[static_cast<size_t>(q) * C::kRows] = w;
         }
+      (void)nslots;
       if (hh == 0) {
-        pm[prow] = m_c;
-        pl[prow] = lt;
+        pv.m[prow] = m_c;
+        pv.l[prow] = lt;
       }
     }
   };
 
+  // workgroups are spread over the 8 XCDs round-robin (u % 8); the row chunks
+  // of one (item) go to consecutive workgroups of the same XCD so that their
+  // shared K/V tiles come from that XCD's L2
+  int w_item, rc_p;
+  {
+    const int RC = mp.row_chunks;
+    const int G0 = mp.balanced ? G / (8 * RC) * (8 * RC) : 0;
+    if (u < G0) {
+      const int x = u & 7, k = u >> 3;
+      rc_p = k % RC;
+      w_item = (k / RC) * 8 + x;
+    } else {
+      w_item = G0 / RC + (u - G0) / RC;
+      rc_p = (u - G0) % RC;
+    }
+  }
+  const int v = !mp.balanced ? ((w_item / mp.pieces) * mp.row_chunks + rc_p) * mp.pieces + w_item % mp.pieces
+                             : (w_item / a.Hkv) * (a.Hkv * mp.row_chunks) + (w_item % a.Hkv) * mp.row_chunks + rc_p;
   if (!mp.balanced) {
     // ---------------- fixed pieces ----------------
-    const int seg_id = u / mp.pieces, piece = u % mp.pieces;
+    const int seg_id = v / mp.pieces, piece = v % mp.pieces;
     const int b = seg_id / segs, seg = seg_id % segs;
     const int Praw = a.prefix_lens[b];
     const int ntiles = tiles_of(a, clamp_prefix(a, Praw));
     const int t0 = piece * mp.T;
-    if (t0 >= ntiles) return;  // whole workgroup: the sequence is shorter than the longest
+    if (t0 >= ntiles) {
+      // the sequence is shorter than the longest: an empty piece, whose row
+      // maxima of -inf give it no weight in the merge
+      if (tid < C::kRows) partial_view<D>(a, mp, G).m[static_cast<size_t>(v) * C::kRows + tid] = -INFINITY;
+      return;
+    }
     const int t1 = min(ntiles, t0 + mp.T);
-    run_piece(b, seg / mp.row_chunks, seg % mp.row_chunks, Praw, t0, t1, t0 == 0 && t1 == ntiles, u);
+    // with several pieces every piece leaves a partial state, so the merge
+    // needs no sequence lengths
+    run_piece(b, seg / mp.row_chunks, seg % mp.row_chunks, Praw, t0, t1, mp.pieces == 1, v);
     return;
   }
 
   // ---------------- balanced shares ----------------
   const int lanes = a.Hkv * mp.row_chunks;
-  const int lane_id = u % lanes, share = u / lanes;
+  const int lane_id = v % lanes, share = v / lanes;
   const int kh = lane_id / mp.row_chunks, rc = lane_id % mp.row_chunks;
   const Start st = balanced_start<NW>(a, G / lanes, share, mp.T, red, found);
+  int* hdr = static_cast<int*>(a.workspace);
   if (u == 0 && tid == 0) {
-    int* hdr = static_cast<int*>(a.workspace);
     hdr[0] = st.S;
     hdr[1] = st.T;
+  }
+  // the cut at this share's start, for the merge: the sequence it splits,
+  // that sequence's first lane tile and tile count, and the cut's rank among
+  // the sequence's cuts (-1: the share starts at a sequence start or past the end)
+  if (lane_id == 0 && tid == 0) {
+    int4 cut = {-1, 0, 0, 0};
+    if (st.b >= 0 && share * st.T > st.base) cut = int4{st.b, st.base, st.ntiles, share - st.base / st.T - 1};
+    reinterpret_cast<int4*>(hdr + 4)[share] = cut;
   }
   if (st.b < 0) return;  // whole workgroup: the lane's tiles ended before this share
   const int j1 = min(st.S, share * st.T + st.T);
@@ -669,91 +775,167 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     }
     const int t0 = j - seq_base;
     const int t1 = min(ntiles, t0 + (j1 - j));
-    run_piece(b, kh, rc, Praw, t0, t1, t0 == 0 && t1 == ntiles, first ? u : G + u);
+    run_piece(b, kh, rc, Praw, t0, t1, t0 == 0 && t1 == ntiles, first ? v : G + v);
     j += t1 - t0;
     first = false;
   }
 }
 
 // Merge the partial states of segments that several workgroups shared
-// (log-sum-exp rule) and write bf16 outputs.  Workgroup (segment, block of
-// 32 rows x 8 four-dim chunks): each thread owns 4 dims of one row (threads
-// of a wave take consecutive rows, matching the partial layout) and walks
-// the segment's pieces.
-template <int D, int NW>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, MfmaParams mp) {
+// (log-sum-exp rule) and write bf16 outputs.  One workgroup per attention
+// workgroup; each merges a slice of the rows of one split segment:
+//   fixed pieces: workgroup (segment, p) takes row slice p of `pieces` and
+//     merges all `pieces` slots (empty pieces carry maxima of -inf);
+//   balanced shares: workgroup (share v, lane) takes the cut at the start of
+//     share v, if any: slice i of the n cuts of the split sequence, whose
+//     pieces are the shares f .. f + n it touches.
+// Threads walk (4-dim chunk, row) items with rows fastest, matching the
+// [slot][D/4][row] partial layout, and fold the pieces four at a time with
+// a running maximum.
+constexpr int kMergeSplit = 4;  // balanced shares: merge workgroups per cut
+template <int D, int NW, int kItems, int kGroup>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, MfmaParams mp) {
   using C = Cfg<D, NW>;
-  constexpr int kQBlocks = D / 4 / 8;                  // 8 chunks of 4 dims per workgroup
-  constexpr int kBlocksPerSeg = C::kRows / 32 * kQBlocks;
+  // kItems items per thread and kGroup pieces of each have their loads in flight together
   const int tid = threadIdx.x;
-  const int segs = a.Hkv * mp.row_chunks;
-  const int seg_id = blockIdx.x / kBlocksPerSeg;  // ((b * Hkv) + kh) * row_chunks + rc
-  const int blk = blockIdx.x % kBlocksPerSeg;
-  const int b = seg_id / segs, seg = seg_id % segs;
-  const int kh = seg / mp.row_chunks, rc = seg % mp.row_chunks;
+  const int u = mp.balanced ? static_cast<int>(blockIdx.x) / kMergeSplit : static_cast<int>(blockIdx.x);
+  const int G = mp.grid;
+  const int RC = mp.row_chunks;
+  const int segs = a.Hkv * RC;
   const int g = a.Hq / a.Hkv;
   const int R = g * a.N;
-  const int G = mp.grid;
-  const int rows = min(C::kRows, R - rc * C::kRows);
-  const int rl = (blk / kQBlocks) * 32 + (tid & 31);
-  const int q = (blk % kQBlocks) * 8 + (tid >> 5);
-  if ((blk / kQBlocks) * 32 >= rows) return;  // whole workgroup: rows past the chunk's end
-  const int ntiles = tiles_of(a, clamp_prefix(a, a.prefix_lens[b]));
-
-  int first_slot_lo, npieces, T;  // pieces are slots first_slot_lo.. (see below)
-  int f = 0, F = 0;
+  int b, kh, rc, npieces, slot0, lane = 0, f = 0, cut_first = 0;
+  int r_lo, n, item0, istep;  // rows r_lo .. r_lo + n of the chunk; this thread's items
+  size_t hbytes;
   if (!mp.balanced) {
-    T = mp.T;
-    npieces = (ntiles + T - 1) / T;
-    first_slot_lo = seg_id * mp.pieces;
+    // workgroup (segment, block of 32 rows x 8 four-dim chunks), one item per thread
+    constexpr int kQBlocks = D / 4 / 8;
+    constexpr int kBlocksPerSeg = C::kRows / 32 * kQBlocks;
+    const int seg_id = u / kBlocksPerSeg, blk = u % kBlocksPerSeg;
+    npieces = mp.pieces;
+    b = seg_id / segs;
+    const int seg = seg_id % segs;
+    kh = seg / RC;
+    rc = seg % RC;
+    slot0 = seg_id * mp.pieces;
+    hbytes = header_bytes(0);
+    const int rows = min(C::kRows, R - rc * C::kRows);
+    r_lo = (blk / kQBlocks) * 32;
+    n = min(32, rows - r_lo);
+    if (n <= 0) return;
+    // items are (chunk q, row): this block's chunks start at 8 (blk % kQBlocks)
+    item0 = ((blk % kQBlocks) * 8 + (tid >> 5)) * n + (tid & 31);
+    if ((tid & 31) >= n) return;
+    istep = 1 << 24;  // one item
   } else {
+    const int shares = G / segs;
+    const int share = u / segs;
+    lane = u % segs;
     const int* hdr = static_cast<const int*>(a.workspace);
-    T = hdr[1];
-    F = hdr[2 + b];  // index of this sequence's first tile in its lane
-    f = F / T;
-    npieces = (F + ntiles - 1) / T - f + 1;
-    first_slot_lo = seg;  // the lane: workgroup of share v is v * lanes + lane
+    const int4 cut = reinterpret_cast<const int4*>(hdr + 4)[share];
+    if (cut.x < 0) return;
+    const int T = hdr[1];
+    b = cut.x;
+    f = cut.y / T;
+    const int last = (cut.y + cut.z - 1) / T;
+    npieces = last - f + 1;
+    const int nslices = last - f, slice = cut.w;
+    kh = lane / RC;
+    rc = lane % RC;
+    cut_first = cut.y != f * T;  // the sequence starts inside share f: that share's last piece
+    slot0 = 0;
+    hbytes = header_bytes(shares);
+    const int rows = min(C::kRows, R - rc * C::kRows);
+    // this workgroup's part of the cut's row slice
+    const int parts = nslices * kMergeSplit, part = slice * kMergeSplit + static_cast<int>(blockIdx.x) % kMergeSplit;
+    r_lo = part * rows / parts;
+    n = (part + 1) * rows / parts - r_lo;
+    if (n <= 0) return;
+    item0 = tid;
+    istep = 256;
   }
-  if (npieces <= 1) return;  // one workgroup ran the whole segment and wrote it
-  if (rl >= rows) return;
-
-  const size_t nslots = static_cast<size_t>(mp.balanced ? 2 * G : G) * C::kRows;
-  const float* ws = reinterpret_cast<const float*>(static_cast<const char*>(a.workspace) + header_bytes(a.B));
-  const float4* po = reinterpret_cast<const float4*>(ws);
-  const float* pm = ws + nslots * D;
-  const float* pl = pm + nslots;
+  (void)hbytes;
+  const PartialView pv = partial_view<D>(a, mp, G);
   auto slot_of = [&](int k) __attribute__((always_inline)) {
-    if (!mp.balanced) return first_slot_lo + k;
-    const int uu = (f + k) * segs + first_slot_lo;  // workgroup of share f + k in this lane
-    return (k == 0 && F != f * T) ? G + uu : uu;
+    if (!mp.balanced) return slot0 + k;
+    const int vv = (f + k) * segs + lane;  // workgroup of share f + k in this lane
+    return (k == 0 && cut_first) ? G + vv : vv;
   };
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int k = 0; k < npieces; ++k) M = fmaxf(M, pm[static_cast<size_t>(slot_of(k)) * C::kRows + rl]);
-  const float Ms = (M == -INFINITY) ? 0.f : M;
-  float4 o = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-#pragma unroll 8
-  for (int k = 0; k < npieces; ++k) {
-    const size_t sl = static_cast<size_t>(slot_of(k));
-    const size_t pr = sl * C::kRows + rl;
-    const float w = exp2_fast(pm[pr] - Ms);
-    L += w * pl[pr];
-    const float4 v = po[(sl * (D / 4) + q) * C::kRows + rl];
-    o.x += w * v.x;
-    o.y += w * v.y;
-    o.z += w * v.z;
-    o.w += w * v.w;
+  const int nitems = n * (D / 4);
+  // kItems items per thread at a time, pieces kGroup at a time: every load
+  // of a round is issued before any is used
+  for (int it0 = item0; it0 < nitems; it0 += kItems * istep) {
+    float M[kItems], L[kItems];
+    float o[kItems][4];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      M[i] = -INFINITY;
+      L[i] = 0.f;
+      o[i][0] = o[i][1] = o[i][2] = o[i][3] = 0.f;
+    }
+    for (int k0 = 0; k0 < npieces; k0 += kGroup) {
+      float m[kItems][kGroup], l[kItems][kGroup];
+      u32x2 ov[kItems][kGroup];
+#pragma unroll
+      for (int i = 0; i < kItems; ++i) {
+        const int item = it0 + i * istep;
+        const int q = item / n, rl = r_lo + item % n;
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+          m[i][j] = -INFINITY;
+          l[i][j] = 0.f;
+          ov[i][j] = u32x2{0u, 0u};
+          if (item < nitems && k0 + j < npieces) {
+            const size_t sl = static_cast<size_t>(slot_of(k0 + j));
+            m[i][j] = pv.m[sl * C::kRows + rl];
+            l[i][j] = pv.l[sl * C::kRows + rl];
+            ov[i][j] = pv.o[(sl * (D / 4) + q) * C::kRows + rl];
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kItems; ++i) {
+        float Mn = M[i];
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) Mn = fmaxf(Mn, m[i][j]);
+        if (Mn == -INFINITY) continue;  // no visible key in any piece so far
+        const float sc = exp2_fast(M[i] - Mn);  // 0 while M is -inf
+        L[i] *= sc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[i][e] *= sc;
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+          // a piece without visible keys (or an empty one) has m = -inf and
+          // contributes nothing; its other values are not used
+          const bool use = m[i][j] != -INFINITY;
+          const float w = use ? exp2_fast(m[i][j] - Mn) * l[i][j] : 0.f;
+          L[i] += w;
+          const float x0 = __uint_as_float(ov[i][j][0] << 16), x1 = __uint_as_float(ov[i][j][0] & 0xFFFF0000u);
+          const float x2 = __uint_as_float(ov[i][j][1] << 16), x3 = __uint_as_float(ov[i][j][1] & 0xFFFF0000u);
+          o[i][0] += use ? w * x0 : 0.f;
+          o[i][1] += use ? w * x1 : 0.f;
+          o[i][2] += use ? w * x2 : 0.f;
+          o[i][3] += use ? w * x3 : 0.f;
+        }
+        M[i] = Mn;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int item = it0 + i * istep;
+      if (item >= nitems) break;
+      const int q = item / n, rl = r_lo + item % n;
+      const float inv = L[i] > 0.f ? 1.f / L[i] : 0.f;
+      const int r = rc * C::kRows + rl;
+      const int node = r / g, hg = r % g;
+      uint16_t* op = static_cast<uint16_t*>(a.out) +
+                     ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D + 4 * q;
+      u32x2 w;
+      w[0] = pack_bf16x2(o[i][0] * inv, o[i][1] * inv);
+      w[1] = pack_bf16x2(o[i][2] * inv, o[i][3] * inv);
+      *reinterpret_cast<u32x2*>(op) = w;
+    }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  const int r = rc * C::kRows + rl;
-  const int node = r / g, hg = r % g;
-  uint16_t* op = static_cast<uint16_t*>(a.out) +
-                 ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D + 4 * q;
-  u32x2 w;
-  w[0] = pack_bf16x2(o.x * inv, o.y * inv);
-  w[1] = pack_bf16x2(o.z * inv, o.w * inv);
-  *reinterpret_cast<u32x2*>(op) = w;
 }
 
 template <int D, int NW>
@@ -765,10 +947,17 @@ hipError_t launch_cfg(const AttnArgs& a, const MfmaParams& mp, hipStream_t strea
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!mp.balanced ? mp.pieces == 1 : mp.grid == a.Hkv * mp.row_chunks) return e;  // no segment is ever shared
-  constexpr int kBlocksPerSeg = C::kRows / 32 * (D / 4 / 8);
-  const long blocks = static_cast<long>(a.B) * a.Hkv * mp.row_chunks * kBlocksPerSeg;
-  hipLaunchKernelGGL((attn_combine_kernel<D, NW>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                     a, mp);
+  // fixed pieces: one workgroup per (segment, 32 rows x 32 dims), one item
+  // per thread with all pieces in flight; balanced: kMergeSplit per attention
+  // workgroup (its cut), four items per thread
+  if (mp.balanced) {
+    hipLaunchKernelGGL((attn_merge_kernel<D, NW, 4, 2>), dim3(static_cast<unsigned>(mp.grid * kMergeSplit)), dim3(256), 0,
+                       stream, a, mp);
+  } else {
+    const long blocks = static_cast<long>(a.B) * a.Hkv * mp.row_chunks * (C::kRows / 32) * (D / 32);
+    hipLaunchKernelGGL((attn_merge_kernel<D, NW, 1, 16>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       a, mp);
+  }
   return hipGetLastError();
 }
 
@@ -825,7 +1014,8 @@ MfmaParams plan_for(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
 size_t attention_mfma_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
   const MfmaParams p = plan_for(B, N, Hq, Hkv, D, max_prefix_len);
   const size_t slots = static_cast<size_t>(p.balanced ? 2 * p.grid : p.grid) * p.waves * 32;
-  return header_bytes(B) + slots * (D + 2) * sizeof(float);
+  const int shares = p.balanced ? p.grid / (Hkv * p.row_chunks) : 0;
+  return header_bytes(shares) + slots * (2 * D + 2 * sizeof(float));
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {

@@ -67,6 +67,7 @@ tv_status tv_tree_attention(const void* q, const void* k_cache, const void* v_ca
     return TV_ERR_ALIGN;
   const size_t need = tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len, dtype);
   if (need > 0 && (!workspace || workspace_bytes < need)) return TV_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return TV_ERR_ALIGN;
 
   AttnArgs a;
   a.q = q;
