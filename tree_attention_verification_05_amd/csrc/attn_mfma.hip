@@ -74,7 +74,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kTile = 32;             // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRescale = 8.0f;  // log2 units a row maximum may grow before rescaling
-constexpr int kSoftmaxPerMfma = 4;   // vector instructions scheduled after each score MFMA
 
 template <int D, int NW>
 struct Cfg {
@@ -90,9 +89,8 @@ struct Cfg {
   static constexpr int kRows = NW * 32;                    // rows per workgroup
   static constexpr int kDmaPerTile = 2 * kCopiesPerWave;   // copies per wave per tile (K and V)
   // LDS buffers (kStages - 2 tiles in flight): 4 (64 KB at D = 128) lets two
-  // 4-wave workgroups share a compute unit; an 8-wave workgroup has the unit
-  // to itself and takes 6 (96 KB)
-  static constexpr int kStages = NW == 8 ? 6 : 4;
+  // 4-wave workgroups share a compute unit
+  static constexpr int kStages = 4;
   static_assert(kCopiesPerTile % NW == 0, "every wave issues the same number of copies");
 };
 
@@ -485,7 +483,7 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     // the next tile's scores S^T = K Q^T computed into `sn` in the same
     // straight-line block as the exponentials, so that the matrix cores work
     // while the vector unit runs the softmax.
-    auto tile_body = [&](auto stage_c, int tile, f32x16 sc, f32x16& sn) __attribute__((always_inline)) {
+    auto tile_body = [&](auto stage_c, int tile, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
         constexpr int kStage = decltype(stage_c)::value;
         constexpr int kStageBytes = kStage * C::kStageElems * 2;
         constexpr int kNextBytes = ((kStage + 1) % C::kStages) * C::kStageElems * 2;
@@ -541,9 +539,11 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
             for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
         }
         const float mcs = (m_c == -INFINITY) ? 0.f : m_c;  // no visible key yet: p = 0
-        f32x16 s2 = {};
+        // the next tile's scores: independent of the softmax below, which the
+        // compiler interleaves with these MFMAs
+        sn = f32x16{};
     #pragma unroll
-        for (int kk = 0; kk < C::kKs; ++kk) s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qreg[kk], s2, 0, 0, 0);
+        for (int kk = 0; kk < C::kKs; ++kk) sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qreg[kk], sn, 0, 0, 0);
         u32x4 pw[2];
         float lsum0 = 0.f, lsum1 = 0.f;
     #pragma unroll
@@ -555,13 +555,6 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
           pw[r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
         }
         l_run += lsum0 + lsum1;
-        // one score MFMA, then a share of the softmax arithmetic, repeated
-    #pragma unroll
-        for (int kk = 0; kk < C::kKs; ++kk) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, kSoftmaxPerMfma, 0);
-        }
-        sn = s2;
         // the transpose reads above are invisible to the compiler's wait
         // tracking: wait for them here, with their results as operands so that
         // no use can be scheduled above the wait
@@ -627,8 +620,12 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
-    f32x16 s_cur = {};
-    if (active) compute_s(std::integral_constant<int, 0>{}, s_cur);
+    // scores of two consecutive tiles, by tile parity (kStages is even), so
+    // that the next tile's MFMAs never wait for this tile's softmax to read
+    // its registers
+    f32x16 s_buf[2];
+    s_buf[1] = f32x16{};
+    if (active) compute_s(std::integral_constant<int, 0>{}, s_buf[0]);
     // the loop body is unrolled over the ring, so that every LDS address is a
     // per-lane base plus a constant
     int tile = t0;
@@ -647,9 +644,7 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
           }
           if (active) {
             // the last tile's "next" scores read a stale buffer and are dropped
-            f32x16 s_next;
-            tile_body(stage_c, tile, s_cur, s_next);
-            s_cur = s_next;
+            tile_body(stage_c, tile, s_buf[kStage & 1], s_buf[(kStage + 1) & 1]);
           }
           if (nt < t1) fetch_ids(nt + 1, nb0, nb1);  // ready by the next issue
           ++tile;
@@ -962,8 +957,10 @@ hipError_t launch_cfg(const AttnArgs& a, const MfmaParams& mp, hipStream_t strea
 }
 
 // MI355X: 256 compute units.  A 4-wave workgroup takes 64 KB of LDS, so two
-// fit on a compute unit (two waves per SIMD); an 8-wave workgroup fills the
-// SIMDs at two waves each by itself.
+// fit on a compute unit (two waves per SIMD).  Two independent workgroups
+// per unit drift apart in phase, so one's softmax overlaps the other's
+// MFMAs; an 8-wave workgroup (one per unit, in lockstep at every tile
+// barrier) measured slower even where it halves the row chunks.
 constexpr int kComputeUnits = 256;
 constexpr int kMinTilesPerPiece = 4;  // balanced shares
 // fixed pieces: each cut adds a partial state of kRows x (D + 2) floats,
@@ -971,8 +968,7 @@ constexpr int kMinTilesPerPiece = 4;  // balanced shares
 // Llama-3-8B-shaped sequence (2k prefix, 60 nodes)
 constexpr int kMinTilesFixed = 8;
 
-// Rows of a KV head go to workgroups of 4 waves (128 rows) or, for D = 128,
-// more than 128 rows and several sequences, 8 waves (256 rows).  One
+// Rows of a KV head go to row chunks of 128 (4 waves).  One
 // sequence: fixed pieces of at least kMinTilesFixed tiles, up to one round of
 // resident workgroups.  Several sequences: balanced
 // shares over one round of resident workgroups, or fewer when the work
@@ -980,13 +976,12 @@ constexpr int kMinTilesFixed = 8;
 MfmaParams plan_for(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
   const int R = (Hq / Hkv) * N;
   MfmaParams p;
-  // one sequence is latency-bound: 4-wave workgroups spread its rows over
-  // twice the compute units (the row chunks share K/V tiles through L2)
-  p.waves = (D == 128 && R > 128 && B > 1) ? 8 : 4;
+  // the row chunks of a KV head share its K/V tiles through L2
+  p.waves = 4;
   p.row_chunks = (R + p.waves * 32 - 1) / (p.waves * 32);
   const long max_tiles = (static_cast<long>(max_prefix_len) + N + kTile - 1) / kTile;
   const long segments = static_cast<long>(B) * Hkv * p.row_chunks;
-  const long resident = static_cast<long>(kComputeUnits) * (p.waves == 8 ? 1 : 2);
+  const long resident = static_cast<long>(kComputeUnits) * 2;
   if (B == 1) {
     long pieces = (resident + segments - 1) / segments;
     const long cap = (max_tiles + kMinTilesFixed - 1) / kMinTilesFixed;
@@ -1020,8 +1015,7 @@ size_t attention_mfma_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int 
 
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
   const MfmaParams p = plan_for(a.B, a.N, a.Hq, a.Hkv, a.D, a.max_prefix_len);
-  if (a.D == 128)
-    return p.waves == 8 ? launch_cfg<128, 8>(a, p, stream) : launch_cfg<128, 4>(a, p, stream);
+  if (a.D == 128) return launch_cfg<128, 4>(a, p, stream);
   return launch_cfg<64, 4>(a, p, stream);
 }
 
