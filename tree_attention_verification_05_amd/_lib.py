@@ -117,8 +117,9 @@ _accept_ws: Dict[Tuple[int, int], torch.Tensor] = {}
 
 
 def accept_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A zero-filled workspace for tv_accept_greedy, kept per device (the
-    library leaves it zero-filled after every call on its stream)."""
+    """A workspace for tv_accept_greedy, kept per device and grown when a
+    call needs more (the library needs no initial contents: every key a call
+    reads is written earlier in the same call)."""
     idx = device.index if device.index is not None else torch.cuda.current_device()
     key = (idx, 0)
     ws = _accept_ws.get(key)

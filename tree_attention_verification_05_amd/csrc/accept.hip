@@ -17,9 +17,9 @@
 namespace tv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMinChunk = 4096;      // floats per workgroup at least
-constexpr int kTargetBlocks = 2048;  // enough workgroups to keep HBM busy
+constexpr int kThreads = 512;
+constexpr int kMinChunk = 8192;      // floats per workgroup at least
+constexpr int kTargetBlocks = 1024;  // enough workgroups to keep HBM busy
 
 struct Split {
   int chunk;   // floats per chunk (multiple of 4)
@@ -131,8 +131,17 @@ __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t* keys = static_cast<const uint64_t*>(a.workspace);
   const size_t base = static_cast<size_t>(b) * N;
-  // the tree and the draft tokens are loaded first; their latency overlaps
-  // the chunk keys below
+  // every (node, chunk) key of the sequence is contiguous in the workspace;
+  // the first eight per thread are loaded together with the tree and the
+  // draft tokens, so both latencies overlap
+  const uint64_t* kb = keys + base * chunks;
+  const int nk = N * chunks;
+  uint64_t kv[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int k = tid + u * kThreads;
+    kv[u] = k < nk ? kb[k] : 0ull;
+  }
   for (int i = tid; i < N; i += kThreads) {
     s_par[i] = a.parents[base + i];
     s_tok[i] = a.draft_tokens[base + i];
@@ -144,21 +153,20 @@ __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int
     s_dmax = 0;
   }
   __syncthreads();
-  // every (node, chunk) key of the sequence, contiguous in the workspace:
-  // eight loads in flight per thread, then folded per node with LDS max
-  const uint64_t* kb = keys + base * chunks;
-  const int nk = N * chunks;
-  for (int k0 = tid; k0 < nk; k0 += 8 * kThreads) {
-    uint64_t kv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = k0 + u * kThreads;
-      kv[u] = k < nk ? kb[k] : 0ull;
-    }
+  // fold the keys per node with LDS max (further rounds of eight per thread
+  // when N * chunks exceeds eight per thread)
+  for (int k0 = tid;;) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int k = k0 + u * kThreads;
       if (k < nk) atomicMax(&s_key[k / chunks], static_cast<unsigned long long>(kv[u]));
+    }
+    k0 += 8 * kThreads;
+    if (k0 >= nk) break;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u * kThreads;
+      kv[u] = k < nk ? kb[k] : 0ull;
     }
   }
   __syncthreads();
