@@ -108,6 +108,13 @@ def test_head_dim_64_bf16():
     verify(w, label="D=64")
 
 
+def test_head_dim_64_bf16_single_sequence():
+    """One sequence (fixed pieces with the deep ring) at head dim 64."""
+    w = _variant(2, name="d64-b1", tag=116, D=64, Hq=8, Hkv=2)
+    assert w.B == 1
+    verify(w, label="D=64 B=1")
+
+
 def test_fp32_d128():
     w = _variant(2, name="f32d128", tag=105, dtype="f32", prefix=300)
     verify(w, label="fp32 D=128")

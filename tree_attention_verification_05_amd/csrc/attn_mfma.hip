@@ -89,7 +89,9 @@ struct Cfg {
   static constexpr int kRows = NW * 32;                    // rows per workgroup
   static constexpr int kDmaPerTile = 2 * kCopiesPerWave;   // copies per wave per tile (K and V)
   // LDS buffers (kStages - 2 tiles in flight): 4 (64 KB at D = 128) lets two
-  // 4-wave workgroups share a compute unit
+  // 4-wave workgroups share a compute unit.  (Six buffers for a grid of one
+  // workgroup per unit measured no faster: a lone wave's per-tile latency,
+  // not the copies in flight, sets its pace.)
   static constexpr int kStages = 4;
   static_assert(kCopiesPerTile % NW == 0, "every wave issues the same number of copies");
 };
@@ -401,8 +403,10 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   // One piece: tiles [t0, t1) of segment (b, kh, rc) whose sequence has
   // prefix length P (raw, checked here).  `whole` pieces write bf16 outputs,
   // the others their partial state into `slot`.
-  auto run_piece = [&](int b, int kh, int rc, int Praw, int t0, int t1, bool whole,
-                       int slot) __attribute__((always_inline)) {
+  // ids[2 i], ids[2 i + 1]: block ids of tile t0 + i, i < kStages, when
+  // `have_ids` (read by the caller before the prefix length arrived)
+  auto run_piece = [&](int b, int kh, int rc, int Praw, int t0, int t1, bool whole, int slot,
+                       const int (&ids)[2 * C::kStages], bool have_ids) __attribute__((always_inline)) {
     // ---- this wave's 32 query rows and their mask words (issued first) ----
     const int rl = wave * 32 + col;  // row within the chunk
     const int row0 = rc * C::kRows + wave * 32;
@@ -438,8 +442,18 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
       b0 = e0 < maxb ? table_s[e0] : 0;
       b1 = e0 + 1 < maxb ? table_s[e0 + 1] : 0;
     };
-    int nb0, nb1;  // block ids of the next tile to issue
-    fetch_ids(t0, nb0, nb1);
+    // the ring's first kStages tiles: all loads issued together
+    int pid[2 * C::kStages];
+#pragma unroll
+    for (int i = 0; i < C::kStages; ++i) {
+      if (have_ids) {
+        pid[2 * i] = ids[2 * i];
+        pid[2 * i + 1] = ids[2 * i + 1];
+      } else {
+        fetch_ids(t0 + i, pid[2 * i], pid[2 * i + 1]);
+      }
+    }
+    int nb0 = pid[2 * (C::kStages - 1)], nb1 = pid[2 * C::kStages - 1];  // the next tile to issue
 
     const bool bad_len = Praw < 0 || Praw > a.max_prefix_len;
     const int P = clamp_prefix(a, Praw);
@@ -583,10 +597,12 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     };
 
     // wait until this wave's copies of a tile are done: `later` tiles (at
-    // most C::kStages - 3) have been issued after it
+    // most C::kStages - 2) have been issued after it
     auto wait_tile = [&](int later) __attribute__((always_inline)) {
-      static_assert(C::kStages >= 3 && C::kStages <= 6, "wait_tile covers 0..3 later tiles");
-      if (later >= 3)
+      static_assert(C::kStages >= 3 && C::kStages <= 6, "wait_tile covers 0..4 later tiles");
+      if (later >= 4)
+        wait_vmcnt<4 * C::kDmaPerTile>();
+      else if (later == 3)
         wait_vmcnt<3 * C::kDmaPerTile>();
       else if (later == 2)
         wait_vmcnt<2 * C::kDmaPerTile>();
@@ -607,16 +623,10 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     __asm__ volatile("" ::: "memory");
     if (bad_len && tid == 0) report(a.dev_status, TV_DEV_BAD_CACHE);
 #pragma unroll
-    for (int i = 0; i < C::kStages - 1; ++i) {
-      if (t0 + i < t1) {
-        const int b0 = nb0, b1 = nb1;
-        fetch_ids(t0 + i + 1, nb0, nb1);
-        issue_tile(i, t0 + i, b0, b1);
-      }
-    }
-    // the query and mask loads went out before these copies; draining here
-    // keeps them out of the per-tile copy waits
-    wait_vmcnt<0>();
+    for (int i = 0; i < C::kStages - 1; ++i)
+      if (t0 + i < t1) issue_tile(i, t0 + i, pid[2 * i], pid[2 * i + 1]);
+    // tile t0 (and the query and mask loads issued before it)
+    wait_tile(min(C::kStages - 2, t1 - 1 - t0));
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
@@ -720,9 +730,21 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     // ---------------- fixed pieces ----------------
     const int seg_id = v / mp.pieces, piece = v % mp.pieces;
     const int b = seg_id / segs, seg = seg_id % segs;
+    const int t0 = piece * mp.T;
+    // the block ids of the ring's first tiles do not depend on the prefix
+    // length: their loads go out together with it
+    int ids[2 * C::kStages];
+    {
+      const CONST_AS int32_t* trow =
+          (const CONST_AS int32_t*)(a.block_table + static_cast<size_t>(b) * a.max_blocks);
+#pragma unroll
+      for (int i = 0; i < 2 * C::kStages; ++i) {
+        const int e = 2 * t0 + i;
+        ids[i] = e < a.max_blocks ? trow[e] : 0;
+      }
+    }
     const int Praw = a.prefix_lens[b];
     const int ntiles = tiles_of(a, clamp_prefix(a, Praw));
-    const int t0 = piece * mp.T;
     if (t0 >= ntiles) {
       // the sequence is shorter than the longest: an empty piece, whose row
       // maxima of -inf give it no weight in the merge
@@ -732,7 +754,7 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     const int t1 = min(ntiles, t0 + mp.T);
     // with several pieces every piece leaves a partial state, so the merge
     // needs no sequence lengths
-    run_piece(b, seg / mp.row_chunks, seg % mp.row_chunks, Praw, t0, t1, mp.pieces == 1, v);
+    run_piece(b, seg / mp.row_chunks, seg % mp.row_chunks, Praw, t0, t1, mp.pieces == 1, v, ids, true);
     return;
   }
 
@@ -761,6 +783,7 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   int Praw = a.prefix_lens[b];
   int ntiles = tiles_of(a, clamp_prefix(a, Praw));
   bool first = true;
+  const int no_ids[2 * C::kStages] = {};
   while (j < j1) {
     while (j >= seq_base + ntiles) {  // the share continues into the next sequence
       seq_base += ntiles;
@@ -770,7 +793,7 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     }
     const int t0 = j - seq_base;
     const int t1 = min(ntiles, t0 + (j1 - j));
-    run_piece(b, kh, rc, Praw, t0, t1, t0 == 0 && t1 == ntiles, first ? v : G + v);
+    run_piece(b, kh, rc, Praw, t0, t1, t0 == 0 && t1 == ntiles, first ? v : G + v, no_ids, false);
     j += t1 - t0;
     first = false;
   }
