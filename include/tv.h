@@ -26,9 +26,11 @@
  *     (Hq % Hkv == 0, query head h reads KV head h / (Hq/Hkv)), head dim D,
  *     vocab V.  W = ceil(N / 64) mask words per node.
  *   - parents[b][0] == -1 and 0 <= parents[b][i] < i for i >= 1.
- *   - Paged K/V cache: k_cache and v_cache are [num_blocks][block_size][Hkv][D]
- *     row-major.  Logical position t of sequence b lives in block
- *     block_table[b][t / block_size], row t % block_size.  Sequence b's prefix
+ *   - Paged K/V cache: k_cache and v_cache are [num_blocks][Hkv][block_size][D]
+ *     row-major (within a block, the block_size slots of KV head 0, then of
+ *     head 1, ...: one head's keys of a block are one contiguous run).
+ *     Logical position t of sequence b lives in block
+ *     block_table[b][t / block_size], slot t % block_size.  Sequence b's prefix
  *     is t in [0, prefix_lens[b]); tree node i's key/value sit at
  *     t = prefix_lens[b] + i and must be written before tv_tree_attention.
  *   - All pointers are DEVICE pointers to caller-owned memory; the library
@@ -122,7 +124,7 @@ TV_API size_t tv_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq,
  *   out[b][i][h] = sum_t softmax_t(scale * <q[b][i][h], k[t][kh]>) * v[t][kh].
  *
  *   q            [B][N][Hq][D], dtype, device, 16-byte aligned.
- *   k_cache, v_cache  [num_blocks][block_size][Hkv][D], dtype, device, 16-byte
+ *   k_cache, v_cache  [num_blocks][Hkv][block_size][D], dtype, device, 16-byte
  *                aligned; read only.
  *   block_table  [B][max_blocks] int32, device.
  *   prefix_lens  [B] int32, device; every entry <= max_prefix_len (host int).
@@ -197,7 +199,7 @@ TV_API tv_status tv_accept_greedy(const float* logits, const int32_t* draft_toke
  * their bytes.  The path must be strictly increasing and start at node 0 (as
  * tv_accept_greedy writes it).
  *
- *   k_cache, v_cache  [num_blocks][block_size][Hkv][D], dtype, device, 16-byte
+ *   k_cache, v_cache  [num_blocks][Hkv][block_size][D], dtype, device, 16-byte
  *                     aligned, updated in place.
  *   new_lens          [B] int32, written (may be NULL): P_b + L.
  * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_DTYPE, TV_ERR_UNSUPPORTED,

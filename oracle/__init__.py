@@ -136,13 +136,29 @@ def build_tree_mask(parents):
 # --------------------------------------------------------------------------
 
 def cache_rows(block_table_row, positions, block_size: int) -> np.ndarray:
-    """Flat cache row of logical positions: block ``table[t // bs]``, row
+    """Flat token row of logical positions: block ``table[t // bs]``, slot
     ``t % bs`` (paged KV layout under the tree-attention layer, "vLLM-TreeEagle"
     README architecture graph; block-manager paging in the "P-EAGLE" page,
-    技术难点和解决方案)."""
+    技术难点和解决方案).  Rows index the token-major view of ``token_rows``."""
     t = np.asarray(positions, dtype=np.int64)
     blk = np.asarray(block_table_row, dtype=np.int64)[t // block_size]
     return blk * block_size + t % block_size
+
+
+def token_rows(cache) -> np.ndarray:
+    """The paged cache ``[num_blocks, Hkv, block_size, D]`` (each block holds
+    the slots of one head after another) as one row per token slot:
+    ``[num_blocks * block_size, Hkv, D]`` (a copy)."""
+    c = np.asarray(cache)
+    nb, Hkv, bs, D = c.shape
+    return np.ascontiguousarray(c.transpose(0, 2, 1, 3)).reshape(nb * bs, Hkv, D)
+
+
+def from_token_rows(rows, nb: int, bs: int) -> np.ndarray:
+    """Inverse of ``token_rows``."""
+    rows = np.asarray(rows)
+    Hkv, D = rows.shape[1:]
+    return np.ascontiguousarray(rows.reshape(nb, bs, Hkv, D).transpose(0, 2, 1, 3))
 
 
 # --------------------------------------------------------------------------
@@ -167,7 +183,7 @@ def tree_attention(q, k_cache, v_cache, block_table, prefix_lens, parents, scale
 
         out[b,i,h] = sum_t exp(s_t - max s) v[t, kh] / sum_t exp(s_t - max s)
 
-    q: [B, N, Hq, D]; caches: [num_blocks, block_size, Hkv, D] (any float
+    q: [B, N, Hq, D]; caches: [num_blocks, Hkv, block_size, D] (any float
     dtype; computed in float64).  Returns float64 [B, N, Hq, D]; sequences not
     in ``seqs`` (default: all) are NaN.  With ``return_weights`` it also
     returns {(b, kh): (weights [N*g, P_b+N], visible [N*g, P_b+N])} with rows
@@ -175,13 +191,13 @@ def tree_attention(q, k_cache, v_cache, block_table, prefix_lens, parents, scale
     """
     q = np.asarray(q, dtype=np.float64)
     B, N, Hq, D = q.shape
-    nb, bs, Hkv, D2 = k_cache.shape
+    nb, Hkv, bs, D2 = k_cache.shape
     assert D2 == D and Hq % Hkv == 0
     g = Hq // Hkv
     if scale is None or scale <= 0:
         scale = 1.0 / np.sqrt(D)
-    kf = np.asarray(k_cache).reshape(nb * bs, Hkv, D)
-    vf = np.asarray(v_cache).reshape(nb * bs, Hkv, D)
+    kf = token_rows(k_cache)
+    vf = token_rows(v_cache)
     out = np.full((B, N, Hq, D), np.nan)
     weights = {}
     for b in (range(B) if seqs is None else seqs):
@@ -292,11 +308,9 @@ def kv_compact(k_cache, v_cache, block_table, prefix_lens, accepted_nodes, accep
     other row keeps its bytes.  Works on copies of the caches (any dtype, bytes
     preserved); returns (k_new, v_new, new_lens = P + L).
     """
-    k_new = np.array(k_cache, copy=True)
-    v_new = np.array(v_cache, copy=True)
-    nb, bs = k_new.shape[:2]
-    kf = k_new.reshape(nb * bs, *k_new.shape[2:])
-    vf = v_new.reshape(nb * bs, *v_new.shape[2:])
+    nb, _, bs, _ = np.asarray(k_cache).shape
+    kf = token_rows(k_cache)
+    vf = token_rows(v_cache)
     B = len(prefix_lens)
     new_lens = np.zeros(B, dtype=np.int32)
     for b in range(B):
@@ -310,7 +324,7 @@ def kv_compact(k_cache, v_cache, block_table, prefix_lens, accepted_nodes, accep
         kf[dst] = ks
         vf[dst] = vs
         new_lens[b] = P + L
-    return k_new, v_new, new_lens
+    return from_token_rows(kf, nb, bs), from_token_rows(vf, nb, bs), new_lens
 
 
 # --------------------------------------------------------------------------

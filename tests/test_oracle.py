@@ -38,17 +38,18 @@ def rand_case(rng, B=2, N=7, Hq=4, Hkv=2, D=16, bs=4, plo=5, phi=23, tree="unifo
         table[b, :nblk[b]] = perm[off:off + nblk[b]]
         off += nblk[b]
     q = rng.standard_normal((B, N, Hq, D))
-    k = rng.standard_normal((nb, bs, Hkv, D))
-    v = rng.standard_normal((nb, bs, Hkv, D))
+    k = rng.standard_normal((nb, Hkv, bs, D))   # [block][head][slot][dim]
+    v = rng.standard_normal((nb, Hkv, bs, D))
     return dict(q=q, k=k, v=v, table=table, P=P, parents=parents, bs=bs)
 
 
 def gather(cache, table_row, positions, bs):
-    """Rows of the paged cache at logical positions (written here from the
-    paging rule itself, independent of the oracle's helper)."""
+    """[len, Hkv, D] rows of the paged cache ``[block][head][slot][dim]`` at
+    logical positions (written here from the paging rule itself,
+    independent of the oracle's helpers)."""
     out = []
     for t in positions:
-        out.append(cache[table_row[t // bs], t % bs])
+        out.append(cache[table_row[t // bs], :, t % bs])
     return np.stack(out)
 
 
@@ -123,7 +124,7 @@ def test_p1_every_path_equals_causal_decode():
         c = rand_case(rng)
         out = run_attention(c)
         B, N, Hq, D = c["q"].shape
-        g = Hq // c["k"].shape[2]
+        g = Hq // c["k"].shape[1]
         for b in range(B):
             P = int(c["P"][b])
             for i, path in enumerate(root_paths(c["parents"][b])):
@@ -197,12 +198,12 @@ def test_p5_mask_revealing_closed_form(P):
     u = rng.standard_normal(D)
     u /= np.linalg.norm(u)
     q = np.tile(u * np.sqrt(D), (1, N, 1, 1))              # scale*q.k = u.k
-    k = rng.standard_normal((nb, bs, 1, D))
-    v = rng.standard_normal((nb, bs, 1, D))
+    k = rng.standard_normal((nb, 1, bs, D))
+    v = rng.standard_normal((nb, 1, bs, D))
     for j in range(N):
         t = P + j
-        k[table[0, t // bs], t % bs, 0] = 30.0 * u
-        v[table[0, t // bs], t % bs, 0] = np.eye(D)[j]
+        k[table[0, t // bs], 0, t % bs] = 30.0 * u
+        v[table[0, t // bs], 0, t % bs] = np.eye(D)[j]
     out = O.tree_attention(q, k, v, table, np.array([P]), par[None])
     anc, depth = O.tree_structure(par)
     for i in range(N):
@@ -216,8 +217,8 @@ def test_p6_gqa_equals_mha_with_repeated_heads():
     c = rand_case(rng, Hq=6, Hkv=2)
     out = run_attention(c)
     mha = dict(c)
-    mha["k"] = np.repeat(c["k"], 3, axis=2)
-    mha["v"] = np.repeat(c["v"], 3, axis=2)
+    mha["k"] = np.repeat(c["k"], 3, axis=1)
+    mha["v"] = np.repeat(c["v"], 3, axis=1)
     np.testing.assert_allclose(run_attention(mha), out, rtol=0, atol=1e-13)
 
 
@@ -263,7 +264,7 @@ def test_p6_relabelling_nodes_permutes_outputs():
     for o in range(N):
         src, dst = P + o, P + pos[o]
         for name in ("k", "v"):
-            c2[name][c["table"][0, dst // bs], dst % bs] = c[name][c["table"][0, src // bs], src % bs]
+            c2[name][c["table"][0, dst // bs], :, dst % bs] = c[name][c["table"][0, src // bs], :, src % bs]
     out2 = run_attention(c2)
     np.testing.assert_allclose(out2[0, pos], out[0], rtol=0, atol=1e-13)
 
@@ -445,10 +446,10 @@ def test_p11_compaction_equals_per_row_copies_bit_exact():
             P = int(c["P"][b])
             for j in range(alen[b] + 1):
                 s, d = P + paths[b, j], P + j
-                for hh in range(k16.shape[2]):
+                for hh in range(k16.shape[1]):
                     for e in range(k16.shape[3]):
-                        kb[c["table"][b, d // bs], d % bs, hh, e] = k16[c["table"][b, s // bs], s % bs, hh, e]
-                        vb[c["table"][b, d // bs], d % bs, hh, e] = v16[c["table"][b, s // bs], s % bs, hh, e]
+                        kb[c["table"][b, d // bs], hh, d % bs, e] = k16[c["table"][b, s // bs], hh, s % bs, e]
+                        vb[c["table"][b, d // bs], hh, d % bs, e] = v16[c["table"][b, s // bs], hh, s % bs, e]
         assert np.array_equal(kn, kb) and np.array_equal(vn, vb)
         assert list(nl) == list(c["P"] + alen + 1)
 
@@ -456,7 +457,7 @@ def test_p11_compaction_equals_per_row_copies_bit_exact():
 def test_p11_overlapping_moves_gather_before_write():
     """Path [0, 2, 3]: slot 2 is both a source (for 1) and a destination (from
     3); the gather-then-write order makes slot 1 hold node 2's old row."""
-    k = np.arange(8, dtype=np.float64).reshape(2, 4, 1, 1)     # 2 blocks of 4 rows
+    k = np.arange(8, dtype=np.float64).reshape(2, 1, 4, 1)     # 2 blocks of 4 rows, 1 head
     table = np.array([[0, 1]])
     kn, _, nl = O.kv_compact(k, k, table, np.array([2]), np.array([[0, 2, 3, -1]]), np.array([2]))
     flat = kn.reshape(-1)
@@ -514,8 +515,10 @@ def test_golden_attention_hand_worked():
     g = _load("attention_hand_worked.json")
     for case in g["cases"]:
         bs = case["block_size"]
-        k = np.array(case["k_cache"], dtype=np.float64)
-        v = np.array(case["v_cache"], dtype=np.float64)
+        # the fixtures list each block's rows as [slot][head][dim]; the cache
+        # layout is [block][head][slot][dim]
+        k = np.array(case["k_cache"], dtype=np.float64).transpose(0, 2, 1, 3)
+        v = np.array(case["v_cache"], dtype=np.float64).transpose(0, 2, 1, 3)
         out = O.tree_attention(np.array(case["q"], dtype=np.float64), k, v,
                                np.array(case["block_table"]), np.array(case["prefix_lens"]),
                                np.array(case["parents"]), scale=case["scale"])

@@ -161,15 +161,15 @@ def tv_tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       mask: torch.Tensor, out: Optional[torch.Tensor] = None, scale: float = 0.0,
                       workspace: Optional[torch.Tensor] = None,
                       dev_status: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """q [B, N, Hq, D]; caches [num_blocks, 16, Hkv, D] (bf16 or fp32, same as
+    """q [B, N, Hq, D]; caches [num_blocks, Hkv, 16, D] (bf16 or fp32, same as
     q); block_table int32 [B, max_blocks]; prefix_lens int32 [B]; mask from
     tv_build_tree_mask.  Returns out [B, N, Hq, D] in q's dtype."""
     dt = _tv_dtype(q)
     _dev(q, "q", q.dtype)
     B, N, Hq, D = q.shape
-    nb, bs, Hkv, D2 = k_cache.shape
-    _dev(k_cache, "k_cache", q.dtype, (nb, bs, Hkv, D))
-    _dev(v_cache, "v_cache", q.dtype, (nb, bs, Hkv, D))
+    nb, Hkv, bs, D2 = k_cache.shape  # [num_blocks, Hkv, block_size, D]
+    _dev(k_cache, "k_cache", q.dtype, (nb, Hkv, bs, D))
+    _dev(v_cache, "v_cache", q.dtype, (nb, Hkv, bs, D))
     _dev(block_table, "block_table", torch.int32)
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_blocks]")
@@ -237,7 +237,7 @@ def tv_kv_compact(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: tor
                   dev_status: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Compacts the accepted path's K/V in place; returns new_lens int32 [B]."""
     dt = _tv_dtype(k_cache)
-    nb, bs, Hkv, D = k_cache.shape
+    nb, Hkv, bs, D = k_cache.shape  # [num_blocks, Hkv, block_size, D]
     _dev(k_cache, "k_cache", k_cache.dtype)
     _dev(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
     _dev(accepted_nodes, "accepted_nodes", torch.int32)

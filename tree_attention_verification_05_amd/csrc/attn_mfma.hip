@@ -373,7 +373,7 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
 #pragma unroll
     for (int jj = 0; jj < C::kCopiesPerWave; ++jj) {
       const int key = (jj * NW + wave) * C::kKeysPerCopy + ckey;
-      const int row = (key & 15) * a.Hkv * D;
+      const int row = (key & 15) * D;
       off_k[jj] = (row + (cpos ^ (key & 7)) * 8) * 2;
       off_v[jj] = (row + (cpos ^ (2 * (key & 3))) * 8) * 2;
     }
@@ -459,10 +459,11 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     const int P = clamp_prefix(a, Praw);
     const int nblk = (P + a.N + kBlockSize - 1) / kBlockSize;
     // buffer descriptors per (cache, block): base = the block's first row of
-    // head kh; the range ends with the block, so a stray offset reads zeros
+    // head kh; the range ends with that head's rows, so a stray offset reads
+    // zeros
     const long block_bytes = block_stride * 2;
-    const long head_bytes = static_cast<long>(kh) * D * 2;
-    const int range = static_cast<int>(block_bytes - head_bytes);
+    const long head_bytes = static_cast<long>(kh) * kBlockSize * D * 2;
+    const int range = kBlockSize * D * 2;
     auto issue_tile = [&](int stage, int tile, int b0, int b1) __attribute__((always_inline)) {
       const int e0 = tile * 2;
       b0 = e0 < nblk ? b0 : 0;

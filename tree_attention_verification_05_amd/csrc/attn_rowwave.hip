@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_rowwave_kernel(AttnArgs a) {
   for (int t0 = 0; t0 < total; t0 += 64) {
     const int t = t0 + lane;
     float s = -INFINITY;
-    int crow = -1;  // cache row (block * block_size + slot) of this lane's key
+    long long crow = -1;  // cache row ((block * Hkv + kh) * block_size + slot) of this lane's key
     if (t < total) {
       bool vis = true;
       if (t >= P) {
@@ -79,8 +79,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_rowwave_kernel(AttnArgs a) {
         vis = false;
       }
       if (vis) {
-        crow = blk * kBlockSize + t % kBlockSize;
-        const long base = (static_cast<long>(crow) * a.Hkv + kh) * D;
+        crow = (static_cast<long long>(blk) * a.Hkv + kh) * kBlockSize + t % kBlockSize;
+        const long long base = crow * D;
         float dot = 0.f;
         for (int d = 0; d < D; ++d) dot += qs[wave][d] * Elt<T>::load(kc + base + d);
         s = dot * c;
@@ -97,9 +97,9 @@ __global__ __launch_bounds__(kWaves * 64) void attn_rowwave_kernel(AttnArgs a) {
     m = mn;
     for (int j = 0; j < 64; ++j) {
       const float pj = __shfl(p, j, 64);
-      const int cj = __shfl(crow, j, 64);
+      const long long cj = __shfl(crow, j, 64);
       if (cj < 0) continue;
-      const long bj = (static_cast<long>(cj) * a.Hkv + kh) * D;
+      const long long bj = cj * D;
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[r] += pj * Elt<T>::load(vc + bj + lane + 64 * r);
     }

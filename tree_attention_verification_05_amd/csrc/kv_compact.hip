@@ -3,9 +3,10 @@
 // them to the rows from prev_length; "P-EAGLE", 技术难点和解决方案: the cache is
 // rolled back to the accepted tokens).
 //
-// One workgroup per sequence.  Each thread owns 16-byte columns of a cache row
-// (K and V, every KV head) and walks the path in ascending order, reading
-// source rows before writing destinations.  For a strictly increasing path
+// One workgroup per sequence.  Each thread owns 16-byte columns of a token's
+// K/V (both caches, every KV head; in the [block][head][slot][dim] layout a
+// token's head h sits block_size rows after its head h - 1) and walks the
+// path in ascending order, reading source rows before writing destinations.  For a strictly increasing path
 // with path[j] >= j, a destination j is never the source of a later step, and
 // the source path[j] of step j is rewritten (as destination) only by the later
 // step j' = path[j], whose store follows this thread's load of it; so the
@@ -18,8 +19,8 @@ namespace {
 constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CompactArgs a) {
-  __shared__ int s_src[TV_MAX_NODES];  // cache row of the source of step j
-  __shared__ int s_dst[TV_MAX_NODES];  // cache row of the destination of step j
+  __shared__ long long s_src[TV_MAX_NODES];  // head-0 cache row of the source of step j
+  __shared__ long long s_dst[TV_MAX_NODES];  // head-0 cache row of the destination of step j
   __shared__ int s_bad, s_L;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -50,8 +51,9 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CompactArgs a) {
         bad |= TV_DEV_BAD_CACHE;
         continue;
       }
-      s_src[j] = bs * kBlockSize + ts % kBlockSize;
-      s_dst[j] = bd * kBlockSize + td % kBlockSize;
+      // row (block * Hkv + head) * block_size + slot, at head 0
+      s_src[j] = static_cast<long long>(bs) * a.Hkv * kBlockSize + ts % kBlockSize;
+      s_dst[j] = static_cast<long long>(bd) * a.Hkv * kBlockSize + td % kBlockSize;
     }
   }
   if (bad) atomicOr(&s_bad, bad);
@@ -62,26 +64,30 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CompactArgs a) {
   }
   if (tid == 0 && a.new_lens) a.new_lens[b] = P + L;
 
-  // 16-byte columns per cache row (one row = Hkv * D elements).  Steps go in
-  // batches of 8: all sources of a batch are loaded before its stores.  A
-  // batch's sources path[j] >= j are never an earlier destination, and a
-  // destination j that is the source of an earlier step of the batch is
-  // stored after that load, so batches keep gather-before-write.
-  const int cols = a.Hkv * a.D * a.elt_bytes / 16;
+  // 16-byte columns of a token: dq per head row (D elements), Hkv heads.
+  // Steps go in batches of 8: all sources of a batch are loaded before its
+  // stores.  A batch's sources path[j] >= j are never an earlier
+  // destination, and a destination j that is the source of an earlier step
+  // of the batch is stored after that load, so batches keep
+  // gather-before-write.
+  const int dq = a.D * a.elt_bytes / 16;
+  const int cols = a.Hkv * dq;
   for (int c = tid; c < 2 * cols; c += kThreads) {
     int4* base = reinterpret_cast<int4*>(c < cols ? a.k_cache : a.v_cache);
-    const int col = c < cols ? c : c - cols;
+    const int cc = c < cols ? c : c - cols;
+    // head cc / dq sits (cc / dq) * block_size rows after head 0
+    const long long col = static_cast<long long>(cc / dq) * kBlockSize * dq + cc % dq;
     for (int j0 = 1; j0 < s_L; j0 += 8) {
       int4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int j = j0 + u;
-        if (j < s_L && s_src[j] != s_dst[j]) v[u] = base[static_cast<size_t>(s_src[j]) * cols + col];
+        if (j < s_L && s_src[j] != s_dst[j]) v[u] = base[s_src[j] * dq + col];
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int j = j0 + u;
-        if (j < s_L && s_src[j] != s_dst[j]) base[static_cast<size_t>(s_dst[j]) * cols + col] = v[u];
+        if (j < s_L && s_src[j] != s_dst[j]) base[s_dst[j] * dq + col] = v[u];
       }
     }
   }

@@ -16,11 +16,12 @@ read):
   section 树结构缓冲: branch prediction, level pruning), depth-biased trees, and
   the P-EAGLE linear chain ("P-EAGLE：vLLM集成并行推测解码加速LLM推理",
   section 技术原理和实现方式).
-* A paged K/V cache ``[num_blocks, block_size, Hkv, D]`` with one block table
-  row per sequence ("vLLM-TreeEagle" README, architecture graph:
-  PagedAttention under the tree-attention layer).  Prefix position ``t`` of
-  sequence ``b`` lives in block ``block_table[b, t // block_size]`` at row
-  ``t % block_size``; tree node ``i`` sits at position ``prefix_len[b] + i``.
+* A paged K/V cache ``[num_blocks, Hkv, block_size, D]`` (within a block, the
+  slots of one KV head after another) with one block table row per sequence
+  ("vLLM-TreeEagle" README, architecture graph: PagedAttention under the
+  tree-attention layer).  Prefix position ``t`` of sequence ``b`` lives in
+  block ``block_table[b, t // block_size]`` at slot ``t % block_size``; tree
+  node ``i`` sits at position ``prefix_len[b] + i``.
 * Query rows ``[B, N, Hq, D]`` for every tree node.
 * Target logits ``[B, N, V]`` in fp32, with the draft token of some children
   planted as the unique maximum of their parent's row so that a controlled
@@ -90,7 +91,7 @@ class Workload:
     planted: np.ndarray           # bool [B, N]: node i's token was planted as its parent row's max
     match_rate: np.ndarray        # float64 [B]
     q: Optional[torch.Tensor]     # [B, N, Hq, D] bf16 or f32
-    k_cache: Optional[torch.Tensor]  # [num_blocks, block_size, Hkv, D]
+    k_cache: Optional[torch.Tensor]  # [num_blocks, Hkv, block_size, D]
     v_cache: Optional[torch.Tensor]
     logits: Optional[torch.Tensor]   # [B, N, V] f32
 
@@ -335,7 +336,7 @@ def build(spec: Spec, seed: int = 0, dense: bool = True, logits: bool = True) ->
     q = k = v = None
     if dense:
         q = _to_dtype(_normal((B, N, spec.Hq, spec.D), 1.0, seed, spec.tag, _C_Q), spec.dtype)
-        cshape = (num_blocks, bs, spec.Hkv, spec.D)
+        cshape = (num_blocks, spec.Hkv, bs, spec.D)
         k = _to_dtype(_normal(cshape, 1.0, seed, spec.tag, _C_K), spec.dtype)
         v = _to_dtype(_normal(cshape, 1.0, seed, spec.tag, _C_V), spec.dtype)
 
