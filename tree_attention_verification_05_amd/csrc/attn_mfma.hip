@@ -987,10 +987,11 @@ hipError_t launch_cfg(const AttnArgs& a, const MfmaParams& mp, hipStream_t strea
 // barrier) measured slower even where it halves the row chunks.
 constexpr int kComputeUnits = 256;
 constexpr int kMinTilesPerPiece = 4;  // balanced shares
-// fixed pieces: each cut adds a partial state of kRows x (D + 2) floats,
-// written and merged; 8 tiles per piece is the measured sweet spot for one
-// Llama-3-8B-shaped sequence (2k prefix, 60 nodes)
-constexpr int kMinTilesFixed = 8;
+// fixed pieces: each cut adds a partial state of kRows rows, written and
+// merged; 5 tiles per piece (14 pieces, 224 workgroups) is the measured sweet
+// spot for one Llama-3-8B-shaped sequence (2k prefix, 60 nodes): 4 and 6-8
+// were 0.5-2 us slower
+constexpr int kMinTilesFixed = 5;
 
 // Rows of a KV head go to row chunks of 128 (4 waves).  One
 // sequence: fixed pieces of at least kMinTilesFixed tiles, up to one round of
