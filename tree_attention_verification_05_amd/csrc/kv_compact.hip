@@ -17,6 +17,7 @@ namespace tv {
 namespace {
 
 constexpr int kThreads = 256;
+static_assert(kThreads >= TV_MAX_NODES, "one path step per thread");
 
 __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CompactArgs a) {
   __shared__ long long s_src[TV_MAX_NODES];  // head-0 cache row of the source of step j
@@ -27,6 +28,9 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CompactArgs a) {
   const int N = a.N;
   const int32_t* table = a.block_table + static_cast<size_t>(b) * a.max_blocks;
   const int32_t* path = a.accepted_nodes + static_cast<size_t>(b) * N;
+  // step tid's path entries go out together with the lengths (N <= kThreads)
+  const int pj_me = tid < N ? path[tid] : 0;
+  const int pj_prev = (tid >= 1 && tid < N) ? path[tid - 1] : 0;
   const int P = a.prefix_lens[b];
   const int L = a.accept_len[b] + 1;
   if (tid == 0) {
@@ -39,8 +43,8 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CompactArgs a) {
   if (P < 0 || static_cast<long>(P) + N > static_cast<long>(a.max_blocks) * kBlockSize) bad |= TV_DEV_BAD_CACHE;
   if (!bad) {
     for (int j = tid; j < L; j += kThreads) {
-      const int pj = path[j];
-      const bool inc = (j == 0) ? (pj == 0) : (pj > path[j - 1] && pj < N);
+      const int pj = pj_me;
+      const bool inc = (j == 0) ? (pj == 0) : (pj > pj_prev && pj < N);
       if (!inc) {
         bad |= TV_DEV_BAD_TREE;
         continue;
@@ -78,17 +82,33 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CompactArgs a) {
     // head cc / dq sits (cc / dq) * block_size rows after head 0
     const long long col = static_cast<long long>(cc / dq) * kBlockSize * dq + cc % dq;
     for (int j0 = 1; j0 < s_L; j0 += 8) {
-      int4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = j0 + u;
-        if (j < s_L && s_src[j] != s_dst[j]) v[u] = base[s_src[j] * dq + col];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = j0 + u;
-        if (j < s_L && s_src[j] != s_dst[j]) base[s_dst[j] * dq + col] = v[u];
-      }
+      // every lane loads eight rows (steps past L or without a move read
+      // column col of block 0, head 0, slot 0, which is in bounds), so the
+      // batch stays in registers; only real moves are stored
+      const int L = s_L;
+      int4 v0, v1, v2, v3, v4, v5, v6, v7;
+      long long d0, d1, d2, d3, d4, d5, d6, d7;  // destination index, -1: no move
+      auto load = [&](int j, int4& v, long long& d) __attribute__((always_inline)) {
+        const bool mv = j < L && s_src[j] != s_dst[j];
+        v = base[(mv ? s_src[j] * dq : 0) + col];
+        d = mv ? s_dst[j] * dq + col : -1;
+      };
+      load(j0 + 0, v0, d0);
+      load(j0 + 1, v1, d1);
+      load(j0 + 2, v2, d2);
+      load(j0 + 3, v3, d3);
+      load(j0 + 4, v4, d4);
+      load(j0 + 5, v5, d5);
+      load(j0 + 6, v6, d6);
+      load(j0 + 7, v7, d7);
+      if (d0 >= 0) base[d0] = v0;
+      if (d1 >= 0) base[d1] = v1;
+      if (d2 >= 0) base[d2] = v2;
+      if (d3 >= 0) base[d3] = v3;
+      if (d4 >= 0) base[d4] = v4;
+      if (d5 >= 0) base[d5] = v5;
+      if (d6 >= 0) base[d6] = v6;
+      if (d7 >= 0) base[d7] = v7;
     }
   }
 }
