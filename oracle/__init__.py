@@ -293,6 +293,66 @@ def accept_greedy(logits, draft_tokens, parents):
 
 
 # --------------------------------------------------------------------------
+# tree K/V write with rotary positions
+# --------------------------------------------------------------------------
+
+def rope(x, pos, theta: float) -> np.ndarray:
+    """Rotary position embedding along the last axis (D even), rotate-half
+    pairing: the pair (x[j], x[j + D/2]), j < D/2, turns by the angle
+    ``pos * theta ** (-2 j / D)``:
+
+        x'[j]       = x[j] cos(a_j) - x[j + D/2] sin(a_j)
+        x'[j + D/2] = x[j + D/2] cos(a_j) + x[j] sin(a_j)
+
+    The pages do not define the positional encoding; this is the textbook
+    rotary embedding in the layout of the Llama-family target models the
+    pages run (Llama 3, Qwen2).  x: [..., D]; pos: integers broadcastable to
+    x.shape[:-1].  Float64."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    h = D // 2
+    inv = float(theta) ** (-2.0 * np.arange(h, dtype=np.float64) / D)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def tree_positions(parents, prefix_lens) -> np.ndarray:
+    """Rotary position of every tree node: ``P_b + depth(i)``.  Siblings are
+    alternative continuations of the same prefix, so they share a position;
+    along a root-to-leaf path positions are consecutive, as in ordinary
+    decoding of that path (reading of the tree attention layer, "vLLM-TreeEagle"
+    README, 核心组件 item 1: every path is verified as if decoded alone)."""
+    parents = np.asarray(parents)
+    B, N = parents.shape
+    pos = np.zeros((B, N), dtype=np.int64)
+    for b in range(B):
+        _, depth = tree_structure(parents[b])
+        pos[b] = int(prefix_lens[b]) + depth
+    return pos
+
+
+def tree_kv_write(q, k_new, parents, prefix_lens, theta: float):
+    """The tree step's queries and keys at their tree positions, and where
+    the new K/V rows go.
+
+    Source: "EAGLE代码实现原理", KV缓存优化 (``cat()`` appends the new rows
+    after the current length inside the preallocated cache); "P-EAGLE" page,
+    技术难点和解决方案 (the block manager appends the proposed tokens to the
+    paged cache); tree positions as in ``tree_positions``.
+
+    Returns (q_rot [B, N, Hq, D], k_rot [B, N, Hkv, D], positions [B, N]),
+    float64.  Node i's rotated key and its value (unchanged) are stored at
+    logical position ``P_b + i`` (``cache_rows``); no other cache row
+    changes."""
+    pos = tree_positions(parents, prefix_lens)
+    q_rot = rope(q, pos[:, :, None], theta)
+    k_rot = rope(k_new, pos[:, :, None], theta)
+    return q_rot, k_rot, pos
+
+
+# --------------------------------------------------------------------------
 # KV compaction
 # --------------------------------------------------------------------------
 

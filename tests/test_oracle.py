@@ -536,3 +536,95 @@ def test_golden_acceptance_hand_worked():
         assert res["accept_len"][0] == case["expected_accept_len"]
         assert list(res["accepted_nodes"][0]) == case["expected_accepted_nodes"]
         assert res["bonus"][0] == case["expected_bonus"]
+
+
+# ---------------------------------------------------------------- tree K/V write (rotary positions)
+
+def _complex_rope(x, m, theta):
+    """Rotary embedding written as complex multiplication: pair j forms
+    z_j = x[j] + i x[j + D/2], rotated to z_j * exp(i m / theta**(2 j / D))."""
+    x = np.asarray(x, dtype=np.float64)
+    h = x.shape[-1] // 2
+    z = x[..., :h] + 1j * x[..., h:]
+    w = np.exp(1j * m / np.power(float(theta), np.arange(0, x.shape[-1], 2) / x.shape[-1]))
+    r = z * w
+    return np.concatenate([r.real, r.imag], axis=-1)
+
+
+def test_rope_equals_complex_rotation():
+    rng = np.random.default_rng(31)
+    for D, theta in ((2, 1.0), (8, 100.0), (64, 10000.0), (128, 500000.0)):
+        x = rng.standard_normal((5, D))
+        for m in (0, 1, 7, 2048, 32775):
+            np.testing.assert_allclose(O.rope(x, np.full(5, m), theta), _complex_rope(x, m, theta),
+                                       rtol=0, atol=1e-9)
+
+
+def test_rope_known_angles():
+    """D = 4, theta = 10000: pair 0 turns by m radians, pair 1 by m / 100
+    (theta ** (-2/4)); pairs are (0, 2) and (1, 3)."""
+    e = np.eye(4)
+    r = O.rope(e, np.full(4, 100), 10000.0)
+    np.testing.assert_allclose(r[0], [np.cos(100.0), 0, np.sin(100.0), 0], atol=1e-12)
+    np.testing.assert_allclose(r[1], [0, np.cos(1.0), 0, np.sin(1.0)], atol=1e-12)
+    np.testing.assert_allclose(r[2], [-np.sin(100.0), 0, np.cos(100.0), 0], atol=1e-12)
+
+
+def test_rope_identity_norm_relative_and_composition():
+    rng = np.random.default_rng(32)
+    D, theta = 32, 10000.0
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    assert np.array_equal(O.rope(q, 0, theta), q)
+    h = D // 2
+    r = O.rope(q, 12345, theta)
+    np.testing.assert_allclose(r[:h] ** 2 + r[h:] ** 2, q[:h] ** 2 + q[h:] ** 2, rtol=1e-12)
+    for m, n in ((5, 3), (100, 2000), (32768, 7)):
+        lhs = O.rope(q, m, theta) @ O.rope(k, n, theta)
+        rhs = O.rope(q, m - n, theta) @ k
+        assert abs(lhs - rhs) < 1e-9 * (1 + abs(rhs))
+    np.testing.assert_allclose(O.rope(O.rope(q, 700, theta), 333, theta), O.rope(q, 1033, theta),
+                               rtol=0, atol=1e-9)
+
+
+def test_tree_positions_brute_force():
+    rng = np.random.default_rng(33)
+    B, N = 4, 12
+    par = np.zeros((B, N), dtype=np.int64)
+    for b in range(B):
+        par[b, 0] = -1
+        for i in range(1, N):
+            par[b, i] = rng.integers(0, i)
+    P = rng.integers(0, 50, size=B)
+    pos = O.tree_positions(par, P)
+    for b in range(B):
+        for i in range(N):
+            d, c = 0, i
+            while c != 0:
+                c = par[b, c]
+                d += 1
+            assert pos[b, i] == P[b] + d
+    # a chain gets consecutive positions; siblings share one
+    chain = np.array([[-1, 0, 1, 2, 3]])
+    assert list(O.tree_positions(chain, [10])[0]) == [10, 11, 12, 13, 14]
+    star = np.array([[-1, 0, 0, 0]])
+    assert list(O.tree_positions(star, [7])[0]) == [7, 8, 8, 8]
+
+
+def test_tree_kv_write_path_equals_causal_rope_attention():
+    """After the write, every root-to-leaf path attends exactly as causal
+    decoding with RoPE at consecutive positions over [prefix ; path]: scores
+    of rotated pairs depend only on the position difference."""
+    rng = np.random.default_rng(34)
+    B, N, Hq, Hkv, D, theta = 1, 7, 2, 1, 16, 10000.0
+    par = np.array([[-1, 0, 0, 1, 1, 2, 4]])
+    P = 5
+    q = rng.standard_normal((B, N, Hq, D))
+    k_new = rng.standard_normal((B, N, Hkv, D))
+    kpre = O.rope(rng.standard_normal((P, Hkv, D)), np.arange(P)[:, None], theta)
+    q_rot, k_rot, pos = O.tree_kv_write(q, k_new, par, np.array([P]), theta)
+    for i, path in enumerate(root_paths(par[0])):
+        # causal decode of [prefix ; path]: token t sits at position t
+        keys = np.concatenate([kpre, O.rope(k_new[0, path], np.arange(P, P + len(path))[:, None], theta)])
+        qd = O.rope(q[0, i], P + len(path) - 1, theta)
+        tree_keys = np.concatenate([kpre, k_rot[0, path]])
+        np.testing.assert_allclose(q_rot[0, i] @ tree_keys[:, 0].T, qd @ keys[:, 0].T, rtol=0, atol=1e-9)

@@ -4,7 +4,8 @@ Each case plants one mistake in a copy of the oracle's source (a dropped or
 transposed mask term, a wrong GQA index, an off-by-one prefix, a missing
 scale, the wrong argmax tie rule, a greedy instead of longest path, the bonus
 taken at the wrong node, compaction without gather-before-write, a wrong new
-length) and runs the pin suite against that copy in a separate process, on
+length, a flipped rotation, a wrong rotary frequency or pairing, node index
+instead of tree depth as position) and runs the pin suite against that copy in a separate process, on
 the CPU.  The suite must fail for every one of them.
 """
 import os
@@ -38,6 +39,13 @@ MUTANTS = {
         "        for s_, d_ in zip(src[::-1], dst[::-1]):\n"
         "            kf[d_] = kf[s_]; vf[d_] = vf[s_]"),
     "new_length_without_root": ("new_lens[b] = P + L", "new_lens[b] = P + L - 1"),
+    "rope_rotation_sign_flipped": ("[x1 * c - x2 * s, x2 * c + x1 * s]", "[x1 * c + x2 * s, x2 * c - x1 * s]"),
+    "rope_frequency_exponent_halved": ("inv = float(theta) ** (-2.0 * np.arange(h, dtype=np.float64) / D)",
+                                       "inv = float(theta) ** (-1.0 * np.arange(h, dtype=np.float64) / D)"),
+    "rope_interleaved_pairs": ("    x1, x2 = x[..., :h], x[..., h:]\n    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)",
+                               "    x1, x2 = x[..., 0::2], x[..., 1::2]\n    y = np.empty_like(x)\n"
+                               "    y[..., 0::2] = x1 * c - x2 * s\n    y[..., 1::2] = x2 * c + x1 * s\n    return y"),
+    "tree_position_is_node_index": ("pos[b] = int(prefix_lens[b]) + depth", "pos[b] = int(prefix_lens[b]) + np.arange(N)"),
 }
 
 COPY = ["pytest.ini", "workloads", os.path.join("tests", "conftest.py"),
