@@ -213,6 +213,45 @@ TV_API tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks,
                         int32_t N, int32_t Hkv, int32_t D, tv_dtype dtype, int32_t* new_lens,
                         int32_t* dev_status, hipStream_t stream);
 
+/*
+ * tv_tree_kv_write -- rotate the step's queries and new keys to their tree
+ * positions and append the new K/V rows to the paged cache, before
+ * tv_tree_attention.  ("EAGLE代码实现原理", KV缓存优化: cat() appends the new
+ * rows after the current length inside the preallocated cache; "P-EAGLE",
+ * 技术难点和解决方案: the block manager appends the proposed tokens.  The pages
+ * leave the positional encoding open: this is the rotary embedding of the
+ * Llama-family targets, at tree positions.)
+ *
+ * Node i of sequence b takes rotary position pos = P_b + depth[b][i]
+ * (siblings share a position; a root-to-leaf path has consecutive ones).
+ * Every pair (x[j], x[j + D/2]), j < D/2, of each query head and each new key
+ * head turns by the angle pos * rope_theta^(-2j/D):
+ *   x'[j] = x[j] cos - x[j + D/2] sin,  x'[j + D/2] = x[j + D/2] cos + x[j] sin
+ * (angles formed in fp64, rotation in fp32, bf16 results rounded to nearest
+ * even).  The rotated key and the unchanged value of node i are written at
+ * logical position P_b + i of the paged cache; no other row changes.
+ *
+ *   q             [B][N][Hq][D], dtype, device, 16-byte aligned, read.
+ *   k_new, v_new  [B][N][Hkv][D], dtype, device, 16-byte aligned, read.
+ *   depth         [B][N] int32, device (as written by tv_build_tree_mask).
+ *   q_out         [B][N][Hq][D], dtype, device, 16-byte aligned, written;
+ *                 may be q itself (in place).
+ *   k_cache, v_cache, block_table, prefix_lens: as for tv_tree_attention;
+ *                 the caches are updated in place.
+ *   rope_theta    rotary base (> 0), e.g. 500000 for Llama 3.
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE (also rope_theta <= 0), TV_ERR_DTYPE,
+ * TV_ERR_UNSUPPORTED, TV_ERR_ALIGN, TV_ERR_LAUNCH.  Device: TV_DEV_BAD_TREE
+ * (a depth outside [0, N): position P_b is used), TV_DEV_BAD_CACHE (the slot
+ * of P_b + i lies outside the table or names a block outside the cache: that
+ * node's rows are not written).
+ */
+TV_API tv_status tv_tree_kv_write(const void* q, const void* k_new, const void* v_new, const int32_t* depth,
+                           void* q_out, void* k_cache, void* v_cache, int32_t num_blocks,
+                           const int32_t* block_table, int32_t max_blocks, int32_t block_size,
+                           const int32_t* prefix_lens, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                           int32_t D, float rope_theta, tv_dtype dtype, int32_t* dev_status,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

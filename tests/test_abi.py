@@ -103,6 +103,24 @@ def test_compact_host_checks():
     assert call(v=P16 + 2) == 5
 
 
+def test_tree_kv_write_host_checks():
+    f = lib.tv_tree_kv_write
+
+    def call(**kw):
+        a = dict(q=P16, kn=P16, vn=P16, dep=P16, qo=P16, k=P16, v=P16, nb=10, table=P16, mb=4, bs=16,
+                 pl=P16, B=1, N=8, Hq=4, Hkv=2, D=128, theta=10000.0, dt=1, st=None, s=None)
+        a.update(kw)
+        return f(a["q"], a["kn"], a["vn"], a["dep"], a["qo"], a["k"], a["v"], a["nb"], a["table"],
+                 a["mb"], a["bs"], a["pl"], a["B"], a["N"], a["Hq"], a["Hkv"], a["D"], a["theta"],
+                 a["dt"], a["st"], a["s"])
+    assert call(q=None) == 1 and call(dep=None) == 1 and call(qo=None) == 1 and call(v=None) == 1
+    assert call(dt=5) == 3
+    assert call(B=0) == 2 and call(N=300) == 2 and call(Hq=6, Hkv=4) == 2
+    assert call(theta=0.0) == 2 and call(theta=-1.0) == 2
+    assert call(D=96) == 4 and call(bs=32) == 4
+    assert call(qo=P16 + 4) == 5 and call(kn=P16 + 2) == 5
+
+
 def test_accept_workspace_grows_with_rows():
     a = lib.tv_accept_greedy_workspace_size(1, 60, 128256)
     b = lib.tv_accept_greedy_workspace_size(128, 9, 128256)

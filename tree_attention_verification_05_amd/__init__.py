@@ -1,12 +1,14 @@
 """Single-pass verification of a draft token tree on AMD Instinct MI355X.
 
-The four calls of libtv (hand-written HIP kernels for gfx950) with the same
+The calls of libtv (hand-written HIP kernels for gfx950) with the same
 names as the C ABI in ``include/tv.h``:
 
 * ``tv_build_tree_mask``  -- ancestor-or-self bitmask of every tree node
 * ``tv_tree_attention``   -- tree-masked attention over the paged prefix
 * ``tv_accept_greedy``    -- target argmax and the longest accepted path
 * ``tv_kv_compact``       -- move the accepted path's K/V after the prefix
+* ``tv_tree_kv_write``    -- rotate q and the new keys to their tree
+  positions and append the new K/V rows (runs before ``tv_tree_attention``)
 
 Importing the package loads libtv.so and raises if it has not been built.
 """
@@ -26,4 +28,5 @@ from ._lib import (  # noqa: F401
     tv_kv_compact,
     tv_tree_attention,
     tv_tree_attention_workspace_size,
+    tv_tree_kv_write,
 )

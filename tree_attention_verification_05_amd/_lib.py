@@ -58,6 +58,9 @@ def _load() -> ctypes.CDLL:
         "tv_kv_compact": (_c_i32, [_c_ptr, _c_ptr, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr, _c_ptr,
                                    _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
                                    _c_ptr]),
+        "tv_tree_kv_write": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32,
+                                      _c_ptr, _c_i32, _c_i32, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32,
+                                      _c_i32, ctypes.c_float, _c_i32, _c_ptr, _c_ptr]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -257,3 +260,35 @@ def tv_kv_compact(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: tor
         _ptr(prefix_lens), _ptr(accepted_nodes), _ptr(accept_len), B, N, Hkv, D, dt,
         _ptr(new_lens), _ptr(dev_status), _stream(k_cache)))
     return new_lens
+
+
+def tv_tree_kv_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, depth: torch.Tensor,
+                     k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                     prefix_lens: torch.Tensor, rope_theta: float, q_out: Optional[torch.Tensor] = None,
+                     dev_status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q [B, N, Hq, D]; k_new, v_new [B, N, Hkv, D]; depth int32 [B, N] (from
+    tv_build_tree_mask); caches [num_blocks, Hkv, 16, D] updated in place at
+    positions P_b + i.  Returns the rotated queries (q_out, may be q)."""
+    dt = _tv_dtype(q)
+    _dev(q, "q", q.dtype)
+    B, N, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape  # [num_blocks, Hkv, block_size, D]
+    _dev(k_new, "k_new", q.dtype, (B, N, Hkv, D))
+    _dev(v_new, "v_new", q.dtype, (B, N, Hkv, D))
+    _dev(depth, "depth", torch.int32, (B, N))
+    _dev(k_cache, "k_cache", q.dtype, (nb, Hkv, bs, D))
+    _dev(v_cache, "v_cache", q.dtype, (nb, Hkv, bs, D))
+    _dev(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _dev(prefix_lens, "prefix_lens", torch.int32, (B,))
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _dev(q_out, "q_out", q.dtype, q.shape)
+    if dev_status is not None:
+        _dev(dev_status, "dev_status", torch.int32)
+    _check("tv_tree_kv_write", lib.tv_tree_kv_write(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(depth), _ptr(q_out), _ptr(k_cache), _ptr(v_cache), nb,
+        _ptr(block_table), block_table.shape[1], bs, _ptr(prefix_lens), B, N, Hq, Hkv, D,
+        float(rope_theta), dt, _ptr(dev_status), _stream(q)))
+    return q_out

@@ -1,0 +1,134 @@
+// Tree K/V write with rotary positions ("EAGLE代码实现原理", KV缓存优化: cat()
+// appends the step's new rows after the current length inside the
+// preallocated cache; "P-EAGLE", 技术难点和解决方案: the block manager appends
+// the proposed tokens to the paged cache).  Node i of sequence b is rotated
+// to position P_b + depth(i): siblings share a position, and every
+// root-to-leaf path carries consecutive positions, as if decoded alone.
+//
+// One workgroup per (sequence, node).  The D/2 rotation angles of the node
+// are formed in fp64 (positions reach tens of thousands of radians) and
+// reduced to fp32 (cos, sin) in LDS; each thread then turns four (x[j],
+// x[j + D/2]) pairs of one head at a time, reading both halves before
+// writing them, so q_out may alias q.  The rotated key and the value go to
+// logical position P_b + i of the paged cache ([block][head][slot][dim]).
+// The step is a stream of small rows: HBM-bound.
+#include <math.h>
+
+#include "tv_internal.h"
+
+namespace tv {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+struct Vec4;
+template <>
+struct Vec4<float> {
+  typedef float4 type;
+  __device__ static void load(const float* p, float (&x)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  }
+  __device__ static void store(float* p, const float (&x)[4]) {
+    *reinterpret_cast<float4*>(p) = float4{x[0], x[1], x[2], x[3]};
+  }
+};
+template <>
+struct Vec4<uint16_t> {
+  __device__ static void load(const uint16_t* p, float (&x)[4]) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    x[0] = __uint_as_float(v.x << 16);
+    x[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(v.y << 16);
+    x[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  }
+  __device__ static void store(uint16_t* p, const float (&x)[4]) {
+    uint2 v;
+    v.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+    v.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+    *reinterpret_cast<uint2*>(p) = v;
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void tree_kv_write_kernel(KvWriteArgs a) {
+  __shared__ float s_cos[64], s_sin[64];
+  const int node = blockIdx.x % a.N, b = blockIdx.x / a.N;
+  const int tid = threadIdx.x;
+  const int D = a.D, h = D / 2;
+  const size_t nidx = static_cast<size_t>(b) * a.N + node;
+  const int P = a.prefix_lens[b];
+  int d = a.depth[nidx];
+  // where the node's K/V rows go: logical position P + node
+  const long t = static_cast<long>(P) + node;
+  int blk = -1;
+  if (P >= 0 && t < static_cast<long>(a.max_blocks) * kBlockSize) blk = a.block_table[static_cast<size_t>(b) * a.max_blocks + t / kBlockSize];
+  if (tid == 0) {
+    if (d < 0 || d >= a.N) report(a.dev_status, TV_DEV_BAD_TREE);
+    if (blk < 0 || blk >= a.num_blocks) report(a.dev_status, TV_DEV_BAD_CACHE);
+  }
+  d = (d < 0 || d >= a.N) ? 0 : d;
+  const double pos = static_cast<double>(P < 0 ? 0 : P) + d;
+  if (tid < h) {
+    // pos * theta^(-2 j / D) in fp64, then fp32 cos and sin of it
+    const double ang = pos * pow(static_cast<double>(a.theta), -2.0 * tid / D);
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    s_cos[tid] = static_cast<float>(cs);
+    s_sin[tid] = static_cast<float>(sn);
+  }
+  __syncthreads();
+
+  const int quads = h / 4;  // groups of four pairs per head row
+  const T* q = static_cast<const T*>(a.q) + nidx * a.Hq * D;
+  T* qo = static_cast<T*>(a.q_out) + nidx * a.Hq * D;
+  const T* kn = static_cast<const T*>(a.k_new) + nidx * a.Hkv * D;
+  const T* vn = static_cast<const T*>(a.v_new) + nidx * a.Hkv * D;
+  const bool write_cache = blk >= 0 && blk < a.num_blocks;
+  const int slot = static_cast<int>(t % kBlockSize);
+  T* kc = static_cast<T*>(a.k_cache);
+  T* vc = static_cast<T*>(a.v_cache);
+  // items: Hq query rows, then Hkv key rows (rotated), then Hkv value rows (copied)
+  const int items = (a.Hq + a.Hkv) * quads + a.Hkv * (D / 4);
+  for (int it = tid; it < items; it += kThreads) {
+    if (it < (a.Hq + a.Hkv) * quads) {
+      const int row = it / quads, j = (it % quads) * 4;
+      const bool is_q = row < a.Hq;
+      if (!is_q && !write_cache) continue;
+      const T* src = is_q ? q + row * D : kn + (row - a.Hq) * D;
+      float x1[4], x2[4], y1[4], y2[4];
+      Vec4<T>::load(src + j, x1);
+      Vec4<T>::load(src + j + h, x2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float c = s_cos[j + e], s = s_sin[j + e];
+        y1[e] = x1[e] * c - x2[e] * s;
+        y2[e] = x2[e] * c + x1[e] * s;
+      }
+      T* dst = is_q ? qo + row * D
+                    : kc + ((static_cast<size_t>(blk) * a.Hkv + (row - a.Hq)) * kBlockSize + slot) * D;
+      Vec4<T>::store(dst + j, y1);
+      Vec4<T>::store(dst + j + h, y2);
+    } else if (write_cache) {
+      const int v_it = it - (a.Hq + a.Hkv) * quads;
+      const int head = v_it / (D / 4), j = (v_it % (D / 4)) * 4;
+      float x[4];
+      Vec4<T>::load(vn + head * D + j, x);
+      Vec4<T>::store(vc + ((static_cast<size_t>(blk) * a.Hkv + head) * kBlockSize + slot) * D + j, x);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tree_kv_write(const KvWriteArgs& a, tv_dtype dtype, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(a.B * a.N));
+  if (dtype == TV_BF16)
+    hipLaunchKernelGGL(tree_kv_write_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(tree_kv_write_kernel<float>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tv

@@ -155,4 +155,43 @@ tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks, const 
   return launched(launch_kv_compact(a, stream));
 }
 
+tv_status tv_tree_kv_write(const void* q, const void* k_new, const void* v_new, const int32_t* depth,
+                           void* q_out, void* k_cache, void* v_cache, int32_t num_blocks,
+                           const int32_t* block_table, int32_t max_blocks, int32_t block_size,
+                           const int32_t* prefix_lens, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                           int32_t D, float rope_theta, tv_dtype dtype, int32_t* dev_status,
+                           hipStream_t stream) {
+  if (!q || !k_new || !v_new || !depth || !q_out || !k_cache || !v_cache || !block_table || !prefix_lens)
+    return TV_ERR_NULL;
+  if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
+  if (B <= 0 || N <= 0 || N > TV_MAX_NODES || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || num_blocks <= 0 ||
+      max_blocks <= 0 || !(rope_theta > 0.f))
+    return TV_ERR_SHAPE;
+  if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
+  if (block_size != kBlockSize) return TV_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(q_out) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return TV_ERR_ALIGN;
+  KvWriteArgs a;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.depth = depth;
+  a.q_out = q_out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = num_blocks;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.prefix_lens = prefix_lens;
+  a.B = B;
+  a.N = N;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.theta = rope_theta;
+  a.dev_status = dev_status;
+  return launched(launch_tree_kv_write(a, dtype, stream));
+}
+
 }  // extern "C"

@@ -95,4 +95,22 @@ struct CompactArgs {
 };
 hipError_t launch_kv_compact(const CompactArgs& a, hipStream_t stream);
 
+struct KvWriteArgs {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* depth;
+  void* q_out;
+  void* k_cache;
+  void* v_cache;
+  int num_blocks;
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* prefix_lens;
+  int B, N, Hq, Hkv, D;
+  float theta;
+  int32_t* dev_status;
+};
+hipError_t launch_tree_kv_write(const KvWriteArgs& a, tv_dtype dtype, hipStream_t stream);
+
 }  // namespace tv

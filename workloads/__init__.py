@@ -49,6 +49,17 @@ _CHUNK = 1 << 22  # elements per independently seeded chunk of a dense tensor
 
 # component tags of the random streams
 _C_PREFIX, _C_TREE, _C_MATCH, _C_BLOCKS, _C_Q, _C_K, _C_V, _C_LOGITS, _C_PLANT = range(1, 10)
+_C_KNEW, _C_VNEW = 10, 11
+
+# Rotary base of the model family each workload is shaped after: Qwen2
+# 1000000; the Llama-3-shaped layers (8B, the batched 32/8-head layer, the
+# 70B share) 500000; the tiny case the classic 10000.
+def rope_theta(spec) -> float:
+    if "qwen2" in spec.name:
+        return 1000000.0
+    if "tiny" in spec.name:
+        return 10000.0
+    return 500000.0
 
 
 @dataclasses.dataclass(frozen=True)
@@ -393,3 +404,14 @@ def make_config(i: int, seed: int = 0, **kw) -> Workload:
 
 def make_small(i: int, seed: int = 0, **kw) -> Workload:
     return build(SMALL[i], seed, **kw)
+
+
+def tree_kv_inputs(spec, seed: int = 0):
+    """The step's new key and value rows of every tree node, [B, N, Hkv, D]
+    in the workload's element type, N(0, 1), for the tree K/V write; they
+    are drawn from streams of their own, so the rest of the workload is
+    unchanged."""
+    shape = (spec.B, spec.N, spec.Hkv, spec.D)
+    k = _to_dtype(_normal(shape, 1.0, seed, spec.tag, _C_KNEW), spec.dtype)
+    v = _to_dtype(_normal(shape, 1.0, seed, spec.tag, _C_VNEW), spec.dtype)
+    return k, v
