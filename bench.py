@@ -16,6 +16,10 @@ step.  The K timed steps carry one event pair each; a second pass of K steps
 with an event between every call gives the per-call times.  Compaction
 rewrites the tree slots in place; later steps accept the same paths and move
 the same number of rows, so the work per step is unchanged.
+
+The tree K/V write (rotary positions and paged append of the step's new
+rows, the path's upstream neighbour) is timed on its own, K calls after an
+eviction each, and reported under `extra_calls`; it is not part of `value`.
 """
 from __future__ import annotations
 
@@ -39,6 +43,7 @@ KERNEL_SOURCES = {
     "tv_accept_greedy": ["accept.hip"],
     "tv_kv_compact": ["kv_compact.hip"],
     "tv_build_tree_mask": ["tree_mask.hip"],
+    "tv_tree_kv_write": ["tree_kv_write.hip"],
 }
 
 
@@ -203,6 +208,25 @@ def main():
     per = np.array([[evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(4)]
                     for s in range(args.steps)])  # ms
 
+    # ---- the tree K/V write (the step's upstream neighbour, before the mask
+    # and attention): timed on its own, K calls after an eviction each ----
+    k_new, v_new = W.tree_kv_inputs(spec, args.seed)
+    k_new, v_new = k_new.to(dev), v_new.to(dev)
+    q_rot = torch.empty_like(q)
+    theta = W.rope_theta(spec)
+    for _ in range(args.warmup):
+        T.tv_tree_kv_write(q, k_new, v_new, depth, k, v, table, prefix, theta, q_out=q_rot,
+                           dev_status=status)
+    kvw_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        evict()
+        kvw_ev[s][0].record(stream)
+        T.tv_tree_kv_write(q, k_new, v_new, depth, k, v, table, prefix, theta, q_out=q_rot,
+                           dev_status=status)
+        kvw_ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    kvw_ms = np.array([e[0].elapsed_time(e[1]) for e in kvw_ev])
+
     # back-to-back steps with warm caches, for reference
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -232,6 +256,16 @@ def main():
         if work[n].get("flops"):
             kern[n]["flops"] = int(work[n]["flops"])
             kern[n]["TFLOP_s"] = round(work[n]["flops"] / (t_us * 1e-6) / 1e12, 2)
+
+    # the tree K/V write, outside the step: its own time and algorithmic bytes
+    elt = 2 if dt == T.TV_BF16 else 4
+    kvw_bytes = (2 * B * N * spec.Hq * spec.D * elt          # q read, q_out written
+                 + 4 * B * N * spec.Hkv * spec.D * elt       # k_new, v_new read; K/V rows written
+                 + B * N * 4 + B * 4 + B * N * 4)            # depth, prefix, one table entry per node
+    kvw_us = float(kvw_ms.mean()) * 1e3
+    extra = {"tv_tree_kv_write": {"us": round(kvw_us, 3), "us_median": round(float(np.median(kvw_ms)) * 1e3, 3),
+                                  "bytes": int(kvw_bytes), "GB_s": round(kvw_bytes / (kvw_us * 1e-6) / 1e9, 1),
+                                  "rope_theta": theta, "in_step": False}}
 
     # roofline of the dominant call
     dom = max(names, key=lambda n: kern[n]["us"])
@@ -269,6 +303,7 @@ def main():
                    "block_size": spec.block_size, "cache_flushed_between_steps": flush is not None},
         "roofline": roof,
         "kernels": kern,
+        "extra_calls": extra,
         "warm_cache_ms_per_step": round(warm_ms, 5),
         "wall_s_timed_region": round(t_wall, 4),
         "mean_accept_len": float(acc_len.float().mean().item()),
