@@ -29,7 +29,9 @@ Sources (web pages; cited by title and section):
   appends to it.
 * "vLLM EAGLE 投机解码实战：EAGLE/EAGLE3 草稿模型配置、源码实现与接受率评测" --
   section 无损性保障: greedy speculative decoding must produce exactly what
-  greedy decoding produces.
+  greedy decoding produces, and sampled speculative decoding must keep the
+  target distribution (its rejection sampler is tested for convergence to
+  it).
 
 Readings taken where the pages are silent (each is also listed with the
 design notes):
@@ -51,6 +53,12 @@ design notes):
   token is the target's choice at the last accepted node.  Compaction moves
   ``accept_len + 1`` cache rows (root plus accepted drafts) and the new
   length is ``prefix_len + accept_len + 1``.
+* Stochastic acceptance: the speculative-sampling rule (accept a proposal x
+  from q with probability min(1, r(x)/q(x)), else continue from the
+  normalised positive part of r - q), applied to the children of a node in
+  index order; a deterministic proposal is the point mass on its token.  The
+  random numbers are inputs: one uniform per node and one Exp(1) variate per
+  vocabulary entry for the final draw (largest r[v] / E[v]).
 
 Parity pins for every function here live in the CPU test suite (brute force,
 closed forms, textbook special cases, invariants).
@@ -63,6 +71,8 @@ import numpy as np
 ST_BAD_TREE = 1      # parents[0] != -1 or parents[i] outside [0, i)
 ST_BAD_CACHE = 2     # a block id outside [0, num_blocks) or prefix_len > max_prefix_len
 ST_BAD_TOKEN = 4     # a draft token (nodes >= 1) outside [0, V)
+ST_BAD_RANDOM = 8    # a uniform outside [0, 1) or an exponential variate not in (0, inf)
+ST_UNSUPPORTED = 16  # proposal distributions given for a tree that is not a chain
 
 
 # --------------------------------------------------------------------------
@@ -293,6 +303,145 @@ def accept_greedy(logits, draft_tokens, parents):
 
 
 # --------------------------------------------------------------------------
+# stochastic acceptance (temperature > 0)
+# --------------------------------------------------------------------------
+
+def target_probs(logits_row, temperature: float) -> np.ndarray:
+    """The target's sampling distribution at a node: softmax(logits / T)
+    over the vocabulary ("P-EAGLE" page, 技术原理和实现方式 step 3: the target
+    scores every proposed token in one pass; 需要注意的问题: the temperature
+    sets how random the target's choice is)."""
+    z = np.asarray(logits_row, dtype=np.float64) / float(temperature)
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def residual(r, q) -> np.ndarray:
+    """What is left of the distribution r after a proposal drawn from q was
+    rejected: the positive part of r - q, normalised.  If that part has no
+    mass (only possible through rounding, since a rejection needs
+    r(x) < q(x)), r is kept."""
+    d = np.maximum(np.asarray(r, dtype=np.float64) - q, 0.0)
+    m = d.sum()
+    return d / m if m > 0 else np.asarray(r, dtype=np.float64)
+
+
+def race_draw(r, expo):
+    """One draw from the distribution proportional to r, given one Exp(1)
+    variate per vocabulary entry: the index with the largest r[v] / E[v]
+    (the first of equals).  Returns (index, relative gap between the best and
+    the runner-up ratio)."""
+    t = np.asarray(r, dtype=np.float64) / np.asarray(expo, dtype=np.float64)
+    i = int(np.argmax(t))
+    if len(t) > 1 and t[i] > 0:
+        second = np.max(np.delete(t, i))
+        gap = (t[i] - second) / t[i]
+    else:
+        gap = 1.0
+    return i, float(gap)
+
+
+def stochastic_walk(logits, draft_tokens, parents, temperature: float, uniforms, expo,
+                    draft_probs=None):
+    """Stochastic verification of one draft tree.
+
+    Source: "P-EAGLE" page, 技术原理和实现方式 steps 3-4 (the target's
+    probabilities of the proposed tokens are compared with the drafter's,
+    the sampling rule decides acceptance, the sequence is cut at the first
+    rejection); "vLLM EAGLE 投机解码实战", 无损性保障 (sampling stays
+    lossless up to floating-point precision, and the rejection sampler is
+    tested for convergence to the target distribution).  The rule that does
+    both is the speculative-sampling rule: a token x proposed from q is
+    accepted with probability min(1, r(x) / q(x)) where r is the target
+    distribution, and after a rejection the remaining choice is drawn from
+    the normalised positive part of r - q.  On a tree it is applied to the
+    children of the current node in index order, each child tested against
+    the residual that the rejections of its earlier siblings left.
+
+    Inputs of one sequence: logits [N, V] (row i = target scores after node
+    i), draft_tokens [N], parents [N], temperature T > 0, uniforms [N]
+    (uniforms[c] in [0, 1) decides child c; entry 0 is unused), expo [V]
+    (Exp(1) variates for the final draw), draft_probs [N, V] or None (row c
+    = the distribution node c's token was drawn from; None means every token
+    was proposed deterministically, a point mass on it, as the top-k
+    expansion of an EAGLE-2 tree does).
+
+    From node u (start at the root) with r = softmax(logits[u] / T): for
+    each child c of u in increasing index, x = draft_tokens[c], q = the
+    proposal of c; c is accepted iff uniforms[c] * q(x) < r(x), and then the
+    walk moves to c.  A rejection replaces r by residual(r, q).  When every
+    child is rejected (or u is a leaf) the bonus token is drawn from r by
+    the exponential race.
+
+    Returns (path, bonus, margin): the accepted nodes from the root, the
+    bonus token, and the smallest relative margin of any decision taken (an
+    acceptance test |u q(x) - r(x)| / max(u q(x), r(x)), or the gap of the
+    final draw), which tells how close a run came to a different result.
+    """
+    logits = np.asarray(logits)
+    parents = np.asarray(parents)
+    draft_tokens = np.asarray(draft_tokens)
+    N, V = logits.shape
+    path = [0]
+    margin = 1.0
+    cur = 0
+    while True:
+        r = target_probs(logits[cur], temperature)
+        moved = False
+        for c in range(cur + 1, N):
+            if parents[c] != cur:
+                continue
+            x = int(draft_tokens[c])
+            if draft_probs is None:
+                q = np.zeros(V)
+                q[x] = 1.0
+            else:
+                q = np.asarray(draft_probs[c], dtype=np.float64)
+            lhs = float(uniforms[c]) * q[x]
+            top = max(lhs, r[x])
+            if top > 0:
+                margin = min(margin, abs(lhs - r[x]) / top)
+            if lhs < r[x]:
+                path.append(c)
+                cur = c
+                moved = True
+                break
+            r = residual(r, q)
+        if not moved:
+            bonus, gap = race_draw(r, expo)
+            return path, bonus, min(margin, gap)
+
+
+def accept_stochastic(logits, draft_tokens, parents, temperature: float, uniforms, expo,
+                      draft_probs=None):
+    """Batched stochastic acceptance: logits [B, N, V], draft_tokens [B, N],
+    parents [B, N], uniforms [B, N], expo [B, V], draft_probs [B, N, V] or
+    None -> dict with accept_len [B], accepted_nodes [B, N] (path from the
+    root, -1 padded), bonus [B] and margin [B] (see ``stochastic_walk``).
+    A sequence whose tree or draft tokens are invalid gets path [0] and a
+    bonus drawn from the root's distribution, as if nothing was proposed."""
+    logits = np.asarray(logits)
+    B, N, V = logits.shape
+    accept_len = np.zeros(B, dtype=np.int32)
+    nodes = np.full((B, N), -1, dtype=np.int32)
+    bonus = np.zeros(B, dtype=np.int32)
+    margin = np.ones(B)
+    for b in range(B):
+        tok = np.asarray(draft_tokens[b])
+        if not tree_valid(parents[b]) or np.any(tok[1:] < 0) or np.any(tok[1:] >= V):
+            path = [0]
+            bon, mg = race_draw(target_probs(logits[b, 0], temperature), expo[b])
+        else:
+            path, bon, mg = stochastic_walk(logits[b], tok, parents[b], temperature, uniforms[b],
+                                            expo[b], None if draft_probs is None else draft_probs[b])
+        accept_len[b] = len(path) - 1
+        nodes[b, :len(path)] = path
+        bonus[b] = bon
+        margin[b] = mg
+    return {"accept_len": accept_len, "accepted_nodes": nodes, "bonus": bonus, "margin": margin}
+
+
+# --------------------------------------------------------------------------
 # tree K/V write with rotary positions
 # --------------------------------------------------------------------------
 
@@ -392,12 +541,17 @@ def kv_compact(k_cache, v_cache, block_table, prefix_lens, accepted_nodes, accep
 # --------------------------------------------------------------------------
 
 def input_status(parents, block_table=None, prefix_lens=None, num_blocks=None,
-                 max_prefix_len=None, block_size=16, draft_tokens=None, V=None) -> int:
+                 max_prefix_len=None, block_size=16, draft_tokens=None, V=None,
+                 uniforms=None, expo=None, proposal_rows=False) -> int:
     """Status bits a verification call should report for these inputs:
     ST_BAD_TREE for an invalid parent array, ST_BAD_CACHE for a block id
     outside [0, num_blocks) among the blocks a sequence uses (prefix plus
     tree) or a prefix longer than ``max_prefix_len``, ST_BAD_TOKEN for a draft
-    token of a non-root node outside [0, V)."""
+    token of a non-root node outside [0, V), ST_BAD_RANDOM for a uniform of
+    a non-root node outside [0, 1) or an exponential variate outside
+    (0, inf), ST_UNSUPPORTED when proposal rows come with a valid tree that
+    is not a chain (the library takes proposal distributions on chains
+    only; the oracle's walk itself has no such limit)."""
     st = 0
     parents = np.asarray(parents)
     B, N = parents.shape
@@ -418,4 +572,16 @@ def input_status(parents, block_table=None, prefix_lens=None, num_blocks=None,
         d = np.asarray(draft_tokens)[:, 1:]
         if np.any(d < 0) or np.any(d >= V):
             st |= ST_BAD_TOKEN
+    if uniforms is not None:
+        u = np.asarray(uniforms)[:, 1:]
+        if not np.all((u >= 0) & (u < 1)):
+            st |= ST_BAD_RANDOM
+    if expo is not None:
+        e = np.asarray(expo)
+        if not np.all((e > 0) & np.isfinite(e)):
+            st |= ST_BAD_RANDOM
+    if proposal_rows:
+        for b in range(B):
+            if tree_valid(parents[b]) and np.any(parents[b][1:] != np.arange(N - 1)):
+                st |= ST_UNSUPPORTED
     return st

@@ -5,8 +5,13 @@ transposed mask term, a wrong GQA index, an off-by-one prefix, a missing
 scale, the wrong argmax tie rule, a greedy instead of longest path, the bonus
 taken at the wrong node, compaction without gather-before-write, a wrong new
 length, a flipped rotation, a wrong rotary frequency or pairing, node index
-instead of tree depth as position) and runs the pin suite against that copy in a separate process, on
-the CPU.  The suite must fail for every one of them.
+instead of tree depth as position, and in stochastic acceptance: siblings
+tested in the wrong order, the acceptance test reversed, the temperature
+dropped, a residual that keeps the rejected mass or is not normalised, the
+final draw multiplying instead of dividing, the proposal probability
+dropped, the target row of the wrong node) and runs the pin suites against
+that copy in a separate process, on the CPU.  The suites must fail for
+every one of them.
 """
 import os
 import shutil
@@ -46,10 +51,25 @@ MUTANTS = {
                                "    x1, x2 = x[..., 0::2], x[..., 1::2]\n    y = np.empty_like(x)\n"
                                "    y[..., 0::2] = x1 * c - x2 * s\n    y[..., 1::2] = x2 * c + x1 * s\n    return y"),
     "tree_position_is_node_index": ("pos[b] = int(prefix_lens[b]) + depth", "pos[b] = int(prefix_lens[b]) + np.arange(N)"),
+    "stochastic_children_descending": ("        for c in range(cur + 1, N):\n            if parents[c] != cur:\n                continue",
+                                       "        for c in range(N - 1, cur, -1):\n            if parents[c] != cur:\n                continue"),
+    "stochastic_accept_when_uniform_above": ("            if lhs < r[x]:", "            if lhs > r[x]:"),
+    "stochastic_temperature_ignored": ("z = np.asarray(logits_row, dtype=np.float64) / float(temperature)",
+                                       "z = np.asarray(logits_row, dtype=np.float64)"),
+    "stochastic_residual_keeps_rejected_mass": ("d = np.maximum(np.asarray(r, dtype=np.float64) - q, 0.0)",
+                                                "d = np.maximum(np.asarray(r, dtype=np.float64), 0.0)"),
+    "stochastic_residual_unnormalised": ("return d / m if m > 0 else np.asarray(r, dtype=np.float64)",
+                                         "return d if m > 0 else np.asarray(r, dtype=np.float64)"),
+    "stochastic_race_multiplies": ("t = np.asarray(r, dtype=np.float64) / np.asarray(expo, dtype=np.float64)",
+                                   "t = np.asarray(r, dtype=np.float64) * np.asarray(expo, dtype=np.float64)"),
+    "stochastic_acceptance_ignores_proposal": ("lhs = float(uniforms[c]) * q[x]", "lhs = float(uniforms[c])"),
+    "stochastic_target_row_of_child": ("        r = target_probs(logits[cur], temperature)\n        moved = False",
+                                       "        r = target_probs(logits[min(cur + 1, N - 1)], temperature)\n        moved = False"),
 }
 
+PIN_FILES = [os.path.join("tests", "test_oracle.py"), os.path.join("tests", "test_oracle_stochastic.py")]
 COPY = ["pytest.ini", "workloads", os.path.join("tests", "conftest.py"),
-        os.path.join("tests", "test_oracle.py"), os.path.join("tests", "golden")]
+        os.path.join("tests", "golden")] + PIN_FILES
 
 
 def _run_mutant(base, name, old, new):
@@ -68,7 +88,7 @@ def _run_mutant(base, name, old, new):
         f.write(src.replace(old, new))
     env = dict(os.environ, OMP_NUM_THREADS="2", OPENBLAS_NUM_THREADS="2", MKL_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "tests/test_oracle.py"], cwd=d, capture_output=True, text=True, env=env,
+                        *PIN_FILES], cwd=d, capture_output=True, text=True, env=env,
                        timeout=600)
     tail = (r.stdout.strip().splitlines() or [""])[-1]
     return name, r.returncode, tail
