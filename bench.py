@@ -18,8 +18,10 @@ rewrites the tree slots in place; later steps accept the same paths and move
 the same number of rows, so the work per step is unchanged.
 
 The tree K/V write (rotary positions and paged append of the step's new
-rows, the path's upstream neighbour) is timed on its own, K calls after an
-eviction each, and reported under `extra_calls`; it is not part of `value`.
+rows, the path's upstream neighbour) and stochastic acceptance (temperature
+> 0, the alternative to the greedy call) are timed on their own, K calls
+after an eviction each, and reported under `extra_calls`; they are not part
+of `value`.
 """
 from __future__ import annotations
 
@@ -44,6 +46,7 @@ KERNEL_SOURCES = {
     "tv_kv_compact": ["kv_compact.hip"],
     "tv_build_tree_mask": ["tree_mask.hip"],
     "tv_tree_kv_write": ["tree_kv_write.hip"],
+    "tv_accept_stochastic": ["accept_stochastic.hip"],
 }
 
 
@@ -227,6 +230,38 @@ def main():
     torch.cuda.synchronize()
     kvw_ms = np.array([e[0].elapsed_time(e[1]) for e in kvw_ev])
 
+    # ---- stochastic acceptance (temperature > 0), the alternative to the
+    # greedy call: timed on its own, K calls after an eviction each; chains
+    # carry proposal rows, trees point-mass proposals ----
+    chain = spec.tree[0] == "chain"
+    sx = W.stochastic_inputs(spec, args.seed, w.logits, proposals=chain)
+    s_tok = (sx["draft_tokens"] if chain else torch.from_numpy(w.draft_tokens)).to(dev)
+    s_u, s_e = sx["uniforms"].to(dev), sx["expo"].to(dev)
+    s_q = sx["draft_probs"].to(dev) if chain else None
+    s_al = torch.empty(B, dtype=torch.int32, device=dev)
+    s_an = torch.empty((B, N), dtype=torch.int32, device=dev)
+    s_bt = torch.empty(B, dtype=torch.int32, device=dev)
+    s_ws = torch.zeros(max(int(T.lib.tv_accept_stochastic_workspace_size(B, N, V)), 16),
+                       dtype=torch.uint8, device=dev)
+
+    def run_stochastic():
+        T.tv_accept_stochastic(logits, s_tok, parents, sx["temperature"], s_u, s_e, s_q,
+                               accept_len=s_al, accepted_nodes=s_an, bonus_token=s_bt,
+                               workspace=s_ws, dev_status=status)
+    for _ in range(args.warmup):
+        run_stochastic()
+    st_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        evict()
+        st_ev[s][0].record(stream)
+        run_stochastic()
+        st_ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    st_ms = np.array([e[0].elapsed_time(e[1]) for e in st_ev])
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())} after the stochastic call")
+    s_al_h = s_al.cpu().numpy()
+
     # back-to-back steps with warm caches, for reference
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -266,6 +301,19 @@ def main():
     extra = {"tv_tree_kv_write": {"us": round(kvw_us, 3), "us_median": round(float(np.median(kvw_ms)) * 1e3, 3),
                                   "bytes": int(kvw_bytes), "GB_s": round(kvw_bytes / (kvw_us * 1e-6) / 1e9, 1),
                                   "rope_theta": theta, "in_step": False}}
+
+    # stochastic acceptance: the logits scan, the gathers of the tree, and
+    # one row each of logits and Exp(1) variates per sequence for the draw
+    # (plus the rejected child's proposal row on chains that stopped early)
+    st_us = float(st_ms.mean()) * 1e3
+    rejected = int((s_al_h < N - 1).sum()) if chain else 0
+    st_bytes = (B * N * V * 4 + B * N * 4 * (4 + (1 if chain else 0))
+                + B * V * 8 + rejected * V * 4)
+    extra["tv_accept_stochastic"] = {
+        "us": round(st_us, 3), "us_median": round(float(np.median(st_ms)) * 1e3, 3),
+        "bytes": int(st_bytes), "GB_s": round(st_bytes / (st_us * 1e-6) / 1e9, 1),
+        "temperature": sx["temperature"], "proposals": "rows" if chain else "point mass",
+        "mean_accept_len": float(s_al_h.mean()), "in_step": False}
 
     # roofline of the dominant call
     dom = max(names, key=lambda n: kern[n]["us"])

@@ -80,6 +80,10 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_DEV_BAD_CACHE 2  /* a used block id outside [0, num_blocks), or a prefix
                                length outside [0, max_prefix_len] */
 #define TV_DEV_BAD_TOKEN 4  /* draft_tokens[b][i] (i >= 1) outside [0, V) */
+#define TV_DEV_BAD_RANDOM 8 /* a uniform (i >= 1) outside [0, 1) or an exponential
+                               variate of the drawn row outside (0, inf) */
+#define TV_DEV_UNSUPPORTED 16 /* proposal rows given for a tree that is not a
+                                 chain (parents[b][i] != i - 1) */
 
 /* Name of a status code (static string). */
 TV_API const char* tv_status_string(tv_status s);
@@ -183,6 +187,59 @@ TV_API tv_status tv_accept_greedy(const float* logits, const int32_t* draft_toke
                            int32_t* accepted_nodes, int32_t* bonus_token, int32_t* target_argmax,
                            void* workspace, size_t workspace_bytes, int32_t* dev_status,
                            hipStream_t stream);
+
+/*
+ * Workspace bytes tv_accept_stochastic needs (per-chunk row statistics, one
+ * stop record per sequence, per-chunk draw keys); 0 for invalid sizes.  The
+ * workspace needs no initialisation; calls that share one must be ordered.
+ */
+TV_API size_t tv_accept_stochastic_workspace_size(int32_t B, int32_t N, int32_t V);
+
+/*
+ * tv_accept_stochastic -- stochastic verification of the draft tree at
+ * temperature > 0: accepted path and bonus token.
+ * ("P-EAGLE", 技术原理和实现方式 steps 3-4: target and draft probabilities of
+ * the proposed tokens are compared, a sampling rule accepts, the sequence is
+ * cut at the first rejection; "vLLM EAGLE 投机解码实战", 无损性保障: the
+ * rejection sampler keeps the target distribution.)
+ *
+ * p_i = softmax(logits[b][i] / temperature).  From node u = 0 with r = p_u,
+ * the children c of u are tested in increasing index: with x =
+ * draft_tokens[b][c] and q_c its proposal (draft_probs[b][c], or the point
+ * mass on x when draft_probs is NULL), c is accepted iff
+ * uniforms[b][c] * q_c(x) < r(x), and the walk continues at c; a rejection
+ * replaces r by max(r - q_c, 0) normalised (kept as is if that has no mass).
+ * When every child of u is rejected, or u is a leaf, the bonus token is the
+ * v with the largest r(v) / exponentials[b][v] (lowest v among equals).
+ * Decisions are taken in fp32 (row sums in a chunked order): a decision
+ * within about 1e-5 relative of its threshold may go either way.
+ *
+ *   logits          [B][N][V] fp32, device, 16-byte aligned; row i holds the
+ *                   target's next-token scores after node i.
+ *   draft_probs     [B][N][V] fp32, device, 16-byte aligned, or NULL; row c is
+ *                   the distribution node c's token was drawn from (row 0
+ *                   unused).  Only chains (parents[b][i] == i - 1) are taken
+ *                   with it; another tree sets TV_DEV_UNSUPPORTED.
+ *   draft_tokens    [B][N] int32, device (entry 0 unused).
+ *   parents         [B][N] int32, device.
+ *   uniforms        [B][N] fp32, device, in [0, 1) (entry 0 unused).
+ *   exponentials    [B][V] fp32, device, Exp(1) variates, in (0, inf).
+ *   temperature     > 0 and finite.
+ *   accept_len      [B] int32, written: accepted draft tokens.
+ *   accepted_nodes  [B][N] int32, written: the path from the root, -1 padded.
+ *   bonus_token     [B] int32, written.
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE (also a temperature that is not > 0 and
+ * finite), TV_ERR_ALIGN, TV_ERR_WORKSPACE, TV_ERR_LAUNCH.  Device:
+ * TV_DEV_BAD_TREE, TV_DEV_BAD_TOKEN, TV_DEV_UNSUPPORTED (the sequence then
+ * reports accept_len 0, path [0] and a bonus drawn from p_0), TV_DEV_BAD_RANDOM
+ * (results unspecified).
+ */
+TV_API tv_status tv_accept_stochastic(const float* logits, const float* draft_probs,
+                               const int32_t* draft_tokens, const int32_t* parents,
+                               const float* uniforms, const float* exponentials, int32_t B,
+                               int32_t N, int32_t V, float temperature, int32_t* accept_len,
+                               int32_t* accepted_nodes, int32_t* bonus_token, void* workspace,
+                               size_t workspace_bytes, int32_t* dev_status, hipStream_t stream);
 
 /*
  * tv_kv_compact -- move the accepted path's K/V rows into the contiguous

@@ -342,7 +342,7 @@ def race_draw(r, expo):
 
 
 def stochastic_walk(logits, draft_tokens, parents, temperature: float, uniforms, expo,
-                    draft_probs=None):
+                    draft_probs=None, with_residual: bool = False):
     """Stochastic verification of one draft tree.
 
     Source: "P-EAGLE" page, 技术原理和实现方式 steps 3-4 (the target's
@@ -377,6 +377,7 @@ def stochastic_walk(logits, draft_tokens, parents, temperature: float, uniforms,
     bonus token, and the smallest relative margin of any decision taken (an
     acceptance test |u q(x) - r(x)| / max(u q(x), r(x)), or the gap of the
     final draw), which tells how close a run came to a different result.
+    With ``with_residual`` the distribution r of the final draw is appended.
     """
     logits = np.asarray(logits)
     parents = np.asarray(parents)
@@ -409,6 +410,8 @@ def stochastic_walk(logits, draft_tokens, parents, temperature: float, uniforms,
             r = residual(r, q)
         if not moved:
             bonus, gap = race_draw(r, expo)
+            if with_residual:
+                return path, bonus, min(margin, gap), r
             return path, bonus, min(margin, gap)
 
 

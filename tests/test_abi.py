@@ -126,3 +126,23 @@ def test_accept_workspace_grows_with_rows():
     b = lib.tv_accept_greedy_workspace_size(128, 9, 128256)
     assert a > 0 and b > 0
     assert lib.tv_accept_greedy_workspace_size(0, 9, 100) == 0
+
+
+def test_accept_stochastic_host_checks():
+    f = lib.tv_accept_stochastic
+    need = lib.tv_accept_stochastic_workspace_size(2, 8, 1000)
+    assert need > 0 and lib.tv_accept_stochastic_workspace_size(2, 0, 1000) == 0
+
+    def call(**kw):
+        a = dict(lg=P16, qp=None, dt=P16, par=P16, u=P16, e=P16, B=2, N=8, V=1000, T=0.7,
+                 al=P16, an=P16, bt=P16, ws=P16, wsb=need, st=None, s=None)
+        a.update(kw)
+        return f(a["lg"], a["qp"], a["dt"], a["par"], a["u"], a["e"], a["B"], a["N"], a["V"], a["T"],
+                 a["al"], a["an"], a["bt"], a["ws"], a["wsb"], a["st"], a["s"])
+    assert call(lg=None) == 1 and call(u=None) == 1 and call(e=None) == 1 and call(bt=None) == 1
+    assert call(B=0) == 2 and call(N=257) == 2 and call(V=0) == 2
+    assert call(T=0.0) == 2 and call(T=-1.0) == 2 and call(T=float("inf")) == 2
+    assert call(T=float("nan")) == 2
+    assert call(lg=P16 + 4) == 5 and call(qp=P16 + 8) == 5
+    assert call(ws=None) == 6 and call(wsb=need - 1) == 6
+    assert call(ws=P16 + 8) == 5

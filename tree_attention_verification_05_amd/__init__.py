@@ -6,6 +6,8 @@ names as the C ABI in ``include/tv.h``:
 * ``tv_build_tree_mask``  -- ancestor-or-self bitmask of every tree node
 * ``tv_tree_attention``   -- tree-masked attention over the paged prefix
 * ``tv_accept_greedy``    -- target argmax and the longest accepted path
+* ``tv_accept_stochastic`` -- accepted path and bonus token at temperature
+  > 0 (speculative sampling over the tree, random numbers passed in)
 * ``tv_kv_compact``       -- move the accepted path's K/V after the prefix
 * ``tv_tree_kv_write``    -- rotate q and the new keys to their tree
   positions and append the new K/V rows (runs before ``tv_tree_attention``)
@@ -16,14 +18,17 @@ from ._lib import (  # noqa: F401
     BLOCK_SIZE,
     TV_BF16,
     TV_DEV_BAD_CACHE,
+    TV_DEV_BAD_RANDOM,
     TV_DEV_BAD_TOKEN,
     TV_DEV_BAD_TREE,
+    TV_DEV_UNSUPPORTED,
     TV_F32,
     TV_MAX_NODES,
     TVError,
     header_functions,
     lib,
     tv_accept_greedy,
+    tv_accept_stochastic,
     tv_build_tree_mask,
     tv_kv_compact,
     tv_tree_attention,

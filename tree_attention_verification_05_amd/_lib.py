@@ -22,6 +22,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "tv.h")
 TV_OK = 0
 TV_F32, TV_BF16 = 0, 1
 TV_DEV_BAD_TREE, TV_DEV_BAD_CACHE, TV_DEV_BAD_TOKEN = 1, 2, 4
+TV_DEV_BAD_RANDOM, TV_DEV_UNSUPPORTED = 8, 16
 TV_MAX_NODES = 256
 BLOCK_SIZE = 16
 
@@ -55,6 +56,10 @@ def _load() -> ctypes.CDLL:
         "tv_accept_greedy_workspace_size": (_c_size, [_c_i32] * 3),
         "tv_accept_greedy": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_ptr,
                                       _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr, _c_ptr]),
+        "tv_accept_stochastic_workspace_size": (_c_size, [_c_i32] * 3),
+        "tv_accept_stochastic": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32,
+                                          _c_i32, _c_i32, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr,
+                                          _c_ptr, _c_size, _c_ptr, _c_ptr]),
         "tv_kv_compact": (_c_i32, [_c_ptr, _c_ptr, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr, _c_ptr,
                                    _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
                                    _c_ptr]),
@@ -119,12 +124,13 @@ def _tv_dtype(t: torch.Tensor) -> int:
 _accept_ws: Dict[Tuple[int, int], torch.Tensor] = {}
 
 
-def accept_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A workspace for tv_accept_greedy, kept per device and grown when a
-    call needs more (the library needs no initial contents: every key a call
-    reads is written earlier in the same call)."""
+def accept_workspace(device: torch.device, nbytes: int, kind: int = 0) -> torch.Tensor:
+    """A workspace for tv_accept_greedy (kind 0) or tv_accept_stochastic
+    (kind 1), kept per device and kind and grown when a call needs more (the
+    library needs no initial contents: everything a call reads from it is
+    written earlier in the same call)."""
     idx = device.index if device.index is not None else torch.cuda.current_device()
-    key = (idx, 0)
+    key = (idx, kind)
     ws = _accept_ws.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
@@ -232,6 +238,49 @@ def tv_accept_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, parents: 
         _ptr(accepted_nodes), _ptr(bonus_token), _ptr(target_argmax), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(dev_status), _stream(logits)))
     return accept_len, accepted_nodes, bonus_token, target_argmax
+
+
+def tv_accept_stochastic(logits: torch.Tensor, draft_tokens: torch.Tensor, parents: torch.Tensor,
+                         temperature: float, uniforms: torch.Tensor, exponentials: torch.Tensor,
+                         draft_probs: Optional[torch.Tensor] = None,
+                         accept_len: Optional[torch.Tensor] = None,
+                         accepted_nodes: Optional[torch.Tensor] = None,
+                         bonus_token: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         dev_status: Optional[torch.Tensor] = None):
+    """logits fp32 [B, N, V]; draft_tokens, parents int32 [B, N]; uniforms fp32
+    [B, N]; exponentials fp32 [B, V]; draft_probs fp32 [B, N, V] or None
+    (point-mass proposals).  Returns (accept_len [B], accepted_nodes [B, N],
+    bonus_token [B]), all int32."""
+    _dev(logits, "logits", torch.float32)
+    B, N, V = logits.shape
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, N))
+    _dev(parents, "parents", torch.int32, (B, N))
+    _dev(uniforms, "uniforms", torch.float32, (B, N))
+    _dev(exponentials, "exponentials", torch.float32, (B, V))
+    if draft_probs is not None:
+        _dev(draft_probs, "draft_probs", torch.float32, (B, N, V))
+    dev = logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if accepted_nodes is None:
+        accepted_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if bonus_token is None:
+        bonus_token = torch.empty(B, dtype=torch.int32, device=dev)
+    _dev(accept_len, "accept_len", torch.int32, (B,))
+    _dev(accepted_nodes, "accepted_nodes", torch.int32, (B, N))
+    _dev(bonus_token, "bonus_token", torch.int32, (B,))
+    need = int(lib.tv_accept_stochastic_workspace_size(B, N, V))
+    if workspace is None:
+        workspace = accept_workspace(dev, need, kind=1)
+    if dev_status is not None:
+        _dev(dev_status, "dev_status", torch.int32)
+    _check("tv_accept_stochastic", lib.tv_accept_stochastic(
+        _ptr(logits), _ptr(draft_probs), _ptr(draft_tokens), _ptr(parents), _ptr(uniforms),
+        _ptr(exponentials), B, N, V, float(temperature), _ptr(accept_len), _ptr(accepted_nodes),
+        _ptr(bonus_token), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(dev_status), _stream(logits)))
+    return accept_len, accepted_nodes, bonus_token
 
 
 def tv_kv_compact(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,

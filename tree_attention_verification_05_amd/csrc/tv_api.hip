@@ -123,6 +123,43 @@ tv_status tv_accept_greedy(const float* logits, const int32_t* draft_tokens, con
   return launched(launch_accept(a, stream));
 }
 
+size_t tv_accept_stochastic_workspace_size(int32_t B, int32_t N, int32_t V) {
+  if (B <= 0 || N <= 0 || N > TV_MAX_NODES || V <= 0) return 0;
+  return stochastic_workspace_bytes(B, N, V);
+}
+
+tv_status tv_accept_stochastic(const float* logits, const float* draft_probs, const int32_t* draft_tokens,
+                               const int32_t* parents, const float* uniforms, const float* exponentials,
+                               int32_t B, int32_t N, int32_t V, float temperature, int32_t* accept_len,
+                               int32_t* accepted_nodes, int32_t* bonus_token, void* workspace,
+                               size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
+  if (!logits || !draft_tokens || !parents || !uniforms || !exponentials || !accept_len || !accepted_nodes ||
+      !bonus_token)
+    return TV_ERR_NULL;
+  if (B <= 0 || N <= 0 || N > TV_MAX_NODES || V <= 0 || !(temperature > 0.f && temperature < INFINITY))
+    return TV_ERR_SHAPE;
+  if (!aligned16(logits) || (draft_probs && !aligned16(draft_probs))) return TV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < stochastic_workspace_bytes(B, N, V)) return TV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TV_ERR_ALIGN;
+  StochArgs a;
+  a.logits = logits;
+  a.draft_probs = draft_probs;
+  a.draft_tokens = draft_tokens;
+  a.parents = parents;
+  a.uniforms = uniforms;
+  a.exponentials = exponentials;
+  a.B = B;
+  a.N = N;
+  a.V = V;
+  a.temperature = temperature;
+  a.accept_len = accept_len;
+  a.accepted_nodes = accepted_nodes;
+  a.bonus_token = bonus_token;
+  a.workspace = workspace;
+  a.dev_status = dev_status;
+  return launched(launch_accept_stochastic(a, stream));
+}
+
 tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks, const int32_t* block_table,
                         int32_t max_blocks, int32_t block_size, const int32_t* prefix_lens,
                         const int32_t* accepted_nodes, const int32_t* accept_len, int32_t B,

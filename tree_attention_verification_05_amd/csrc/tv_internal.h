@@ -79,6 +79,24 @@ struct AcceptArgs {
 size_t accept_workspace_bytes(int B, int N, int V);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
 
+struct StochArgs {
+  const float* logits;
+  const float* draft_probs;  // NULL: point-mass proposals
+  const int32_t* draft_tokens;
+  const int32_t* parents;
+  const float* uniforms;
+  const float* exponentials;
+  int B, N, V;
+  float temperature;
+  int32_t* accept_len;
+  int32_t* accepted_nodes;
+  int32_t* bonus_token;
+  void* workspace;
+  int32_t* dev_status;
+};
+size_t stochastic_workspace_bytes(int B, int N, int V);
+hipError_t launch_accept_stochastic(const StochArgs& a, hipStream_t stream);
+
 struct CompactArgs {
   void* k_cache;
   void* v_cache;

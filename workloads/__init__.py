@@ -50,6 +50,11 @@ _CHUNK = 1 << 22  # elements per independently seeded chunk of a dense tensor
 # component tags of the random streams
 _C_PREFIX, _C_TREE, _C_MATCH, _C_BLOCKS, _C_Q, _C_K, _C_V, _C_LOGITS, _C_PLANT = range(1, 10)
 _C_KNEW, _C_VNEW = 10, 11
+_C_UNIF, _C_EXPO, _C_QNOISE, _C_QDRAW = 12, 13, 14, 15
+
+# Sampling temperature of the stochastic-verification inputs: the top of the
+# 0.0-0.7 range that the P-EAGLE page's practical notes recommend for speedup.
+SAMPLING_TEMPERATURE = 0.7
 
 # Rotary base of the model family each workload is shaped after: Qwen2
 # 1000000; the Llama-3-shaped layers (8B, the batched 32/8-head layer, the
@@ -415,3 +420,45 @@ def tree_kv_inputs(spec, seed: int = 0):
     k = _to_dtype(_normal(shape, 1.0, seed, spec.tag, _C_KNEW), spec.dtype)
     v = _to_dtype(_normal(shape, 1.0, seed, spec.tag, _C_VNEW), spec.dtype)
     return k, v
+
+
+def stochastic_inputs(spec, seed: int = 0, logits=None, proposals: bool = False):
+    """Random inputs of stochastic verification, each from its own stream.
+
+    Returns a dict with ``uniforms`` [B, N] float32 in [0, 1) (entry c decides
+    node c), ``expo`` [B, V] float32 Exp(1) variates (an exact zero, which
+    float64 draws with probability about 2^-53, is replaced by 2^-53), and
+    ``temperature``.  With ``proposals`` (chain trees only) it also returns
+    ``draft_probs`` [B, N, V] float32 and ``draft_tokens`` [B, N] int32: the
+    drafter stand-in's distribution for node c is a softmax at the sampling
+    temperature of the target row of node c - 1 plus N(0, 1) noise, and node
+    c's token is drawn from it by inverse CDF (row 0 is uniform and unused).
+    ``logits`` [B, N, V] (the workload's target logits) is needed then.
+    """
+    B, N, V = spec.B, spec.N, spec.V
+    u = _rng(seed, spec.tag, _C_UNIF).random((B, N), dtype=np.float32)
+    e = _rng(seed, spec.tag, _C_EXPO).standard_exponential((B, V))
+    e[e == 0] = 2.0 ** -53
+    out = {"uniforms": torch.from_numpy(u), "expo": torch.from_numpy(e.astype(np.float32)),
+           "temperature": SAMPLING_TEMPERATURE}
+    if proposals:
+        if spec.tree[0] != "chain":
+            raise ValueError("proposal distributions are generated for chain trees only")
+        lg = logits.numpy() if isinstance(logits, torch.Tensor) else np.asarray(logits)
+        noise = _normal((B, N, V), 1.0, seed, spec.tag, _C_QNOISE)
+        probs = np.empty((B, N, V), dtype=np.float32)
+        probs[:, 0, :] = np.float32(1.0 / V)
+        draw = _rng(seed, spec.tag, _C_QDRAW).random((B, N))
+        tok = np.zeros((B, N), dtype=np.int32)
+        for b in range(B):
+            z = (lg[b, :N - 1].astype(np.float64) + noise[b, 1:]) / SAMPLING_TEMPERATURE
+            z -= z.max(axis=-1, keepdims=True)
+            q = np.exp(z)
+            q /= q.sum(axis=-1, keepdims=True)
+            probs[b, 1:] = q
+            cdf = np.cumsum(q, axis=-1)
+            for c in range(1, N):
+                tok[b, c] = min(int(np.searchsorted(cdf[c - 1], draw[b, c] * cdf[c - 1, -1], side="right")), V - 1)
+        out["draft_probs"] = torch.from_numpy(probs)
+        out["draft_tokens"] = torch.from_numpy(tok)
+    return out
