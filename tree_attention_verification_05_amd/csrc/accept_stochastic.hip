@@ -20,6 +20,9 @@
 //  3. draw (sequences x chunks workgroups): the best r[v] / E[v] key of one
 //     chunk of the stop node's row;
 //  4. pick (one thread per sequence): the best key -> bonus token.
+// Folding the pick into the draw (the last workgroup of a sequence to
+// arrive picks) needs a device-scope fence per workgroup, an L2 write-back
+// on this chip, which cost far more than the launch it saves.
 #include "tv_internal.h"
 
 namespace tv {
@@ -334,17 +337,47 @@ __global__ __launch_bounds__(kThreads) void stoch_draw_kernel(StochArgs a, float
   const float inv_s = 1.f / s;
   uint64_t best = 0ull;
   bool bad = false;
-  for (int v = lo + tid; v < hi; v += kThreads) {
-    const float p = exp2f(lrow[v] * k2 - m) * inv_s;
-    const float e = erow[v];
+  // one vocabulary entry: r(v) / E(v) as a key
+  auto score = [&](int v, float lg, float e, float q) {
+    const float p = exp2f(lg * k2 - m) * inv_s;
     float rv;
     if (qrow)
-      rv = fmaxf(p - qrow[v], 0.f);
+      rv = fmaxf(p - q, 0.f);
     else
       rv = ((s_bits[(v - lo) >> 5] >> ((v - lo) & 31)) & 1u) ? 0.f : p;
     if (!(e > 0.f && e < INFINITY)) bad = true;
     const uint64_t k = make_key(rv / e, v);
     best = k > best ? k : best;
+  };
+  const bool vec = (V & 3) == 0 && ((reinterpret_cast<uintptr_t>(erow) | reinterpret_cast<uintptr_t>(lrow) |
+                                     reinterpret_cast<uintptr_t>(qrow)) & 15u) == 0;
+  if (vec) {
+    // four 16-byte loads of each row in flight per thread
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4* l4 = reinterpret_cast<const f32x4*>(lrow);
+    const f32x4* e4 = reinterpret_cast<const f32x4*>(erow);
+    const f32x4* q4 = reinterpret_cast<const f32x4*>(qrow);
+    const int lo4 = lo / 4, hi4 = hi / 4;
+    for (int j0 = lo4 + tid; j0 < hi4; j0 += 4 * kThreads) {
+      f32x4 lv[4], ev[4], qv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * kThreads;
+        const bool in = j < hi4;
+        lv[u] = in ? __builtin_nontemporal_load(l4 + j) : f32x4{0.f, 0.f, 0.f, 0.f};
+        ev[u] = in ? __builtin_nontemporal_load(e4 + j) : f32x4{1.f, 1.f, 1.f, 1.f};
+        qv[u] = (in && qrow) ? __builtin_nontemporal_load(q4 + j) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * kThreads;
+        if (j >= hi4) break;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) score(4 * j + e, lv[u][e], ev[u][e], qv[u][e]);
+      }
+    }
+  } else {
+    for (int v = lo + tid; v < hi; v += kThreads) score(v, lrow[v], erow[v], qrow ? qrow[v] : 0.f);
   }
   if (bad) s_bad = 1;
   for (int o = 32; o > 0; o >>= 1) {
@@ -356,8 +389,8 @@ __global__ __launch_bounds__(kThreads) void stoch_draw_kernel(StochArgs a, float
   if (tid == 0) {
     uint64_t k = wbest[0];
     for (int w = 1; w < kWaves; ++w) k = wbest[w] > k ? wbest[w] : k;
-    keys[static_cast<size_t>(b) * chunks + ch] = k;
     if (s_bad) report(a.dev_status, TV_DEV_BAD_RANDOM);
+    keys[static_cast<size_t>(b) * chunks + ch] = k;
   }
 }
 
