@@ -303,6 +303,32 @@ def accept_greedy(logits, draft_tokens, parents):
 
 
 # --------------------------------------------------------------------------
+# target LM head fused with the greedy choice
+# --------------------------------------------------------------------------
+
+def lm_head_logits(hidden, weight) -> np.ndarray:
+    """The target's scores of every vocabulary entry at every tree node:
+    logits[m, v] = sum_h hidden[m, h] * weight[v, h], in float64 (the output
+    projection of the final hidden state onto the vocabulary, no bias, as in
+    the Llama- and Qwen-family targets the pages run).  Source: "P-EAGLE"
+    page, 技术原理和实现方式 step 3 (one target pass scores every proposed
+    token).  hidden [M, H], weight [V, H] -> [M, V]."""
+    h = np.asarray(hidden, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    return h @ w.T
+
+
+def lm_head_argmax(hidden, weight):
+    """Greedy choice and its score per row, without keeping the scores:
+    returns (argmax [M] int64, lowest index among the row's maxima; max [M]
+    float64).  Source: "vLLM EAGLE 投机解码实战", 无损性保障 (greedy
+    verification compares drafts with the target's greedy choice)."""
+    lg = lm_head_logits(hidden, weight)
+    am = target_argmax(lg)
+    return am, lg[np.arange(lg.shape[0]), am]
+
+
+# --------------------------------------------------------------------------
 # stochastic acceptance (temperature > 0)
 # --------------------------------------------------------------------------
 

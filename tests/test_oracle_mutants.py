@@ -9,9 +9,10 @@ instead of tree depth as position, and in stochastic acceptance: siblings
 tested in the wrong order, the acceptance test reversed, the temperature
 dropped, a residual that keeps the rejected mass or is not normalised, the
 final draw multiplying instead of dividing, the proposal probability
-dropped, the target row of the wrong node) and runs the pin suites against
-that copy in a separate process, on the CPU.  The suites must fail for
-every one of them.
+dropped, the target row of the wrong node; and in the fused LM head: a
+dropped hidden column, the score taken from the wrong row) and runs the pin
+suites against that copy in a separate process, on the CPU.  The suites must
+fail for every one of them.
 """
 import os
 import shutil
@@ -63,11 +64,14 @@ MUTANTS = {
     "stochastic_race_multiplies": ("t = np.asarray(r, dtype=np.float64) / np.asarray(expo, dtype=np.float64)",
                                    "t = np.asarray(r, dtype=np.float64) * np.asarray(expo, dtype=np.float64)"),
     "stochastic_acceptance_ignores_proposal": ("lhs = float(uniforms[c]) * q[x]", "lhs = float(uniforms[c])"),
+    "lm_head_drops_last_hidden_column": ("    return h @ w.T", "    return h[:, :-1] @ w[:, :-1].T"),
+    "lm_head_max_from_first_row": ("return am, lg[np.arange(lg.shape[0]), am]", "return am, lg[0, am]"),
     "stochastic_target_row_of_child": ("        r = target_probs(logits[cur], temperature)\n        moved = False",
                                        "        r = target_probs(logits[min(cur + 1, N - 1)], temperature)\n        moved = False"),
 }
 
-PIN_FILES = [os.path.join("tests", "test_oracle.py"), os.path.join("tests", "test_oracle_stochastic.py")]
+PIN_FILES = [os.path.join("tests", "test_oracle.py"), os.path.join("tests", "test_oracle_stochastic.py"),
+             os.path.join("tests", "test_oracle_lmhead.py")]
 COPY = ["pytest.ini", "workloads", os.path.join("tests", "conftest.py"),
         os.path.join("tests", "golden")] + PIN_FILES
 

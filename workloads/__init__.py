@@ -51,6 +51,7 @@ _CHUNK = 1 << 22  # elements per independently seeded chunk of a dense tensor
 _C_PREFIX, _C_TREE, _C_MATCH, _C_BLOCKS, _C_Q, _C_K, _C_V, _C_LOGITS, _C_PLANT = range(1, 10)
 _C_KNEW, _C_VNEW = 10, 11
 _C_UNIF, _C_EXPO, _C_QNOISE, _C_QDRAW = 12, 13, 14, 15
+_C_HID, _C_WLM = 16, 17
 
 # Sampling temperature of the stochastic-verification inputs: the top of the
 # 0.0-0.7 range that the P-EAGLE page's practical notes recommend for speedup.
@@ -65,6 +66,18 @@ def rope_theta(spec) -> float:
     if "tiny" in spec.name:
         return 10000.0
     return 500000.0
+
+
+def hidden_size(spec) -> int:
+    """Width of the final hidden state that the target's LM head projects
+    (Llama-3-8B 4096, Qwen2-7B 3584, Llama-3-70B 8192; 256 for the tiny case)."""
+    if "tiny" in spec.name:
+        return 256
+    if "qwen2" in spec.name:
+        return 3584
+    if "70b" in spec.name or "chain" in spec.name:
+        return 8192
+    return 4096
 
 
 @dataclasses.dataclass(frozen=True)
@@ -462,3 +475,13 @@ def stochastic_inputs(spec, seed: int = 0, logits=None, proposals: bool = False)
         out["draft_probs"] = torch.from_numpy(probs)
         out["draft_tokens"] = torch.from_numpy(tok)
     return out
+
+
+def lm_head_inputs(spec, seed: int = 0):
+    """Final hidden states [B, N, H] and the LM-head weight [V, H], both bf16:
+    hidden N(0, 1), weight N(0, (logit_std / sqrt(H))^2), so that the scores
+    have the workload's logit spread."""
+    H = hidden_size(spec)
+    hid = _to_dtype(_normal((spec.B, spec.N, H), 1.0, seed, spec.tag, _C_HID), "bf16")
+    w = _to_dtype(_normal((spec.V, H), spec.logit_std / float(np.sqrt(H)), seed, spec.tag, _C_WLM), "bf16")
+    return hid, w
