@@ -67,7 +67,7 @@ typedef enum {
   TV_ERR_SHAPE = 2,       /* a size <= 0, Hq % Hkv != 0, N > TV_MAX_NODES, or the
                              block table cannot hold max_prefix_len + N positions */
   TV_ERR_DTYPE = 3,       /* dtype is neither TV_F32 nor TV_BF16 */
-  TV_ERR_UNSUPPORTED = 4, /* D not in {64, 128} or block_size != 16 */
+  TV_ERR_UNSUPPORTED = 4, /* D not in {64, 128}, block_size != 16, or H % 64 != 0 */
   TV_ERR_ALIGN = 5,       /* q, out, cache, logits or workspace pointer not 16-byte aligned */
   TV_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the queried size */
   TV_ERR_LAUNCH = 7       /* the HIP runtime reported an error at launch */
@@ -240,6 +240,42 @@ TV_API tv_status tv_accept_stochastic(const float* logits, const float* draft_pr
                                int32_t N, int32_t V, float temperature, int32_t* accept_len,
                                int32_t* accepted_nodes, int32_t* bonus_token, void* workspace,
                                size_t workspace_bytes, int32_t* dev_status, hipStream_t stream);
+
+/*
+ * Workspace bytes tv_lm_head_argmax needs (one 64-bit key per row and
+ * 256-wide vocabulary tile); 0 for invalid sizes.  No initialisation needed.
+ */
+TV_API size_t tv_lm_head_argmax_workspace_size(int32_t M, int32_t H, int32_t V);
+
+/*
+ * tv_lm_head_argmax -- the target's LM head fused with the greedy choice:
+ * per row, the best-scoring vocabulary entry and its score, without
+ * writing the [M][V] scores.
+ * ("P-EAGLE", 技术原理和实现方式 step 3: one target pass scores every
+ * proposed token; "vLLM EAGLE 投机解码实战", 无损性保障: greedy verification
+ * compares drafts with the target's greedy choice.)
+ *
+ * score[m][v] = sum_h hidden[m][h] * weight[v][h] (bf16 products, fp32
+ * accumulation); argmax[m] = lowest v among the row's maxima (-0.0 and
+ * +0.0 compare equal; NaN rows unspecified).  The scores differ from exact
+ * ones by fp32 rounding, so two entries within that rounding of each other
+ * may swap.  With rows = B * N tree nodes, argmax is the target_argmax a
+ * greedy walk needs.
+ *
+ *   hidden      [M][H] bf16, device, 16-byte aligned: final hidden states.
+ *   weight      [V][H] bf16, device, 16-byte aligned: LM-head rows.
+ *   H           a multiple of 64, at most 2^20.
+ *   argmax      [M] int32, device, written.
+ *   max_score   [M] fp32, device, written (may be NULL).
+ *   workspace   device buffer of tv_lm_head_argmax_workspace_size(M, H, V)
+ *               bytes, 16-byte aligned.
+ * Errors: TV_ERR_NULL, TV_ERR_DTYPE (only TV_BF16), TV_ERR_SHAPE,
+ * TV_ERR_UNSUPPORTED (H % 64 != 0), TV_ERR_ALIGN, TV_ERR_WORKSPACE,
+ * TV_ERR_LAUNCH.
+ */
+TV_API tv_status tv_lm_head_argmax(const void* hidden, const void* weight, int32_t M, int32_t H,
+                            int32_t V, tv_dtype dtype, int32_t* argmax, float* max_score,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * tv_kv_compact -- move the accepted path's K/V rows into the contiguous

@@ -146,3 +146,20 @@ def test_accept_stochastic_host_checks():
     assert call(lg=P16 + 4) == 5 and call(qp=P16 + 8) == 5
     assert call(ws=None) == 6 and call(wsb=need - 1) == 6
     assert call(ws=P16 + 8) == 5
+
+
+def test_lm_head_host_checks():
+    f = lib.tv_lm_head_argmax
+    need = lib.tv_lm_head_argmax_workspace_size(60, 4096, 128256)
+    assert need == 60 * 501 * 8 and lib.tv_lm_head_argmax_workspace_size(0, 64, 10) == 0
+
+    def call(**kw):
+        a = dict(h=P16, w=P16, M=60, H=4096, V=128256, dt=1, am=P16, mx=None, ws=P16, wsb=need, s=None)
+        a.update(kw)
+        return f(a["h"], a["w"], a["M"], a["H"], a["V"], a["dt"], a["am"], a["mx"], a["ws"], a["wsb"], a["s"])
+    assert call(h=None) == 1 and call(w=None) == 1 and call(am=None) == 1
+    assert call(dt=0) == 3
+    assert call(M=0) == 2 and call(V=0) == 2 and call(H=0) == 2 and call(H=1 << 21) == 2
+    assert call(H=4000) == 4
+    assert call(h=P16 + 2) == 5 and call(w=P16 + 8) == 5
+    assert call(ws=None) == 6 and call(wsb=need - 1) == 6

@@ -9,6 +9,8 @@ names as the C ABI in ``include/tv.h``:
 * ``tv_accept_stochastic`` -- accepted path and bonus token at temperature
   > 0 (speculative sampling over the tree, random numbers passed in)
 * ``tv_kv_compact``       -- move the accepted path's K/V after the prefix
+* ``tv_lm_head_argmax``   -- the target's LM head fused with the greedy
+  choice (scores never written)
 * ``tv_tree_kv_write``    -- rotate q and the new keys to their tree
   positions and append the new K/V rows (runs before ``tv_tree_attention``)
 
@@ -31,6 +33,7 @@ from ._lib import (  # noqa: F401
     tv_accept_stochastic,
     tv_build_tree_mask,
     tv_kv_compact,
+    tv_lm_head_argmax,
     tv_tree_attention,
     tv_tree_attention_workspace_size,
     tv_tree_kv_write,

@@ -60,6 +60,9 @@ def _load() -> ctypes.CDLL:
         "tv_accept_stochastic": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32,
                                           _c_i32, _c_i32, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr,
                                           _c_ptr, _c_size, _c_ptr, _c_ptr]),
+        "tv_lm_head_argmax_workspace_size": (_c_size, [_c_i32] * 3),
+        "tv_lm_head_argmax": (_c_i32, [_c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
+                                       _c_ptr, _c_size, _c_ptr]),
         "tv_kv_compact": (_c_i32, [_c_ptr, _c_ptr, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr, _c_ptr,
                                    _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
                                    _c_ptr]),
@@ -125,8 +128,8 @@ _accept_ws: Dict[Tuple[int, int], torch.Tensor] = {}
 
 
 def accept_workspace(device: torch.device, nbytes: int, kind: int = 0) -> torch.Tensor:
-    """A workspace for tv_accept_greedy (kind 0) or tv_accept_stochastic
-    (kind 1), kept per device and kind and grown when a call needs more (the
+    """A workspace for tv_accept_greedy (kind 0), tv_accept_stochastic
+    (kind 1) or tv_lm_head_argmax (kind 2), kept per device and kind and grown when a call needs more (the
     library needs no initial contents: everything a call reads from it is
     written earlier in the same call)."""
     idx = device.index if device.index is not None else torch.cuda.current_device()
@@ -281,6 +284,39 @@ def tv_accept_stochastic(logits: torch.Tensor, draft_tokens: torch.Tensor, paren
         _ptr(bonus_token), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(dev_status), _stream(logits)))
     return accept_len, accepted_nodes, bonus_token
+
+
+def tv_lm_head_argmax(hidden: torch.Tensor, weight: torch.Tensor,
+                      argmax: Optional[torch.Tensor] = None,
+                      max_score: Optional[torch.Tensor] = None, want_max: bool = True,
+                      workspace: Optional[torch.Tensor] = None):
+    """hidden bf16 [..., H] (rows = all leading dims), weight bf16 [V, H].
+    Returns (argmax int32 [...], max_score fp32 [...] or None)."""
+    _dev(hidden, "hidden", torch.bfloat16)
+    _dev(weight, "weight", torch.bfloat16)
+    H = hidden.shape[-1]
+    V = weight.shape[0]
+    if weight.dim() != 2 or weight.shape[1] != H:
+        raise ValueError("weight must be [V, H] with the hidden width of `hidden`")
+    lead = tuple(hidden.shape[:-1])
+    M = 1
+    for d in lead:
+        M *= int(d)
+    dev = hidden.device
+    if argmax is None:
+        argmax = torch.empty(lead, dtype=torch.int32, device=dev)
+    if max_score is None and want_max:
+        max_score = torch.empty(lead, dtype=torch.float32, device=dev)
+    _dev(argmax, "argmax", torch.int32, lead)
+    if max_score is not None:
+        _dev(max_score, "max_score", torch.float32, lead)
+    need = int(lib.tv_lm_head_argmax_workspace_size(M, H, V))
+    if workspace is None:
+        workspace = accept_workspace(dev, need, kind=2)
+    _check("tv_lm_head_argmax", lib.tv_lm_head_argmax(
+        _ptr(hidden), _ptr(weight), M, H, V, TV_BF16, _ptr(argmax), _ptr(max_score), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(hidden)))
+    return argmax, max_score
 
 
 def tv_kv_compact(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,

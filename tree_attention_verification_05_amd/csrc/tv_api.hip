@@ -23,7 +23,7 @@ const char* tv_status_string(tv_status s) {
     case TV_ERR_NULL: return "TV_ERR_NULL: a required pointer is NULL";
     case TV_ERR_SHAPE: return "TV_ERR_SHAPE: sizes are inconsistent or out of range";
     case TV_ERR_DTYPE: return "TV_ERR_DTYPE: dtype must be TV_F32 or TV_BF16";
-    case TV_ERR_UNSUPPORTED: return "TV_ERR_UNSUPPORTED: D must be 64 or 128 and block_size 16";
+    case TV_ERR_UNSUPPORTED: return "TV_ERR_UNSUPPORTED: D must be 64 or 128, block_size 16, and H a multiple of 64";
     case TV_ERR_ALIGN: return "TV_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
     case TV_ERR_WORKSPACE: return "TV_ERR_WORKSPACE: workspace missing or too small";
     case TV_ERR_LAUNCH: return "TV_ERR_LAUNCH: kernel launch failed";
@@ -158,6 +158,34 @@ tv_status tv_accept_stochastic(const float* logits, const float* draft_probs, co
   a.workspace = workspace;
   a.dev_status = dev_status;
   return launched(launch_accept_stochastic(a, stream));
+}
+
+size_t tv_lm_head_argmax_workspace_size(int32_t M, int32_t H, int32_t V) {
+  if (M <= 0 || H <= 0 || V <= 0) return 0;
+  return lm_head_workspace_bytes(M, V);
+}
+
+tv_status tv_lm_head_argmax(const void* hidden, const void* weight, int32_t M, int32_t H, int32_t V,
+                            tv_dtype dtype, int32_t* argmax, float* max_score, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!hidden || !weight || !argmax) return TV_ERR_NULL;
+  if (dtype != TV_BF16) return TV_ERR_DTYPE;
+  // the score kernel addresses one 256-row slab of the weight with 32-bit offsets
+  if (M <= 0 || H <= 0 || V <= 0 || H > 1 << 20) return TV_ERR_SHAPE;
+  if (H % 64 != 0) return TV_ERR_UNSUPPORTED;
+  if (!aligned16(hidden) || !aligned16(weight)) return TV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < lm_head_workspace_bytes(M, V)) return TV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TV_ERR_ALIGN;
+  LmArgs a;
+  a.hidden = hidden;
+  a.weight = weight;
+  a.M = M;
+  a.H = H;
+  a.V = V;
+  a.argmax = argmax;
+  a.max_score = max_score;
+  a.workspace = workspace;
+  return launched(launch_lm_head_argmax(a, stream));
 }
 
 tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks, const int32_t* block_table,

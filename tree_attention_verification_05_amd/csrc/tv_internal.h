@@ -97,6 +97,17 @@ struct StochArgs {
 size_t stochastic_workspace_bytes(int B, int N, int V);
 hipError_t launch_accept_stochastic(const StochArgs& a, hipStream_t stream);
 
+struct LmArgs {
+  const void* hidden;  // [M][H] bf16
+  const void* weight;  // [V][H] bf16
+  int M, H, V;
+  int32_t* argmax;
+  float* max_score;    // may be NULL
+  void* workspace;
+};
+size_t lm_head_workspace_bytes(int M, int V);
+hipError_t launch_lm_head_argmax(const LmArgs& a, hipStream_t stream);
+
 struct CompactArgs {
   void* k_cache;
   void* v_cache;
