@@ -18,10 +18,12 @@ rewrites the tree slots in place; later steps accept the same paths and move
 the same number of rows, so the work per step is unchanged.
 
 The tree K/V write (rotary positions and paged append of the step's new
-rows, the path's upstream neighbour) and stochastic acceptance (temperature
-> 0, the alternative to the greedy call) are timed on their own, K calls
-after an eviction each, and reported under `extra_calls`; they are not part
-of `value`.
+rows, the path's upstream neighbour), stochastic acceptance (temperature
+> 0, the alternative to the greedy call) and the target's LM head fused with
+the greedy choice (bf16 hidden states and weight of the workload's model,
+hidden 4096 / 3584 / 8192) are timed on their own, K calls after an
+eviction each, and reported under `extra_calls`; they are not part of
+`value`.
 """
 from __future__ import annotations
 
@@ -47,6 +49,7 @@ KERNEL_SOURCES = {
     "tv_build_tree_mask": ["tree_mask.hip"],
     "tv_tree_kv_write": ["tree_kv_write.hip"],
     "tv_accept_stochastic": ["accept_stochastic.hip"],
+    "tv_lm_head_argmax": ["lm_head.hip"],
 }
 
 
@@ -262,6 +265,26 @@ def main():
         raise RuntimeError(f"device status {int(status.item())} after the stochastic call")
     s_al_h = s_al.cpu().numpy()
 
+    # ---- the target's LM head fused with the greedy choice (upstream of the
+    # acceptance walk; the [B, N, V] scores are never written) ----
+    lm_hid, lm_w = W.lm_head_inputs(spec, args.seed)
+    lm_hid = lm_hid.reshape(-1, lm_hid.shape[-1]).to(dev)
+    lm_w = lm_w.to(dev)
+    lm_am = torch.empty(lm_hid.shape[0], dtype=torch.int32, device=dev)
+    lm_mx = torch.empty(lm_hid.shape[0], dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        T.tv_lm_head_argmax(lm_hid, lm_w, argmax=lm_am, max_score=lm_mx)
+    lm_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        evict()
+        lm_ev[s][0].record(stream)
+        T.tv_lm_head_argmax(lm_hid, lm_w, argmax=lm_am, max_score=lm_mx)
+        lm_ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    lm_ms = np.array([e[0].elapsed_time(e[1]) for e in lm_ev])
+    lm_M, lm_H = lm_hid.shape
+    del lm_hid, lm_w
+
     # back-to-back steps with warm caches, for reference
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -314,6 +337,22 @@ def main():
         "bytes": int(st_bytes), "GB_s": round(st_bytes / (st_us * 1e-6) / 1e9, 1),
         "temperature": sx["temperature"], "proposals": "rows" if chain else "point mass",
         "mean_accept_len": float(s_al_h.mean()), "in_step": False}
+
+    # fused LM head: weight and hidden states read once, per-tile keys
+    # written and read back; 2 M H V flops, MFMA-bound above the ridge
+    lm_us = float(lm_ms.mean()) * 1e3
+    lm_tiles = (V + 255) // 256
+    lm_bytes = V * lm_H * 2 + lm_M * lm_H * 2 + 2 * lm_M * lm_tiles * 8 + lm_M * 8
+    lm_flops = 2.0 * lm_M * lm_H * V
+    extra["tv_lm_head_argmax"] = {
+        "us": round(lm_us, 3), "us_median": round(float(np.median(lm_ms)) * 1e3, 3),
+        "bytes": int(lm_bytes), "GB_s": round(lm_bytes / (lm_us * 1e-6) / 1e9, 1),
+        "flops": int(lm_flops), "TFLOP_s": round(lm_flops / (lm_us * 1e-6) / 1e12, 2),
+        "rows": int(lm_M), "hidden": int(lm_H),
+        "bound": "mfma" if lm_flops / lm_bytes > RIDGE_FLOP_PER_BYTE else "hbm", "in_step": False}
+    lm_rec = extra["tv_lm_head_argmax"]
+    lm_rec["frac"] = round(lm_rec["TFLOP_s"] / BF16_PEAK_TFLOPS if lm_rec["bound"] == "mfma"
+                           else lm_rec["GB_s"] / HBM_PEAK_GBS, 4)
 
     # roofline of the dominant call
     dom = max(names, key=lambda n: kern[n]["us"])
