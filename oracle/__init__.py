@@ -471,6 +471,81 @@ def accept_stochastic(logits, draft_tokens, parents, temperature: float, uniform
 
 
 # --------------------------------------------------------------------------
+# draft-tree construction (EAGLE-2 style expansion and pruning)
+# --------------------------------------------------------------------------
+
+def log_softmax(row) -> np.ndarray:
+    """log softmax of one score row, float64."""
+    z = np.asarray(row, dtype=np.float64)
+    m = z.max()
+    return z - m - np.log(np.exp(z - m).sum())
+
+
+def top_tokens(logp, k: int) -> np.ndarray:
+    """The k most probable tokens of a row, most probable first, the lower
+    index first among equals."""
+    return np.argsort(-np.asarray(logp), kind="stable")[:k]
+
+
+def build_draft_tree(draft_logits, N: int, topk: int, root_token: int = 0,
+                     return_generated: bool = False):
+    """Draft tree of N nodes grown level by level from the drafter's scores.
+
+    Source: "EAGLE代码实现原理" page, 树结构缓冲 (branch prediction: likely
+    continuations are proposed ahead; level pruning: high-probability paths
+    are kept and low-probability branches cut); "vLLM-TreeEagle" README,
+    核心组件 item 3 (multi-level candidate generation with path pruning).
+
+    draft_logits [depth, topk, V]: row (l, j) is the drafter's next-token
+    scores at the j-th kept node of level l (level 0 keeps the root alone,
+    row (0, 0)).  A node's score is the sum of the log-probabilities
+    (log softmax of its row) of the tokens on its path; the root's is 0.
+    Level l: each kept node proposes its topk most probable tokens (the
+    candidates, in order (j, rank)); the topk best candidates (score, then
+    candidate order) are kept for level l + 1.  All candidates of all levels
+    are the generated nodes; the tree is the root plus the N - 1 best of
+    them (score, then level, then candidate order), which is ancestor-closed
+    since a child never scores above its parent.  Nodes are numbered by
+    (level, rank in that order), so parents come first.
+
+    Returns (parents [N], tokens [N], scores [N]) and, with
+    ``return_generated``, the generated nodes as (score, level, j, rank,
+    token, parent generated index or -1 for the root).
+    """
+    lg = np.asarray(draft_logits)
+    depth, K, V = lg.shape
+    assert K == topk and 1 <= N
+    gen = []                                  # generated nodes
+    frontier = [(0.0, -1)]                    # (score, generated index); -1 = root
+    for lev in range(depth):
+        cands = []
+        for j, (fs, fid) in enumerate(frontier):
+            lp = log_softmax(lg[lev, j])
+            for r, t in enumerate(top_tokens(lp, topk)):
+                cands.append((fs + lp[t], lev, j, r, int(t), fid))
+        first = len(gen)
+        gen.extend(cands)
+        order = sorted(range(len(cands)), key=lambda i: (-cands[i][0], i))
+        frontier = [(cands[i][0], first + i) for i in order[:topk]]
+    assert N - 1 <= len(gen), "not enough generated nodes"
+    keep = sorted(range(len(gen)), key=lambda g: (-gen[g][0], gen[g][1], gen[g][2], gen[g][3]))[:N - 1]
+    keep = sorted(keep, key=lambda g: (gen[g][1], -gen[g][0], gen[g][2], gen[g][3]))
+    label = {g: i + 1 for i, g in enumerate(keep)}
+    parents = np.full(N, -1, dtype=np.int64)
+    tokens = np.zeros(N, dtype=np.int64)
+    scores = np.zeros(N)
+    tokens[0] = root_token
+    for g, i in label.items():
+        pg = gen[g][5]
+        parents[i] = 0 if pg < 0 else label[pg]   # KeyError would mean not ancestor-closed
+        tokens[i] = gen[g][4]
+        scores[i] = gen[g][0]
+    if return_generated:
+        return parents, tokens, scores, gen
+    return parents, tokens, scores
+
+
+# --------------------------------------------------------------------------
 # tree K/V write with rotary positions
 # --------------------------------------------------------------------------
 

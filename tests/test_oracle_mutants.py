@@ -10,8 +10,11 @@ tested in the wrong order, the acceptance test reversed, the temperature
 dropped, a residual that keeps the rejected mass or is not normalised, the
 final draw multiplying instead of dividing, the proposal probability
 dropped, the target row of the wrong node; and in the fused LM head: a
-dropped hidden column, the score taken from the wrong row) and runs the pin
-suites against that copy in a separate process, on the CPU.  The suites must
+dropped hidden column, the score taken from the wrong row; and in draft-tree
+construction: the kept nodes taken in candidate order, probabilities added
+instead of log-probabilities, nodes numbered by score alone, one drafter row
+for every kept node) and runs the pin suites against that copy in a
+separate process, on the CPU.  The suites must
 fail for every one of them.
 """
 import os
@@ -66,12 +69,19 @@ MUTANTS = {
     "stochastic_acceptance_ignores_proposal": ("lhs = float(uniforms[c]) * q[x]", "lhs = float(uniforms[c])"),
     "lm_head_drops_last_hidden_column": ("    return h @ w.T", "    return h[:, :-1] @ w[:, :-1].T"),
     "lm_head_max_from_first_row": ("return am, lg[np.arange(lg.shape[0]), am]", "return am, lg[0, am]"),
+    "draft_tree_frontier_in_candidate_order": ("        order = sorted(range(len(cands)), key=lambda i: (-cands[i][0], i))",
+                                               "        order = list(range(len(cands)))"),
+    "draft_tree_adds_probabilities": ("cands.append((fs + lp[t], lev, j, r, int(t), fid))",
+                                      "cands.append((fs + np.exp(lp[t]), lev, j, r, int(t), fid))"),
+    "draft_tree_numbered_by_score_only": ("keep = sorted(keep, key=lambda g: (gen[g][1], -gen[g][0], gen[g][2], gen[g][3]))",
+                                          "keep = sorted(keep, key=lambda g: (-gen[g][0], gen[g][2], gen[g][3]))"),
+    "draft_tree_first_row_for_every_slot": ("            lp = log_softmax(lg[lev, j])", "            lp = log_softmax(lg[lev, 0])"),
     "stochastic_target_row_of_child": ("        r = target_probs(logits[cur], temperature)\n        moved = False",
                                        "        r = target_probs(logits[min(cur + 1, N - 1)], temperature)\n        moved = False"),
 }
 
 PIN_FILES = [os.path.join("tests", "test_oracle.py"), os.path.join("tests", "test_oracle_stochastic.py"),
-             os.path.join("tests", "test_oracle_lmhead.py")]
+             os.path.join("tests", "test_oracle_lmhead.py"), os.path.join("tests", "test_oracle_tree.py")]
 COPY = ["pytest.ini", "workloads", os.path.join("tests", "conftest.py"),
         os.path.join("tests", "golden")] + PIN_FILES
 
