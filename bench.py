@@ -21,9 +21,10 @@ The tree K/V write (rotary positions and paged append of the step's new
 rows, the path's upstream neighbour), stochastic acceptance (temperature
 > 0, the alternative to the greedy call) and the target's LM head fused with
 the greedy choice (bf16 hidden states and weight of the workload's model,
-hidden 4096 / 3584 / 8192) are timed on their own, K calls after an
-eviction each, and reported under `extra_calls`; they are not part of
-`value`.
+hidden 4096 / 3584 / 8192) and the draft-tree construction that produces
+the step's parents and tokens (the drafter's scores of every level, fp32)
+are timed on their own, K calls after an eviction each, and reported under
+`extra_calls`; they are not part of `value`.
 """
 from __future__ import annotations
 
@@ -50,6 +51,7 @@ KERNEL_SOURCES = {
     "tv_tree_kv_write": ["tree_kv_write.hip"],
     "tv_accept_stochastic": ["accept_stochastic.hip"],
     "tv_lm_head_argmax": ["lm_head.hip"],
+    "tv_build_draft_tree": ["draft_tree.hip"],
 }
 
 
@@ -285,6 +287,32 @@ def main():
     lm_M, lm_H = lm_hid.shape
     del lm_hid, lm_w
 
+    # ---- draft-tree construction (the producer of the step's parents and
+    # tokens): the drafter's score rows of every level read once ----
+    dx = W.draft_tree_inputs(spec, args.seed)
+    d_lg = dx["draft_logits"].to(dev)
+    d_root = dx["root_tokens"].to(dev)
+    d_par = torch.empty((B, N), dtype=torch.int32, device=dev)
+    d_tok = torch.empty((B, N), dtype=torch.int32, device=dev)
+    d_sc = torch.empty((B, N), dtype=torch.float32, device=dev)
+    d_ws = torch.empty(max(int(T.lib.tv_build_draft_tree_workspace_size(B, dx["depth"], dx["topk"], V)), 16),
+                       dtype=torch.uint8, device=dev)
+
+    def run_draft_tree():
+        T.tv_build_draft_tree(d_lg, N, root_tokens=d_root, parents=d_par, tokens=d_tok, scores=d_sc,
+                              workspace=d_ws)
+    for _ in range(args.warmup):
+        run_draft_tree()
+    dt_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        evict()
+        dt_ev[s][0].record(stream)
+        run_draft_tree()
+        dt_ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    dt_ms = np.array([e[0].elapsed_time(e[1]) for e in dt_ev])
+    del d_lg
+
     # back-to-back steps with warm caches, for reference
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -353,6 +381,19 @@ def main():
     lm_rec = extra["tv_lm_head_argmax"]
     lm_rec["frac"] = round(lm_rec["TFLOP_s"] / BF16_PEAK_TFLOPS if lm_rec["bound"] == "mfma"
                            else lm_rec["GB_s"] / HBM_PEAK_GBS, 4)
+
+    # draft-tree construction: each used score row read once (the root's
+    # row and topk rows per later level), the per-chunk statistics and keys
+    # written and read back, the tree written
+    dt_us = float(dt_ms.mean()) * 1e3
+    dt_rows = B * (1 + (dx["depth"] - 1) * dx["topk"])
+    dt_chunks = dt_rows * ((V + 8191) // 8192)
+    dt_bytes = dt_rows * V * 4 + 2 * dt_chunks * (8 + 8 * dx["topk"]) + B * 4 + 3 * B * N * 4
+    extra["tv_build_draft_tree"] = {
+        "us": round(dt_us, 3), "us_median": round(float(np.median(dt_ms)) * 1e3, 3),
+        "bytes": int(dt_bytes), "GB_s": round(dt_bytes / (dt_us * 1e-6) / 1e9, 1),
+        "frac": round(dt_bytes / (dt_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bound": "hbm",
+        "depth": dx["depth"], "topk": dx["topk"], "rows": int(dt_rows), "in_step": False}
 
     # roofline of the dominant call
     dom = max(names, key=lambda n: kern[n]["us"])

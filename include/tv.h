@@ -345,6 +345,64 @@ TV_API tv_status tv_tree_kv_write(const void* q, const void* k_new, const void* 
                            int32_t D, float rope_theta, tv_dtype dtype, int32_t* dev_status,
                            hipStream_t stream);
 
+/* limits of tv_build_draft_tree */
+#define TV_DRAFT_MAX_DEPTH 16
+#define TV_DRAFT_MAX_TOPK 16
+#define TV_DRAFT_MAX_VOCAB 262144
+
+/*
+ * Workspace bytes tv_build_draft_tree needs (per row chunk: its maximum, its
+ * sum of exponentials and its topk best entries); 0 for invalid sizes.  No
+ * initialisation needed; calls that share one must be ordered.
+ */
+TV_API size_t tv_build_draft_tree_workspace_size(int32_t B, int32_t depth, int32_t topk, int32_t V);
+
+/*
+ * tv_build_draft_tree -- the draft token tree of N nodes, grown level by
+ * level from the drafter's scores: top-k expansion and a global rerank by
+ * cumulative log-probability.
+ * ("EAGLE代码实现原理", 树结构缓冲: branch prediction proposes likely
+ * continuations ahead, level pruning keeps the high-probability paths and
+ * cuts the low-probability branches; "vLLM-TreeEagle" README, 核心组件
+ * item 3: multi-level candidate generation with path pruning.)
+ *
+ * A node's score is the sum of the log-probabilities (log softmax of the
+ * row it was proposed from) of the tokens on its path; the root's is 0.
+ * Level 0: the root proposes the topk most probable tokens of row (0, 0).
+ * Level l >= 1: the j-th best candidate of level l - 1 (by score, then
+ * generation order) proposes the topk most probable tokens of row (l, j),
+ * giving candidates in order (j, rank); within a row, more probable first
+ * and the lower token id among equals.  Every candidate of every level is a
+ * generated node; the tree is the root plus the N - 1 best generated nodes
+ * (score, then level, then generation order), which is ancestor-closed.
+ * Nodes are numbered level by level and by that order within a level, so
+ * parents[b][i] < i and the output feeds tv_build_tree_mask directly.
+ * Scores are computed in fp32 (row log-sum-exp in a chunked order): two
+ * candidates whose scores lie within about 1e-5 of each other may swap.
+ *
+ *   draft_logits  [B][depth][topk][V] fp32, device, 16-byte aligned, finite:
+ *                 row (l, j) holds the drafter's next-token scores at the
+ *                 j-th best node of level l - 1 (row (0, 0): at the root;
+ *                 rows (0, j >= 1) are not read).
+ *   depth         1 .. TV_DRAFT_MAX_DEPTH levels of expansion.
+ *   topk          1 .. TV_DRAFT_MAX_TOPK, at most V.
+ *   V             at most TV_DRAFT_MAX_VOCAB.
+ *   N             1 .. TV_MAX_NODES, with N - 1 <= topk + (depth - 1) * topk^2
+ *                 (the number of generated nodes).
+ *   root_tokens   [B] int32, device, or NULL (then 0): token of node 0.
+ *   parents       [B][N] int32, device, written: parents[b][0] = -1.
+ *   tokens        [B][N] int32, device, written: draft token of each node.
+ *   scores        [B][N] fp32, device, written (may be NULL): node scores.
+ *   workspace     device buffer of tv_build_draft_tree_workspace_size(B,
+ *                 depth, topk, V) bytes, 16-byte aligned.
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_ALIGN, TV_ERR_WORKSPACE,
+ * TV_ERR_LAUNCH.
+ */
+TV_API tv_status tv_build_draft_tree(const float* draft_logits, int32_t B, int32_t depth, int32_t topk,
+                              int32_t V, int32_t N, const int32_t* root_tokens, int32_t* parents,
+                              int32_t* tokens, float* scores, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,9 @@ names as the C ABI in ``include/tv.h``:
   choice (scores never written)
 * ``tv_tree_kv_write``    -- rotate q and the new keys to their tree
   positions and append the new K/V rows (runs before ``tv_tree_attention``)
+* ``tv_build_draft_tree`` -- grow the draft tree level by level from the
+  drafter's scores (top-k expansion, global rerank by cumulative
+  log-probability); its parents and tokens feed the calls above
 
 Importing the package loads libtv.so and raises if it has not been built.
 """
@@ -31,6 +34,7 @@ from ._lib import (  # noqa: F401
     lib,
     tv_accept_greedy,
     tv_accept_stochastic,
+    tv_build_draft_tree,
     tv_build_tree_mask,
     tv_kv_compact,
     tv_lm_head_argmax,

@@ -63,6 +63,9 @@ def _load() -> ctypes.CDLL:
         "tv_lm_head_argmax_workspace_size": (_c_size, [_c_i32] * 3),
         "tv_lm_head_argmax": (_c_i32, [_c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
                                        _c_ptr, _c_size, _c_ptr]),
+        "tv_build_draft_tree_workspace_size": (_c_size, [_c_i32] * 4),
+        "tv_build_draft_tree": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
+                                         _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
         "tv_kv_compact": (_c_i32, [_c_ptr, _c_ptr, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr, _c_ptr,
                                    _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
                                    _c_ptr]),
@@ -129,7 +132,8 @@ _accept_ws: Dict[Tuple[int, int], torch.Tensor] = {}
 
 def accept_workspace(device: torch.device, nbytes: int, kind: int = 0) -> torch.Tensor:
     """A workspace for tv_accept_greedy (kind 0), tv_accept_stochastic
-    (kind 1) or tv_lm_head_argmax (kind 2), kept per device and kind and grown when a call needs more (the
+    (kind 1), tv_lm_head_argmax (kind 2) or tv_build_draft_tree (kind 3),
+    kept per device and kind and grown when a call needs more (the
     library needs no initial contents: everything a call reads from it is
     written earlier in the same call)."""
     idx = device.index if device.index is not None else torch.cuda.current_device()
@@ -317,6 +321,42 @@ def tv_lm_head_argmax(hidden: torch.Tensor, weight: torch.Tensor,
         _ptr(hidden), _ptr(weight), M, H, V, TV_BF16, _ptr(argmax), _ptr(max_score), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(hidden)))
     return argmax, max_score
+
+
+def tv_build_draft_tree(draft_logits: torch.Tensor, N: int,
+                        root_tokens: Optional[torch.Tensor] = None,
+                        parents: Optional[torch.Tensor] = None,
+                        tokens: Optional[torch.Tensor] = None,
+                        scores: Optional[torch.Tensor] = None, want_scores: bool = True,
+                        workspace: Optional[torch.Tensor] = None):
+    """draft_logits fp32 [B, depth, topk, V] (row (l, j): the drafter's scores
+    at the j-th best node of level l - 1; row (0, 0) at the root).
+    Returns (parents int32 [B, N], tokens int32 [B, N], scores fp32 [B, N] or None)."""
+    _dev(draft_logits, "draft_logits", torch.float32)
+    if draft_logits.dim() != 4:
+        raise ValueError("draft_logits must be [B, depth, topk, V]")
+    B, depth, topk, V = (int(x) for x in draft_logits.shape)
+    dev = draft_logits.device
+    if root_tokens is not None:
+        _dev(root_tokens, "root_tokens", torch.int32, (B,))
+    if parents is None:
+        parents = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if scores is None and want_scores:
+        scores = torch.empty((B, N), dtype=torch.float32, device=dev)
+    _dev(parents, "parents", torch.int32, (B, N))
+    _dev(tokens, "tokens", torch.int32, (B, N))
+    if scores is not None:
+        _dev(scores, "scores", torch.float32, (B, N))
+    need = int(lib.tv_build_draft_tree_workspace_size(B, depth, topk, V))
+    if workspace is None:
+        workspace = accept_workspace(dev, need, kind=3)
+    _check("tv_build_draft_tree", lib.tv_build_draft_tree(
+        _ptr(draft_logits), B, depth, topk, V, N, _ptr(root_tokens), _ptr(parents), _ptr(tokens),
+        _ptr(scores), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(draft_logits)))
+    return parents, tokens, scores
 
 
 def tv_kv_compact(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,

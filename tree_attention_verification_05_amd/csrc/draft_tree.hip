@@ -1,0 +1,451 @@
+// Draft-tree construction from the drafter's scores: top-k expansion level by
+// level and a global rerank by cumulative log-probability.
+// ("EAGLE代码实现原理", 树结构缓冲: branch prediction proposes likely
+// continuations ahead and level pruning keeps the high-probability paths;
+// "vLLM-TreeEagle" README, 核心组件 item 3: multi-level candidate generation
+// with path pruning.)
+//
+// Chunk kernel (rows x chunks workgroups of 256 threads): one 8192-entry chunk
+// of one score row is held in registers after one pass of 16-byte loads.  It
+// yields the chunk's maximum, its sum of exp(x - max), and its topk best
+// entries as 64-bit keys (value, then lower index).  The topk selection cuts
+// first: T = the topk-th largest of the 32 maxima of 8-lane groups bounds the
+// chunk's topk-th entry from below, and only entries at or above T (at most
+// the 256 of each of topk groups, usually a few more than topk) are ranked.
+// If more than kCandCap pass the cut, topk block-wide max rounds take over.
+//
+// Row kernel (one wave per row): merges the chunks of each row into its
+// log-sum-exp and its topk best keys (the same cut-then-rank selection over
+// the chunk lists), all rows of all sequences at once.
+//
+// Build kernel (one 1024-thread workgroup per sequence): walks the levels:
+// candidate (j, r) of level l scores F_j + x - lse, where F_j is the score of
+// the j-th best node of level l - 1; every level's candidates are ranked in
+// full.  The kept nodes of a level are a prefix of its ranked list (the
+// global order restricted to one level is that level's order), so the global
+// top N - 1 is found by counting, per candidate, the better candidates of
+// every other level with a binary search, and node labels follow as level
+// offsets plus ranks.
+#include "tv_internal.h"
+
+namespace tv {
+namespace {
+
+constexpr int kChunkThreads = 256;
+constexpr int kPer4 = 8;                                // 16-byte loads per thread
+constexpr int kChunk = kChunkThreads * kPer4 * 4;       // 8192 entries per chunk
+constexpr int kGroups = kChunkThreads / 8;              // 8-lane groups per chunk workgroup
+constexpr int kCandCap = 512;                           // ranked candidates per chunk
+constexpr int kRowWaves = 4;                            // rows per row-merge workgroup
+constexpr int kBuildThreads = 1024;
+constexpr int kMaxK = TV_DRAFT_MAX_TOPK;
+constexpr int kMaxCand = kMaxK * kMaxK;                 // candidates of one level
+constexpr int kMaxRows = 1 + (TV_DRAFT_MAX_DEPTH - 1) * kMaxK;
+constexpr int kMaxChunks = (TV_DRAFT_MAX_VOCAB + kChunk - 1) / kChunk;
+static_assert(kMaxChunks <= 64, "one lane per chunk in the row merge");
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Orders floats as unsigned integers; -0.0 and +0.0 map to the same value.
+__device__ __forceinline__ uint32_t ordered(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unordered(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+// Larger key = larger value, then lower index.  Every key of a real entry is
+// nonzero; 0 marks "none".
+__device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
+  return (static_cast<uint64_t>(ordered(v)) << 32) | static_cast<uint32_t>(~idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) {
+  return ~static_cast<uint32_t>(k & 0xFFFFFFFFu);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  return unordered(static_cast<uint32_t>(k >> 32));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = max_u64(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(v & 0xFFFFFFFFu), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Row r of a sequence: r = 0 is the root's row (level 0, slot 0); r >= 1 is
+// level 1 + (r - 1) / topk, slot (r - 1) % topk.
+__device__ __forceinline__ int row_level(int r, int topk) { return r == 0 ? 0 : 1 + (r - 1) / topk; }
+__device__ __forceinline__ int row_slot(int r, int topk) { return r == 0 ? 0 : (r - 1) % topk; }
+
+template <bool kVec>
+__global__ __launch_bounds__(kChunkThreads) void dtree_chunk_kernel(
+    const float* __restrict__ logits, int depth, int topk, int V, int R, int C,
+    float2* __restrict__ stats, uint64_t* __restrict__ keys) {
+  __shared__ float s_m[kChunkThreads / 64], s_s[kChunkThreads / 64];
+  __shared__ uint64_t s_grp[kGroups];
+  __shared__ uint64_t s_cand[kCandCap];
+  __shared__ uint64_t s_wk[kChunkThreads / 64];
+  __shared__ uint64_t s_T;
+  __shared__ int s_n;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long sr = blockIdx.x / C;  // (sequence, row) index
+  const int c = static_cast<int>(blockIdx.x - sr * C);
+  const long b = sr / R;
+  const int r = static_cast<int>(sr - b * R);
+  const float* row = logits + ((b * depth + row_level(r, topk)) * topk + row_slot(r, topk)) * static_cast<long>(V);
+  const int lo = c * kChunk, hi = min(V, lo + kChunk);
+  // entry x[4u + e] of this thread is lo + 4 (u * 256 + tid) + e: indices
+  // increase with (u, e)
+  float x[4 * kPer4];
+  if (kVec) {
+    const f32x4* r4 = reinterpret_cast<const f32x4*>(row + lo);
+    const int n4 = (hi - lo) >> 2;
+#pragma unroll
+    for (int u = 0; u < kPer4; ++u) {
+      const int q = u * kChunkThreads + tid;
+      const f32x4 v = q < n4 ? __builtin_nontemporal_load(r4 + q)
+                             : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * u + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPer4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = lo + 4 * (u * kChunkThreads + tid) + e;
+        x[4 * u + e] = idx < hi ? row[idx] : -INFINITY;
+      }
+  }
+  if (tid == 0) {
+    s_n = 0;
+    s_T = 0ull;
+  }
+
+  // chunk maximum and sum of exp(x - max); entries past the row end are -inf
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4 * kPer4; ++i) m = fmaxf(m, x[i]);
+  m = wave_max(m);
+  if (lane == 0) s_m[wave] = m;
+  // this thread's best entry (strict '>' keeps the lowest index of equals)
+  float bv = -INFINITY;
+  int bi = -1;
+#pragma unroll
+  for (int u = 0; u < kPer4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = lo + 4 * (u * kChunkThreads + tid) + e;
+      if (idx < hi && (bi < 0 || x[4 * u + e] > bv)) {
+        bv = x[4 * u + e];
+        bi = idx;
+      }
+    }
+  uint64_t gk = bi < 0 ? 0ull : make_key(bv, static_cast<uint32_t>(bi));
+  gk = max_u64(gk, __shfl_xor(gk, 1, 64));
+  gk = max_u64(gk, __shfl_xor(gk, 2, 64));
+  gk = max_u64(gk, __shfl_xor(gk, 4, 64));
+  if ((tid & 7) == 0) s_grp[tid >> 3] = gk;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4 * kPer4; ++i) s += __expf(x[i] - m);
+  s = wave_sum(s);
+  if (lane == 0) s_s[wave] = s;
+  // cut: the topk-th largest group maximum (0 when fewer than topk groups
+  // hold an entry: then every entry passes)
+  if (tid < kGroups) {
+    const uint64_t mine = s_grp[tid];
+    int rank = 0;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) rank += s_grp[g] > mine;
+    if (mine != 0ull && rank == topk - 1) s_T = mine;
+  }
+  __syncthreads();
+  const uint64_t T = s_T;
+  const float tval = T == 0ull ? -INFINITY : key_value(T);
+#pragma unroll
+  for (int u = 0; u < kPer4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = lo + 4 * (u * kChunkThreads + tid) + e;
+      if (idx < hi && x[4 * u + e] >= tval) {
+        const uint64_t k = make_key(x[4 * u + e], static_cast<uint32_t>(idx));
+        if (k >= T) {
+          const int pos = atomicAdd(&s_n, 1);
+          if (pos < kCandCap) s_cand[pos] = k;
+        }
+      }
+    }
+  __syncthreads();
+  const int n = s_n;
+  uint64_t* out = keys + (sr * C + c) * topk;
+  if (n <= kCandCap) {
+    for (int p = tid; p < n; p += kChunkThreads) {
+      const uint64_t k = s_cand[p];
+      int rank = 0, q = 0;
+      for (; q + 4 <= n; q += 4)
+        rank += (s_cand[q] > k) + (s_cand[q + 1] > k) + (s_cand[q + 2] > k) + (s_cand[q + 3] > k);
+      for (; q < n; ++q) rank += s_cand[q] > k;
+      if (rank < topk) out[rank] = k;
+    }
+    for (int q = n + tid; q < topk; q += kChunkThreads) out[q] = 0ull;
+  } else {
+    // many entries at or above the cut: topk rounds of "largest key below
+    // the previous one" over the whole chunk
+    uint64_t prev = ~0ull;
+    for (int q = 0; q < topk; ++q) {
+      uint64_t best = 0ull;
+#pragma unroll
+      for (int u = 0; u < kPer4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = lo + 4 * (u * kChunkThreads + tid) + e;
+          if (idx < hi) {
+            const uint64_t k = make_key(x[4 * u + e], static_cast<uint32_t>(idx));
+            if (k < prev && k > best) best = k;
+          }
+        }
+      best = wave_max_u64(best);
+      if (lane == 0) s_wk[wave] = best;
+      __syncthreads();
+      best = max_u64(max_u64(s_wk[0], s_wk[1]), max_u64(s_wk[2], s_wk[3]));
+      if (tid == 0) out[q] = best;
+      prev = best;
+      __syncthreads();
+    }
+  }
+  if (tid == 0) {
+    const float ss = s_s[0] + s_s[1] + s_s[2] + s_s[3];
+    stats[sr * C + c] = make_float2(m, ss);
+  }
+}
+
+// Number of entries of a descending list of distinct keys that exceed k.
+__device__ __forceinline__ int count_above(const uint64_t* list, int n, uint64_t k) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] > k) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Row merge (one wave per row, one lane per chunk): the row's log-sum-exp
+// and its topk best keys, by the same cut-then-rank selection over the chunk
+// lists (descending): T = the topk-th largest chunk maximum (0 with fewer
+// than topk chunks); only lists whose maximum is at or above T hold keys at or
+// above T, so at most topk^2 keys are ranked.
+__global__ __launch_bounds__(64 * kRowWaves) void dtree_row_kernel(
+    const float2* __restrict__ stats, const uint64_t* __restrict__ keys, int topk, int C, long rows,
+    uint64_t* __restrict__ row_top, float* __restrict__ row_lse) {
+  __shared__ uint64_t s_scr[kRowWaves][kMaxCand];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long r = static_cast<long>(blockIdx.x) * kRowWaves + wave;
+  const bool active = r < rows;
+  uint64_t* scratch = s_scr[wave];
+  int n = 0;
+  if (active) {
+    const long rc = r * C;
+    const bool has = lane < C;
+    uint64_t kk[kMaxK];
+#pragma unroll
+    for (int q = 0; q < kMaxK; ++q) kk[q] = (has && q < topk) ? keys[(rc + lane) * topk + q] : 0ull;
+    const float2 st = has ? stats[rc + lane] : make_float2(-INFINITY, 0.f);
+    const float M = wave_max(st.x);
+    const float S = wave_sum(has ? st.y * __expf(st.x - M) : 0.f);
+    const uint64_t head = kk[0];
+    int rank = 0;
+    for (int q = 0; q < C; ++q) rank += readlane_u64(head, q) > head;
+    const unsigned long long hit = __ballot(has && rank == topk - 1);
+    const uint64_t T = hit ? readlane_u64(head, __ffsll(static_cast<long long>(hit)) - 1) : 0ull;
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxK; ++q) cnt += (kk[q] != 0ull && kk[q] >= T);
+    int incl = cnt;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    n = min(__shfl(incl, 63, 64), kMaxCand);
+    int pos = incl - cnt;
+#pragma unroll
+    for (int q = 0; q < kMaxK; ++q)
+      if (kk[q] != 0ull && kk[q] >= T && pos < kMaxCand) scratch[pos++] = kk[q];
+    if (lane == 0) row_lse[r] = M + __logf(S);
+  }
+  __syncthreads();
+  if (active) {
+    for (int p = lane; p < n; p += 64) {
+      const uint64_t k = scratch[p];
+      int rk = 0, q = 0;
+      for (; q + 4 <= n; q += 4)
+        rk += (scratch[q] > k) + (scratch[q + 1] > k) + (scratch[q + 2] > k) + (scratch[q + 3] > k);
+      for (; q < n; ++q) rk += scratch[q] > k;
+      if (rk < topk) row_top[r * topk + rk] = k;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBuildThreads) void dtree_build_kernel(
+    const uint64_t* __restrict__ row_top, const float* __restrict__ row_lse, int depth, int topk, int R,
+    int N, const int32_t* __restrict__ root_tokens, int32_t* __restrict__ parents,
+    int32_t* __restrict__ tokens, float* __restrict__ scores) {
+  __shared__ float s_lse[kMaxRows];
+  __shared__ uint64_t s_top[kMaxRows * kMaxK];        // row r's best keys at r * topk + rank
+  __shared__ uint64_t s_list[TV_DRAFT_MAX_DEPTH * kMaxCand];  // level l ranked at l * kMaxCand
+  __shared__ uint64_t s_tmp[kMaxCand];
+  __shared__ int s_rank[kMaxCand];
+  __shared__ int s_kept[TV_DRAFT_MAX_DEPTH], s_base[TV_DRAFT_MAX_DEPTH];
+
+  const int tid = threadIdx.x;
+  const long b = blockIdx.x;
+  const long seq_rows = b * R;
+  for (int e = tid; e < R * topk; e += kBuildThreads) s_top[e] = row_top[seq_rows * topk + e];
+  for (int e = tid; e < R; e += kBuildThreads) s_lse[e] = row_lse[seq_rows + e];
+  __syncthreads();
+
+  // ---- levels: score and rank every candidate; the rank of candidate c
+  // is counted in kBuildThreads / nc parts and summed in LDS ----
+  const int K2 = topk * topk;
+  for (int l = 0; l < depth; ++l) {
+    const int nc = l == 0 ? topk : K2;
+    const uint32_t gbase = l == 0 ? 0u : static_cast<uint32_t>(topk + (l - 1) * K2);
+    if (tid < nc) {
+      const int j = tid / topk, rr = tid - j * topk;
+      const int row = l == 0 ? 0 : 1 + (l - 1) * topk + j;
+      const uint64_t tk = s_top[row * topk + rr];
+      const float F = l == 0 ? 0.f : key_value(s_list[(l - 1) * kMaxCand + j]);
+      const float sc = F + (key_value(tk) - s_lse[row]);
+      s_tmp[tid] = make_key(sc, gbase + tid);
+      s_rank[tid] = 0;
+    }
+    __syncthreads();
+    {
+      const int parts = kBuildThreads / nc;
+      const int part = tid / nc, c = tid - part * nc;
+      if (part < parts) {
+        const int span = (nc + parts - 1) / parts;
+        const int q0 = part * span, q1 = min(nc, q0 + span);
+        const uint64_t k = s_tmp[c];
+        int cnt = 0;
+        for (int q = q0; q < q1; ++q) cnt += s_tmp[q] > k;
+        if (cnt) atomicAdd(&s_rank[c], cnt);
+      }
+    }
+    __syncthreads();
+    if (tid < nc) s_list[l * kMaxCand + s_rank[tid]] = s_tmp[tid];
+    __syncthreads();
+  }
+
+  // ---- global top N - 1: a prefix of every level's ranked list ----
+  const int need = N - 1;
+  if (tid < depth) s_kept[tid] = 0;
+  __syncthreads();
+  for (int p = tid; p < depth * kMaxCand; p += kBuildThreads) {
+    const int l = p / kMaxCand, rho = p - l * kMaxCand;
+    const int nl = l == 0 ? topk : K2;
+    if (rho >= nl || rho >= need) continue;
+    const uint64_t k = s_list[l * kMaxCand + rho];
+    int g = rho;
+    for (int l2 = 0; l2 < depth && g < need; ++l2)
+      if (l2 != l) g += count_above(s_list + l2 * kMaxCand, l2 == 0 ? topk : K2, k);
+    if (g < need) atomicMax(&s_kept[l], rho + 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 1;
+    for (int l = 0; l < depth; ++l) {
+      s_base[l] = acc;
+      acc += s_kept[l];
+    }
+  }
+  __syncthreads();
+
+  // ---- labels: level by level, rank order within a level ----
+  const long ob = b * N;
+  if (tid == 0) {
+    parents[ob] = -1;
+    tokens[ob] = root_tokens ? root_tokens[b] : 0;
+    if (scores) scores[ob] = 0.f;
+  }
+  for (int p = tid; p < depth * kMaxCand; p += kBuildThreads) {
+    const int l = p / kMaxCand, rho = p - l * kMaxCand;
+    if (rho >= s_kept[l]) continue;
+    const uint64_t k = s_list[l * kMaxCand + rho];
+    const uint32_t gbase = l == 0 ? 0u : static_cast<uint32_t>(topk + (l - 1) * K2);
+    const int i = static_cast<int>(key_index(k) - gbase);
+    const int j = i / topk, rr = i - j * topk;
+    const int row = l == 0 ? 0 : 1 + (l - 1) * topk + j;
+    const int label = s_base[l] + rho;
+    if (label >= N || row >= R) continue;
+    parents[ob + label] = l == 0 ? 0 : s_base[l - 1] + j;
+    tokens[ob + label] = static_cast<int32_t>(key_index(s_top[row * topk + rr]));
+    if (scores) scores[ob + label] = key_value(k);
+  }
+}
+
+struct Layout {
+  int R, C;
+  size_t units;        // (sequence, row, chunk) triples
+  size_t off_keys, off_top, off_lse, bytes;
+};
+Layout layout_for(int B, int depth, int topk, int V) {
+  Layout s;
+  s.R = 1 + (depth - 1) * topk;
+  s.C = (V + kChunk - 1) / kChunk;
+  s.units = static_cast<size_t>(B) * s.R * s.C;
+  const size_t rows = static_cast<size_t>(B) * s.R;
+  s.off_keys = s.units * sizeof(float2);
+  s.off_top = s.off_keys + s.units * topk * sizeof(uint64_t);
+  s.off_lse = s.off_top + rows * topk * sizeof(uint64_t);
+  s.bytes = s.off_lse + rows * sizeof(float);
+  return s;
+}
+
+}  // namespace
+
+size_t draft_tree_workspace_bytes(int B, int depth, int topk, int V) {
+  return layout_for(B, depth, topk, V).bytes;
+}
+
+hipError_t launch_draft_tree(const DraftTreeArgs& a, hipStream_t stream) {
+  const Layout s = layout_for(a.B, a.depth, a.topk, a.V);
+  char* ws = static_cast<char*>(a.workspace);
+  float2* stats = reinterpret_cast<float2*>(ws);
+  uint64_t* keys = reinterpret_cast<uint64_t*>(ws + s.off_keys);
+  uint64_t* top = reinterpret_cast<uint64_t*>(ws + s.off_top);
+  float* lse = reinterpret_cast<float*>(ws + s.off_lse);
+  const dim3 grid1(static_cast<unsigned>(s.units));
+  if ((a.V & 3) == 0)
+    hipLaunchKernelGGL(dtree_chunk_kernel<true>, grid1, dim3(kChunkThreads), 0, stream, a.draft_logits,
+                       a.depth, a.topk, a.V, s.R, s.C, stats, keys);
+  else
+    hipLaunchKernelGGL(dtree_chunk_kernel<false>, grid1, dim3(kChunkThreads), 0, stream, a.draft_logits,
+                       a.depth, a.topk, a.V, s.R, s.C, stats, keys);
+  const long rows = static_cast<long>(a.B) * s.R;
+  hipLaunchKernelGGL(dtree_row_kernel, dim3(static_cast<unsigned>((rows + kRowWaves - 1) / kRowWaves)),
+                     dim3(64 * kRowWaves), 0, stream, stats, keys, a.topk, s.C, rows, top, lse);
+  hipLaunchKernelGGL(dtree_build_kernel, dim3(a.B), dim3(kBuildThreads), 0, stream, top, lse, a.depth,
+                     a.topk, s.R, a.N, a.root_tokens, a.parents, a.tokens, a.scores);
+  return hipGetLastError();
+}
+
+}  // namespace tv

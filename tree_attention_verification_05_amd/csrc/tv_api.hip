@@ -188,6 +188,41 @@ tv_status tv_lm_head_argmax(const void* hidden, const void* weight, int32_t M, i
   return launched(launch_lm_head_argmax(a, stream));
 }
 
+static bool draft_tree_shape_ok(int32_t B, int32_t depth, int32_t topk, int32_t V) {
+  return B > 0 && depth >= 1 && depth <= TV_DRAFT_MAX_DEPTH && topk >= 1 && topk <= TV_DRAFT_MAX_TOPK &&
+         topk <= V && V <= TV_DRAFT_MAX_VOCAB;
+}
+
+size_t tv_build_draft_tree_workspace_size(int32_t B, int32_t depth, int32_t topk, int32_t V) {
+  if (!draft_tree_shape_ok(B, depth, topk, V)) return 0;
+  return draft_tree_workspace_bytes(B, depth, topk, V);
+}
+
+tv_status tv_build_draft_tree(const float* draft_logits, int32_t B, int32_t depth, int32_t topk, int32_t V,
+                              int32_t N, const int32_t* root_tokens, int32_t* parents, int32_t* tokens,
+                              float* scores, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!draft_logits || !parents || !tokens) return TV_ERR_NULL;
+  if (!draft_tree_shape_ok(B, depth, topk, V) || N < 1 || N > TV_MAX_NODES) return TV_ERR_SHAPE;
+  const long generated = topk + static_cast<long>(depth - 1) * topk * topk;
+  if (N - 1 > generated) return TV_ERR_SHAPE;
+  if (!aligned16(draft_logits)) return TV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < draft_tree_workspace_bytes(B, depth, topk, V)) return TV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TV_ERR_ALIGN;
+  DraftTreeArgs a;
+  a.draft_logits = draft_logits;
+  a.B = B;
+  a.depth = depth;
+  a.topk = topk;
+  a.V = V;
+  a.N = N;
+  a.root_tokens = root_tokens;
+  a.parents = parents;
+  a.tokens = tokens;
+  a.scores = scores;
+  a.workspace = workspace;
+  return launched(launch_draft_tree(a, stream));
+}
+
 tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks, const int32_t* block_table,
                         int32_t max_blocks, int32_t block_size, const int32_t* prefix_lens,
                         const int32_t* accepted_nodes, const int32_t* accept_len, int32_t B,

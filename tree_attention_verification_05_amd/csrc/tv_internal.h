@@ -108,6 +108,18 @@ struct LmArgs {
 size_t lm_head_workspace_bytes(int M, int V);
 hipError_t launch_lm_head_argmax(const LmArgs& a, hipStream_t stream);
 
+struct DraftTreeArgs {
+  const float* draft_logits;  // [B][depth][topk][V]
+  int B, depth, topk, V, N;
+  const int32_t* root_tokens;  // may be NULL
+  int32_t* parents;
+  int32_t* tokens;
+  float* scores;               // may be NULL
+  void* workspace;
+};
+size_t draft_tree_workspace_bytes(int B, int depth, int topk, int V);
+hipError_t launch_draft_tree(const DraftTreeArgs& a, hipStream_t stream);
+
 struct CompactArgs {
   void* k_cache;
   void* v_cache;

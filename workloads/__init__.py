@@ -52,6 +52,7 @@ _C_PREFIX, _C_TREE, _C_MATCH, _C_BLOCKS, _C_Q, _C_K, _C_V, _C_LOGITS, _C_PLANT =
 _C_KNEW, _C_VNEW = 10, 11
 _C_UNIF, _C_EXPO, _C_QNOISE, _C_QDRAW = 12, 13, 14, 15
 _C_HID, _C_WLM = 16, 17
+_C_DLOGITS, _C_DROOT = 18, 19
 
 # Sampling temperature of the stochastic-verification inputs: the top of the
 # 0.0-0.7 range that the P-EAGLE page's practical notes recommend for speedup.
@@ -485,3 +486,34 @@ def lm_head_inputs(spec, seed: int = 0):
     hid = _to_dtype(_normal((spec.B, spec.N, H), 1.0, seed, spec.tag, _C_HID), "bf16")
     w = _to_dtype(_normal((spec.V, H), spec.logit_std / float(np.sqrt(H)), seed, spec.tag, _C_WLM), "bf16")
     return hid, w
+
+
+def draft_tree_shape(spec) -> Tuple[int, int]:
+    """(depth, topk) of the draft-tree construction that yields the
+    workload's tree size: the EAGLE-2 tree keeps its own; the random trees
+    expand their depth with topk 10 (4 in the tiny case, whose vocab is
+    1000); the chain is topk 1 over N - 1 levels (the greedy chain)."""
+    kind = spec.tree[0]
+    if kind == "eagle2":
+        return int(spec.tree[2]), int(spec.tree[3])
+    if kind == "chain":
+        return spec.N - 1, 1
+    return int(spec.tree[2]), (4 if "tiny" in spec.name else 10)
+
+
+def draft_tree_inputs(spec, seed: int = 0, depth: Optional[int] = None, topk: Optional[int] = None):
+    """The drafter's next-token scores for draft-tree construction.
+
+    Returns a dict with ``draft_logits`` [B, depth, topk, V] float32,
+    N(0, logit_std^2) (row (l, j): the scores at the j-th best node of
+    level l - 1; row (0, 0) at the root), ``root_tokens`` [B] int32 uniform
+    in [0, V), and ``depth``, ``topk``, ``N``.  Each from its own stream.
+    """
+    d0, k0 = draft_tree_shape(spec)
+    depth = d0 if depth is None else depth
+    topk = k0 if topk is None else topk
+    B, V = spec.B, spec.V
+    lg = _normal((B, depth, topk, V), spec.logit_std, seed, spec.tag, _C_DLOGITS)
+    root = _rng(seed, spec.tag, _C_DROOT).integers(0, V, size=B, dtype=np.int64).astype(np.int32)
+    return {"draft_logits": torch.from_numpy(lg.reshape(B, depth, topk, V)),
+            "root_tokens": torch.from_numpy(root), "depth": depth, "topk": topk, "N": spec.N}
