@@ -137,13 +137,8 @@ __global__ __launch_bounds__(kChunkThreads) void dtree_chunk_kernel(
     s_T = 0ull;
   }
 
-  // chunk maximum and sum of exp(x - max); entries past the row end are -inf
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 4 * kPer4; ++i) m = fmaxf(m, x[i]);
-  m = wave_max(m);
-  if (lane == 0) s_m[wave] = m;
-  // this thread's best entry (strict '>' keeps the lowest index of equals)
+  // this thread's best entry (strict '>' keeps the lowest index of equals),
+  // which is also its maximum; entries past the row end are -inf
   float bv = -INFINITY;
   int bi = -1;
 #pragma unroll
@@ -161,13 +156,20 @@ __global__ __launch_bounds__(kChunkThreads) void dtree_chunk_kernel(
   gk = max_u64(gk, __shfl_xor(gk, 2, 64));
   gk = max_u64(gk, __shfl_xor(gk, 4, 64));
   if ((tid & 7) == 0) s_grp[tid >> 3] = gk;
-  __syncthreads();
-  m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  // sum of exp(x - thread max), then rescaled to the wave maximum; the chunk
+  // combines the waves at the end
   float s = 0.f;
+  if (bi >= 0) {
 #pragma unroll
-  for (int i = 0; i < 4 * kPer4; ++i) s += __expf(x[i] - m);
-  s = wave_sum(s);
-  if (lane == 0) s_s[wave] = s;
+    for (int i = 0; i < 4 * kPer4; ++i) s += __expf(x[i] - bv);
+  }
+  const float mw = wave_max(bv);
+  s = wave_sum(bi >= 0 ? s * __expf(bv - mw) : 0.f);
+  if (lane == 0) {
+    s_m[wave] = mw;
+    s_s[wave] = s;
+  }
+  __syncthreads();
   // cut: the topk-th largest group maximum (0 when fewer than topk groups
   // hold an entry: then every entry passes)
   if (tid < kGroups) {
@@ -232,7 +234,11 @@ __global__ __launch_bounds__(kChunkThreads) void dtree_chunk_kernel(
     }
   }
   if (tid == 0) {
-    const float ss = s_s[0] + s_s[1] + s_s[2] + s_s[3];
+    const float m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    float ss = 0.f;
+#pragma unroll
+    for (int w = 0; w < kChunkThreads / 64; ++w)
+      if (s_m[w] > -INFINITY) ss += s_s[w] * __expf(s_m[w] - m);
     stats[sr * C + c] = make_float2(m, ss);
   }
 }
@@ -313,7 +319,8 @@ __global__ __launch_bounds__(kBuildThreads) void dtree_build_kernel(
   __shared__ uint64_t s_list[TV_DRAFT_MAX_DEPTH * kMaxCand];  // level l ranked at l * kMaxCand
   __shared__ uint64_t s_tmp[kMaxCand];
   __shared__ int s_rank[kMaxCand];
-  __shared__ int s_kept[TV_DRAFT_MAX_DEPTH], s_base[TV_DRAFT_MAX_DEPTH];
+  __shared__ int s_grank[TV_DRAFT_MAX_DEPTH * kMaxCand];  // global rank of each level's leading entries
+  __shared__ int s_kept[TV_DRAFT_MAX_DEPTH], s_base[TV_DRAFT_MAX_DEPTH], s_moff[TV_DRAFT_MAX_DEPTH + 1];
 
   const int tid = threadIdx.x;
   const long b = blockIdx.x;
@@ -355,19 +362,49 @@ __global__ __launch_bounds__(kBuildThreads) void dtree_build_kernel(
     __syncthreads();
   }
 
-  // ---- global top N - 1: a prefix of every level's ranked list ----
+  // ---- global top N - 1: a prefix of every level's ranked list.  Only the
+  // first m_l = min(n_l, N - 1) entries of level l can be kept; the global
+  // rank of one of them is its rank in its level plus, for every other level,
+  // the number of entries there that are better (one binary search per
+  // (entry, other level) pair, summed in LDS) ----
   const int need = N - 1;
+  if (tid == 0) {
+    int acc = 0;
+    for (int l = 0; l < depth; ++l) {
+      s_moff[l] = acc;
+      acc += min(l == 0 ? topk : K2, need);
+    }
+    s_moff[depth] = acc;
+  }
   if (tid < depth) s_kept[tid] = 0;
   __syncthreads();
-  for (int p = tid; p < depth * kMaxCand; p += kBuildThreads) {
-    const int l = p / kMaxCand, rho = p - l * kMaxCand;
-    const int nl = l == 0 ? topk : K2;
-    if (rho >= nl || rho >= need) continue;
-    const uint64_t k = s_list[l * kMaxCand + rho];
-    int g = rho;
-    for (int l2 = 0; l2 < depth && g < need; ++l2)
-      if (l2 != l) g += count_above(s_list + l2 * kMaxCand, l2 == 0 ? topk : K2, k);
-    if (g < need) atomicMax(&s_kept[l], rho + 1);
+  const int npairs = s_moff[depth];
+  for (int p = tid; p < npairs; p += kBuildThreads) {
+    int l = 0;
+    while (s_moff[l + 1] <= p) ++l;
+    s_grank[p] = p - s_moff[l];
+  }
+  __syncthreads();
+  if (depth > 1) {
+    const int nitems = npairs * (depth - 1);
+    for (int it = tid; it < nitems; it += kBuildThreads) {
+      const int p = it / (depth - 1);
+      int l2 = it - p * (depth - 1);
+      int l = 0;
+      while (s_moff[l + 1] <= p) ++l;
+      if (l2 >= l) ++l2;
+      const int rho = p - s_moff[l];
+      const uint64_t k = s_list[l * kMaxCand + rho];
+      const int c = count_above(s_list + l2 * kMaxCand, l2 == 0 ? topk : K2, k);
+      if (c) atomicAdd(&s_grank[p], c);
+    }
+    __syncthreads();
+  }
+  for (int p = tid; p < npairs; p += kBuildThreads) {
+    if (s_grank[p] >= need) continue;
+    int l = 0;
+    while (s_moff[l + 1] <= p) ++l;
+    atomicMax(&s_kept[l], p - s_moff[l] + 1);
   }
   __syncthreads();
   if (tid == 0) {
