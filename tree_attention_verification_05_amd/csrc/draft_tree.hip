@@ -5,8 +5,10 @@
 // "vLLM-TreeEagle" README, 核心组件 item 3: multi-level candidate generation
 // with path pruning.)
 //
-// Chunk kernel (rows x chunks workgroups of 256 threads): one 8192-entry chunk
-// of one score row is held in registers after one pass of 16-byte loads.  It
+// Chunk kernel (rows x chunks workgroups of 256 threads): one chunk of one
+// score row (8192 entries, or 4096 when a batch has fewer than 1024 of the
+// larger ones, so that loads and the selection of different workgroups
+// overlap) is held in registers after one pass of 16-byte loads.  It
 // yields the chunk's maximum, its sum of exp(x - max), and its topk best
 // entries as 64-bit keys (value, then lower index).  The topk selection cuts
 // first: T = the topk-th largest of the 32 maxima of 8-lane groups bounds the
@@ -32,8 +34,9 @@ namespace tv {
 namespace {
 
 constexpr int kChunkThreads = 256;
-constexpr int kPer4 = 8;                                // 16-byte loads per thread
-constexpr int kChunk = kChunkThreads * kPer4 * 4;       // 8192 entries per chunk
+constexpr int kBigPer4 = 8;                             // 16-byte loads per thread: 8192-entry chunks
+constexpr int kSmallPer4 = 4;                           // 4096-entry chunks for small batches
+constexpr int kSmallBatchUnits = 1024;                  // below this many 8192-entry chunks, halve them
 constexpr int kGroups = kChunkThreads / 8;              // 8-lane groups per chunk workgroup
 constexpr int kCandCap = 512;                           // ranked candidates per chunk
 constexpr int kRowWaves = 4;                            // rows per row-merge workgroup
@@ -41,7 +44,8 @@ constexpr int kBuildThreads = 1024;
 constexpr int kMaxK = TV_DRAFT_MAX_TOPK;
 constexpr int kMaxCand = kMaxK * kMaxK;                 // candidates of one level
 constexpr int kMaxRows = 1 + (TV_DRAFT_MAX_DEPTH - 1) * kMaxK;
-constexpr int kMaxChunks = (TV_DRAFT_MAX_VOCAB + kChunk - 1) / kChunk;
+constexpr int kMinChunk = kChunkThreads * kSmallPer4 * 4;
+constexpr int kMaxChunks = (TV_DRAFT_MAX_VOCAB + kMinChunk - 1) / kMinChunk;
 static_assert(kMaxChunks <= 64, "one lane per chunk in the row merge");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -86,18 +90,36 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// Number of keys in a[q0, q1) greater than k.  a is 16-byte aligned and q0
+// even: keys come in pairs from 16-byte LDS reads, eight keys per round trip.
+__device__ __forceinline__ int count_greater(const uint64_t* a, int q0, int q1, uint64_t k) {
+  const ulonglong2* a2 = reinterpret_cast<const ulonglong2*>(a);
+  int cnt = 0, q = q0;
+  for (; q + 8 <= q1; q += 8) {
+    const ulonglong2 x0 = a2[q >> 1], x1 = a2[(q >> 1) + 1], x2 = a2[(q >> 1) + 2], x3 = a2[(q >> 1) + 3];
+    cnt += (x0.x > k) + (x0.y > k) + (x1.x > k) + (x1.y > k) + (x2.x > k) + (x2.y > k) + (x3.x > k) +
+           (x3.y > k);
+  }
+  for (; q + 2 <= q1; q += 2) {
+    const ulonglong2 x0 = a2[q >> 1];
+    cnt += (x0.x > k) + (x0.y > k);
+  }
+  if (q < q1) cnt += a[q] > k;
+  return cnt;
+}
+
 // Row r of a sequence: r = 0 is the root's row (level 0, slot 0); r >= 1 is
 // level 1 + (r - 1) / topk, slot (r - 1) % topk.
 __device__ __forceinline__ int row_level(int r, int topk) { return r == 0 ? 0 : 1 + (r - 1) / topk; }
 __device__ __forceinline__ int row_slot(int r, int topk) { return r == 0 ? 0 : (r - 1) % topk; }
 
-template <bool kVec>
+template <bool kVec, int kPer4>
 __global__ __launch_bounds__(kChunkThreads) void dtree_chunk_kernel(
     const float* __restrict__ logits, int depth, int topk, int V, int R, int C,
     float2* __restrict__ stats, uint64_t* __restrict__ keys) {
   __shared__ float s_m[kChunkThreads / 64], s_s[kChunkThreads / 64];
   __shared__ uint64_t s_grp[kGroups];
-  __shared__ uint64_t s_cand[kCandCap];
+  __shared__ __attribute__((aligned(16))) uint64_t s_cand[kCandCap];
   __shared__ uint64_t s_wk[kChunkThreads / 64];
   __shared__ uint64_t s_T;
   __shared__ int s_n;
@@ -108,6 +130,7 @@ __global__ __launch_bounds__(kChunkThreads) void dtree_chunk_kernel(
   const long b = sr / R;
   const int r = static_cast<int>(sr - b * R);
   const float* row = logits + ((b * depth + row_level(r, topk)) * topk + row_slot(r, topk)) * static_cast<long>(V);
+  constexpr int kChunk = kChunkThreads * kPer4 * 4;
   const int lo = c * kChunk, hi = min(V, lo + kChunk);
   // entry x[4u + e] of this thread is lo + 4 (u * 256 + tid) + e: indices
   // increase with (u, e)
@@ -201,10 +224,7 @@ __global__ __launch_bounds__(kChunkThreads) void dtree_chunk_kernel(
   if (n <= kCandCap) {
     for (int p = tid; p < n; p += kChunkThreads) {
       const uint64_t k = s_cand[p];
-      int rank = 0, q = 0;
-      for (; q + 4 <= n; q += 4)
-        rank += (s_cand[q] > k) + (s_cand[q + 1] > k) + (s_cand[q + 2] > k) + (s_cand[q + 3] > k);
-      for (; q < n; ++q) rank += s_cand[q] > k;
+      const int rank = count_greater(s_cand, 0, n, k);
       if (rank < topk) out[rank] = k;
     }
     for (int q = n + tid; q < topk; q += kChunkThreads) out[q] = 0ull;
@@ -243,17 +263,6 @@ __global__ __launch_bounds__(kChunkThreads) void dtree_chunk_kernel(
   }
 }
 
-// Number of entries of a descending list of distinct keys that exceed k.
-__device__ __forceinline__ int count_above(const uint64_t* list, int n, uint64_t k) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (list[mid] > k) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo;
-}
-
 // Row merge (one wave per row, one lane per chunk): the row's log-sum-exp
 // and its topk best keys, by the same cut-then-rank selection over the chunk
 // lists (descending): T = the topk-th largest chunk maximum (0 with fewer
@@ -262,7 +271,7 @@ __device__ __forceinline__ int count_above(const uint64_t* list, int n, uint64_t
 __global__ __launch_bounds__(64 * kRowWaves) void dtree_row_kernel(
     const float2* __restrict__ stats, const uint64_t* __restrict__ keys, int topk, int C, long rows,
     uint64_t* __restrict__ row_top, float* __restrict__ row_lse) {
-  __shared__ uint64_t s_scr[kRowWaves][kMaxCand];
+  __shared__ __attribute__((aligned(16))) uint64_t s_scr[kRowWaves][kMaxCand];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const long r = static_cast<long>(blockIdx.x) * kRowWaves + wave;
   const bool active = r < rows;
@@ -301,13 +310,30 @@ __global__ __launch_bounds__(64 * kRowWaves) void dtree_row_kernel(
   if (active) {
     for (int p = lane; p < n; p += 64) {
       const uint64_t k = scratch[p];
-      int rk = 0, q = 0;
-      for (; q + 4 <= n; q += 4)
-        rk += (scratch[q] > k) + (scratch[q + 1] > k) + (scratch[q + 2] > k) + (scratch[q + 3] > k);
-      for (; q < n; ++q) rk += scratch[q] > k;
+      const int rk = count_greater(scratch, 0, n, k);
       if (rk < topk) row_top[r * topk + rk] = k;
     }
   }
+}
+
+// Number of entries of a descending list of distinct keys that exceed k.
+__device__ __forceinline__ int count_above(const uint64_t* list, int n, uint64_t k) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] > k) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// The level l < depth with off[l] <= p < off[l + 1], for nondecreasing
+// offsets held in registers (unrolled compares, no indexed access).
+__device__ __forceinline__ int level_of(int p, const int (&off)[TV_DRAFT_MAX_DEPTH + 1], int depth) {
+  int l = 0;
+#pragma unroll
+  for (int q = 1; q < TV_DRAFT_MAX_DEPTH; ++q) l += (q < depth && off[q] <= p);
+  return l;
 }
 
 __global__ __launch_bounds__(kBuildThreads) void dtree_build_kernel(
@@ -317,10 +343,10 @@ __global__ __launch_bounds__(kBuildThreads) void dtree_build_kernel(
   __shared__ float s_lse[kMaxRows];
   __shared__ uint64_t s_top[kMaxRows * kMaxK];        // row r's best keys at r * topk + rank
   __shared__ uint64_t s_list[TV_DRAFT_MAX_DEPTH * kMaxCand];  // level l ranked at l * kMaxCand
-  __shared__ uint64_t s_tmp[kMaxCand];
+  __shared__ __attribute__((aligned(16))) uint64_t s_tmp[kMaxCand];
   __shared__ int s_rank[kMaxCand];
   __shared__ int s_grank[TV_DRAFT_MAX_DEPTH * kMaxCand];  // global rank of each level's leading entries
-  __shared__ int s_kept[TV_DRAFT_MAX_DEPTH], s_base[TV_DRAFT_MAX_DEPTH], s_moff[TV_DRAFT_MAX_DEPTH + 1];
+  __shared__ int s_kept[TV_DRAFT_MAX_DEPTH];
 
   const int tid = threadIdx.x;
   const long b = blockIdx.x;
@@ -348,12 +374,10 @@ __global__ __launch_bounds__(kBuildThreads) void dtree_build_kernel(
     {
       const int parts = kBuildThreads / nc;
       const int part = tid / nc, c = tid - part * nc;
-      if (part < parts) {
-        const int span = (nc + parts - 1) / parts;
-        const int q0 = part * span, q1 = min(nc, q0 + span);
-        const uint64_t k = s_tmp[c];
-        int cnt = 0;
-        for (int q = q0; q < q1; ++q) cnt += s_tmp[q] > k;
+      const int span = (((nc + parts - 1) / parts) + 1) & ~1;  // even: pairs of keys
+      const int q0 = part * span;
+      if (part < parts && q0 < nc) {
+        const int cnt = count_greater(s_tmp, q0, min(nc, q0 + span), s_tmp[c]);
         if (cnt) atomicAdd(&s_rank[c], cnt);
       }
     }
@@ -366,88 +390,92 @@ __global__ __launch_bounds__(kBuildThreads) void dtree_build_kernel(
   // first m_l = min(n_l, N - 1) entries of level l can be kept; the global
   // rank of one of them is its rank in its level plus, for every other level,
   // the number of entries there that are better (one binary search per
-  // (entry, other level) pair, summed in LDS) ----
+  // (entry, other level) pair, summed in LDS).  Pair p of level l is entry
+  // p - moff[l] of that level; every thread keeps the level offsets in
+  // registers ----
   const int need = N - 1;
-  if (tid == 0) {
+  int moff[TV_DRAFT_MAX_DEPTH + 1];
+  {
     int acc = 0;
-    for (int l = 0; l < depth; ++l) {
-      s_moff[l] = acc;
-      acc += min(l == 0 ? topk : K2, need);
+#pragma unroll
+    for (int l = 0; l <= TV_DRAFT_MAX_DEPTH; ++l) {
+      moff[l] = acc;
+      if (l < depth) acc += min(l == 0 ? topk : K2, need);
     }
-    s_moff[depth] = acc;
   }
+  const int npairs = moff[depth < TV_DRAFT_MAX_DEPTH ? depth : TV_DRAFT_MAX_DEPTH];
   if (tid < depth) s_kept[tid] = 0;
-  __syncthreads();
-  const int npairs = s_moff[depth];
-  for (int p = tid; p < npairs; p += kBuildThreads) {
-    int l = 0;
-    while (s_moff[l + 1] <= p) ++l;
-    s_grank[p] = p - s_moff[l];
-  }
+  for (int p = tid; p < npairs; p += kBuildThreads) s_grank[p] = p - moff[level_of(p, moff, depth)];
   __syncthreads();
   if (depth > 1) {
     const int nitems = npairs * (depth - 1);
     for (int it = tid; it < nitems; it += kBuildThreads) {
-      const int p = it / (depth - 1);
-      int l2 = it - p * (depth - 1);
-      int l = 0;
-      while (s_moff[l + 1] <= p) ++l;
+      // consecutive threads take different entries against one list: their
+      // LDS atomics hit different words
+      int l2 = it / npairs;
+      const int p = it - l2 * npairs;
+      const int l = level_of(p, moff, depth);
       if (l2 >= l) ++l2;
-      const int rho = p - s_moff[l];
-      const uint64_t k = s_list[l * kMaxCand + rho];
-      const int c = count_above(s_list + l2 * kMaxCand, l2 == 0 ? topk : K2, k);
+      const uint64_t k = s_list[l * kMaxCand + (p - moff[l])];
+      // entries past the first N - 1 of a level only matter as "N - 1 or more"
+      const int c = count_above(s_list + l2 * kMaxCand, moff[l2 + 1] - moff[l2], k);
       if (c) atomicAdd(&s_grank[p], c);
     }
     __syncthreads();
   }
   for (int p = tid; p < npairs; p += kBuildThreads) {
     if (s_grank[p] >= need) continue;
-    int l = 0;
-    while (s_moff[l + 1] <= p) ++l;
-    atomicMax(&s_kept[l], p - s_moff[l] + 1);
+    const int l = level_of(p, moff, depth);
+    atomicMax(&s_kept[l], p - moff[l] + 1);
   }
   __syncthreads();
-  if (tid == 0) {
+  // labels: level by level (level offsets base[l] = 1 + kept nodes of the
+  // levels above), rank order within a level
+  int base[TV_DRAFT_MAX_DEPTH + 1];
+  {
     int acc = 1;
-    for (int l = 0; l < depth; ++l) {
-      s_base[l] = acc;
-      acc += s_kept[l];
+#pragma unroll
+    for (int l = 0; l <= TV_DRAFT_MAX_DEPTH; ++l) {
+      base[l] = acc;
+      if (l < depth) acc += s_kept[l];
     }
   }
-  __syncthreads();
 
-  // ---- labels: level by level, rank order within a level ----
   const long ob = b * N;
   if (tid == 0) {
     parents[ob] = -1;
     tokens[ob] = root_tokens ? root_tokens[b] : 0;
     if (scores) scores[ob] = 0.f;
   }
-  for (int p = tid; p < depth * kMaxCand; p += kBuildThreads) {
-    const int l = p / kMaxCand, rho = p - l * kMaxCand;
-    if (rho >= s_kept[l]) continue;
+  for (int p = tid; p < need; p += kBuildThreads) {
+    const int label = 1 + p;
+    const int l = level_of(label, base, depth);
+    const int rho = label - base[l];
     const uint64_t k = s_list[l * kMaxCand + rho];
     const uint32_t gbase = l == 0 ? 0u : static_cast<uint32_t>(topk + (l - 1) * K2);
     const int i = static_cast<int>(key_index(k) - gbase);
     const int j = i / topk, rr = i - j * topk;
     const int row = l == 0 ? 0 : 1 + (l - 1) * topk + j;
-    const int label = s_base[l] + rho;
-    if (label >= N || row >= R) continue;
-    parents[ob + label] = l == 0 ? 0 : s_base[l - 1] + j;
+    if (row >= R) continue;
+    parents[ob + label] = l == 0 ? 0 : base[l - 1] + j;
     tokens[ob + label] = static_cast<int32_t>(key_index(s_top[row * topk + rr]));
     if (scores) scores[ob + label] = key_value(k);
   }
 }
 
 struct Layout {
-  int R, C;
+  int R, C, per4;
   size_t units;        // (sequence, row, chunk) triples
   size_t off_keys, off_top, off_lse, bytes;
 };
 Layout layout_for(int B, int depth, int topk, int V) {
   Layout s;
   s.R = 1 + (depth - 1) * topk;
-  s.C = (V + kChunk - 1) / kChunk;
+  const int big = kChunkThreads * kBigPer4 * 4;
+  const long big_units = static_cast<long>(B) * s.R * ((V + big - 1) / big);
+  s.per4 = big_units < kSmallBatchUnits ? kSmallPer4 : kBigPer4;
+  const int chunk = kChunkThreads * s.per4 * 4;
+  s.C = (V + chunk - 1) / chunk;
   s.units = static_cast<size_t>(B) * s.R * s.C;
   const size_t rows = static_cast<size_t>(B) * s.R;
   s.off_keys = s.units * sizeof(float2);
@@ -471,12 +499,22 @@ hipError_t launch_draft_tree(const DraftTreeArgs& a, hipStream_t stream) {
   uint64_t* top = reinterpret_cast<uint64_t*>(ws + s.off_top);
   float* lse = reinterpret_cast<float*>(ws + s.off_lse);
   const dim3 grid1(static_cast<unsigned>(s.units));
-  if ((a.V & 3) == 0)
-    hipLaunchKernelGGL(dtree_chunk_kernel<true>, grid1, dim3(kChunkThreads), 0, stream, a.draft_logits,
-                       a.depth, a.topk, a.V, s.R, s.C, stats, keys);
-  else
-    hipLaunchKernelGGL(dtree_chunk_kernel<false>, grid1, dim3(kChunkThreads), 0, stream, a.draft_logits,
-                       a.depth, a.topk, a.V, s.R, s.C, stats, keys);
+  const bool vec = (a.V & 3) == 0;
+  if (s.per4 == kSmallPer4) {
+    if (vec)
+      hipLaunchKernelGGL((dtree_chunk_kernel<true, kSmallPer4>), grid1, dim3(kChunkThreads), 0, stream,
+                         a.draft_logits, a.depth, a.topk, a.V, s.R, s.C, stats, keys);
+    else
+      hipLaunchKernelGGL((dtree_chunk_kernel<false, kSmallPer4>), grid1, dim3(kChunkThreads), 0, stream,
+                         a.draft_logits, a.depth, a.topk, a.V, s.R, s.C, stats, keys);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((dtree_chunk_kernel<true, kBigPer4>), grid1, dim3(kChunkThreads), 0, stream,
+                         a.draft_logits, a.depth, a.topk, a.V, s.R, s.C, stats, keys);
+    else
+      hipLaunchKernelGGL((dtree_chunk_kernel<false, kBigPer4>), grid1, dim3(kChunkThreads), 0, stream,
+                         a.draft_logits, a.depth, a.topk, a.V, s.R, s.C, stats, keys);
+  }
   const long rows = static_cast<long>(a.B) * s.R;
   hipLaunchKernelGGL(dtree_row_kernel, dim3(static_cast<unsigned>((rows + kRowWaves - 1) / kRowWaves)),
                      dim3(64 * kRowWaves), 0, stream, stats, keys, a.topk, s.C, rows, top, lse);
