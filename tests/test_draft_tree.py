@@ -265,3 +265,62 @@ def test_draft_tree_parity_full_size(cfg, sample):
     assert (gp[:, 0] == -1).all() and (gt[:, 0] == root).all()
     for b in range(spec.B):
         assert ((gp[b, 1:] >= 0) & (gp[b, 1:] < np.arange(1, spec.N))).all()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_built_tree_drives_the_verification_step(cfg):
+    """The tree built on the GPU (parents and tokens) drives the verification
+    step on the GPU (mask, attention, greedy acceptance, compaction); the
+    oracle builds its own tree from the same drafter scores and runs its own
+    step.  Some drafted tokens are planted as the target's choice at their
+    parent, so that paths of several nodes are accepted."""
+    import dataclasses
+    import tree_attention_verification_05_amd as T
+    from gpu_util import check_accept, check_attention, oracle_attention, raw_bits, run_step, upload
+    w = W.make_small(cfg)
+    spec = w.spec
+    depth, topk = W.draft_tree_shape(spec)
+    for seed in range(20):       # drafter scores whose every decision is clear
+        x = W.draft_tree_inputs(spec, seed)
+        lg = x["draft_logits"].numpy()
+        root = x["root_tokens"].numpy()
+        built = [O.build_draft_tree(lg[b], spec.N, topk, root_token=int(root[b]), return_generated=True)
+                 for b in range(spec.B)]
+        if all(decision_margin(g[3], g[0], topk, depth) >= DECISION_TOL for g in built):
+            break
+    else:
+        raise AssertionError("no drafter scores with clear decisions")
+    print(f"draft tree -> step on {spec.name}, drafter seed {seed}", flush=True)
+    gp, gt, _ = run_gpu(lg, spec.N, root)
+    parents = np.stack([g[0] for g in built]).astype(np.int32)
+    tokens = np.stack([g[1] for g in built]).astype(np.int32)
+    assert np.array_equal(gp, parents) and np.array_equal(gt, tokens)
+
+    # the target agrees with the drafter at 70 % of the nodes (one child per parent)
+    logits = w.logits.numpy().copy()
+    rng = np.random.default_rng(cfg)
+    for b in range(spec.B):
+        planted_parent = set()
+        for i in range(1, spec.N):
+            p = int(parents[b, i])
+            if p not in planted_parent and rng.random() < 0.7:
+                logits[b, p, tokens[b, i]] = logits[b, p].max() + np.float32(1.0)
+                planted_parent.add(p)
+    w2 = dataclasses.replace(w, parents=gp.astype(np.int32), draft_tokens=gt.astype(np.int32),
+                             logits=torch.from_numpy(logits))
+    d = upload(w2)
+    k0, v0 = raw_bits(w2.k_cache), raw_bits(w2.v_cache)
+    res = run_step(T, d, w2.max_prefix_len)
+    assert int(d["status"].item()) == 0
+    mref, dref = O.build_tree_mask(parents)
+    assert np.array_equal(res["mask"].cpu().numpy().view(np.uint64), mref)
+    seqs = list(range(spec.B))
+    check_attention(res["out"], oracle_attention(w2, seqs), seqs, w2.q.dtype)
+    aref = O.accept_greedy(logits, tokens, parents)
+    check_accept(res, aref)
+    assert aref["accept_len"].max() >= 2
+    kref, vref, nl = O.kv_compact(k0, v0, w2.block_table, w2.prefix_lens, aref["accepted_nodes"],
+                                  aref["accept_len"])
+    assert np.array_equal(res["new_lens"].cpu().numpy(), nl)
+    assert np.array_equal(raw_bits(d["k"]), kref) and np.array_equal(raw_bits(d["v"]), vref)
