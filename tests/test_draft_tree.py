@@ -324,3 +324,15 @@ def test_built_tree_drives_the_verification_step(cfg):
                                   aref["accept_len"])
     assert np.array_equal(res["new_lens"].cpu().numpy(), nl)
     assert np.array_equal(raw_bits(d["k"]), kref) and np.array_equal(raw_bits(d["v"]), vref)
+
+
+def test_binding_rejects_host_tensors_and_bad_shapes():
+    """Argument marshalling only: host tensors, wrong dtypes and ranks are
+    refused before anything reaches the library (no GPU needed)."""
+    import tree_attention_verification_05_amd as T
+    with pytest.raises(ValueError, match="GPU"):
+        T.tv_build_draft_tree(torch.zeros(1, 2, 3, 8), 4)
+    with pytest.raises((TypeError, ValueError)):
+        T.tv_build_draft_tree(torch.zeros(1, 2, 3, 8, dtype=torch.float64), 4)
+    with pytest.raises(TypeError):
+        T.tv_build_draft_tree(np.zeros((1, 2, 3, 8), dtype=np.float32), 4)
