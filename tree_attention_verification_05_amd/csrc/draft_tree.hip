@@ -12,8 +12,8 @@
 // yields the chunk's maximum, its sum of exp(x - max), and its topk best
 // entries as 64-bit keys (value, then lower index).  The topk selection cuts
 // first: T = the topk-th largest of the 32 maxima of 8-lane groups bounds the
-// chunk's topk-th entry from below, and only entries at or above T (at most
-// the 256 of each of topk groups, usually a few more than topk) are ranked.
+// chunk's topk-th entry from below, and only entries at or above T (all of
+// them in at most topk groups, usually a few more than topk) are ranked.
 // If more than kCandCap pass the cut, topk block-wide max rounds take over.
 //
 // Row kernel (one wave per row): merges the chunks of each row into its
@@ -454,6 +454,7 @@ __global__ __launch_bounds__(kBuildThreads) void dtree_build_kernel(
     const uint64_t k = s_list[l * kMaxCand + rho];
     const uint32_t gbase = l == 0 ? 0u : static_cast<uint32_t>(topk + (l - 1) * K2);
     const int i = static_cast<int>(key_index(k) - gbase);
+    if (i < 0 || i >= (l == 0 ? topk : K2)) continue;  // only non-finite scores get here
     const int j = i / topk, rr = i - j * topk;
     const int row = l == 0 ? 0 : 1 + (l - 1) * topk + j;
     if (row >= R) continue;
