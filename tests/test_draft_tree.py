@@ -336,3 +336,24 @@ def test_binding_rejects_host_tensors_and_bad_shapes():
         T.tv_build_draft_tree(torch.zeros(1, 2, 3, 8, dtype=torch.float64), 4)
     with pytest.raises(TypeError):
         T.tv_build_draft_tree(np.zeros((1, 2, 3, 8), dtype=np.float32), 4)
+
+
+@pytest.mark.gpu
+def test_optional_root_tokens_and_scores():
+    """root_tokens NULL gives root token 0; scores NULL leaves the scores
+    unwritten while parents and tokens are unchanged."""
+    import tree_attention_verification_05_amd as T
+    B, depth, topk, V, N = 3, 4, 5, 6000, 30
+    lg, root = clear_inputs(B, depth, topk, V, N, seed0=21)
+    x = torch.from_numpy(lg).cuda()
+    p0, t0, s0 = T.tv_build_draft_tree(x, N, root_tokens=torch.from_numpy(root).cuda())
+    p1, t1, s1 = T.tv_build_draft_tree(x, N, want_scores=False)
+    torch.cuda.synchronize()
+    assert s1 is None
+    assert torch.equal(p0, p1)
+    assert torch.equal(t0[:, 1:], t1[:, 1:]) and (t1[:, 0] == 0).all()
+    assert (t0[:, 0].cpu().numpy() == root).all()
+    for b in range(B):
+        parents, tokens, scores = O.build_draft_tree(lg[b], N, topk)
+        assert np.array_equal(p1[b].cpu().numpy(), parents) and np.array_equal(t1[b].cpu().numpy(), tokens)
+        assert np.abs(s0[b].cpu().numpy() - scores).max() <= SCORE_ATOL
