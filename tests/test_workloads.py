@@ -83,3 +83,25 @@ def test_bf16_values_are_rounded_normals():
     assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
     lg = w.logits.numpy()
     assert abs(lg.std() - 2.0) < 0.05
+
+
+@pytest.mark.parametrize("i", [1, 2, 5])
+def test_draft_tree_inputs(i):
+    """The drafter's scores: seeded and repeatable, [B, depth, topk, V] fp32
+    with the workload's spread, root tokens in range, and a stream of their
+    own (the rest of the workload does not change when they are drawn)."""
+    s = W.SMALL[i]
+    depth, topk = W.draft_tree_shape(s)
+    a = W.draft_tree_inputs(s, 0)
+    b = W.draft_tree_inputs(s, 0)
+    c = W.draft_tree_inputs(s, 1)
+    lg = a["draft_logits"].numpy()
+    assert lg.shape == (s.B, depth, topk, s.V) and lg.dtype == np.float32
+    assert np.array_equal(lg, b["draft_logits"].numpy()) and not np.array_equal(lg, c["draft_logits"].numpy())
+    assert abs(float(lg.std()) - s.logit_std) < 0.05 * s.logit_std
+    r = a["root_tokens"].numpy()
+    assert r.shape == (s.B,) and r.min() >= 0 and r.max() < s.V
+    assert (a["depth"], a["topk"], a["N"]) == (depth, topk, s.N)
+    w0 = W.make_small(i, dense=False)
+    w1 = W.make_small(i, dense=False)
+    assert np.array_equal(w0.parents, w1.parents) and np.array_equal(w0.logits.numpy(), w1.logits.numpy())
