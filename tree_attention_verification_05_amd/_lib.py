@@ -1,4 +1,4 @@
-"""ctypes binding of libtv.so: the same four calls, argument marshalling only.
+"""ctypes binding of libtv.so: the calls include/tv.h declares, argument marshalling only.
 
 Every function takes torch tensors that live on an AMD GPU, checks dtype,
 shape, contiguity and device, and passes raw device pointers plus the current
