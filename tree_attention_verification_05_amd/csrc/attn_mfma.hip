@@ -170,13 +170,18 @@ __device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t addr) {
 
 // One wave copies 64 x 16 bytes from a buffer (base, range in bytes;
 // per-lane byte offset) into LDS: lane l's bytes land at dst + 16 l.  Reads
-// past the range return zeros.  (A plain device function: lambdas would also
-// be compiled for the host, which has no buffer resources.)
+// past the range return zeros.  POLICY is the copy's cache policy: 0, or 2
+// (non-temporal) for data that no other workgroup reads again.  (A plain
+// device function: lambdas would also be compiled for the host, which has no
+// buffer resources.)
+template <int POLICY = 0>
 __device__ __forceinline__ void copy_to_lds(const char* base, int range, int voff, uint16_t* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, range, 0x00020000),
-      (LDS_AS void*)dst, 16, voff, 0, 0, 0);
+      (LDS_AS void*)dst, 16, voff, 0, 0, POLICY);
 }
+
+constexpr int kNonTemporal = 2;  // cache-policy bit of a buffer access (gfx950: nt)
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -334,7 +339,9 @@ __device__ Start balanced_start(const AttnArgs& a, int shares, int share_idx, in
   return st;
 }
 
-template <int D, int NW>
+// POLICY: the cache policy of the K/V copies (kNonTemporal when each tile is
+// read by one workgroup only, i.e. one row chunk per KV head).
+template <int D, int NW, int POLICY>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   using C = Cfg<D, NW>;
@@ -481,8 +488,8 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
         const int copy = jj * NW + wave;
         const int blk = copy * C::kKeysPerCopy < kBlockSize ? b0 : b1;
         const long src = blk * block_bytes + head_bytes;
-        copy_to_lds(kcb + src, range, off_k[jj], kst + copy * 512);
-        copy_to_lds(vcb + src, range, off_v[jj], vst + copy * 512);
+        copy_to_lds<POLICY>(kcb + src, range, off_k[jj], kst + copy * 512);
+        copy_to_lds<POLICY>(vcb + src, range, off_v[jj], vst + copy * 512);
       }
     };
 
@@ -961,8 +968,16 @@ template <int D, int NW>
 hipError_t launch_cfg(const AttnArgs& a, const MfmaParams& mp, hipStream_t stream) {
   using C = Cfg<D, NW>;
   const size_t shmem = C::kStages * C::kStageElems * sizeof(uint16_t);
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NW>), dim3(static_cast<unsigned>(mp.grid)), dim3(C::kThreads),
-                     shmem, stream, a, mp);
+  // with one row chunk per KV head no other workgroup reads a K/V tile
+  // again, and its copies go non-temporal (batched workload 144 -> 129 us,
+  // 70B-shaped chain 306 -> 286 us); several row chunks share each tile
+  // through the L2, where the hint measured 6 % slower
+  if (mp.row_chunks == 1)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NW, kNonTemporal>), dim3(static_cast<unsigned>(mp.grid)),
+                       dim3(C::kThreads), shmem, stream, a, mp);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NW, 0>), dim3(static_cast<unsigned>(mp.grid)), dim3(C::kThreads),
+                       shmem, stream, a, mp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!mp.balanced ? mp.pieces == 1 : mp.grid == a.Hkv * mp.row_chunks) return e;  // no segment is ever shared
