@@ -84,11 +84,13 @@ __device__ __forceinline__ uint64_t make_key(float v, int idx) {
 
 // One wave copies 64 x 16 bytes from a buffer (base, range in bytes; per-lane
 // byte offset) into LDS: lane l's bytes land at dst + 16 l.  Reads past the
-// range return zeros.
+// range return zeros.  POLICY: the copy's cache policy (0, or kNonTemporal
+// for data no other workgroup reads again).
+template <int POLICY = 0>
 __device__ __forceinline__ void copy_to_lds(const char* base, int range, int voff, uint16_t* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, range, 0x00020000),
-      (LDS_AS void*)dst, 16, voff, 0, 0, 0);
+      (LDS_AS void*)dst, 16, voff, 0, 0, POLICY);
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -140,7 +142,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
 }
 
-template <int RW, int CW, int NWR, int BK, int STAGES>
+// WPOL: cache policy of the weight copies (kNonTemporal when one row tile
+// reads the weight once; several row tiles share each slab through the L2).
+template <int RW, int CW, int NWR, int BK, int STAGES, int WPOL>
 __global__ __launch_bounds__((LCfg<RW, CW, NWR, BK, STAGES>::kThreads)) void lmhead_score_kernel(
     LmArgs a, int nmt, int nvt, uint64_t* __restrict__ keys) {
   using C = LCfg<RW, CW, NWR, BK, STAGES>;
@@ -185,7 +189,7 @@ __global__ __launch_bounds__((LCfg<RW, CW, NWR, BK, STAGES>::kThreads)) void lmh
     const int kb = kc * BK * 2;
 #pragma unroll
     for (int j = 0; j < C::kWCopies; ++j)
-      copy_to_lds(wbase, wrange, voff_w[j] + kb, sbase + C::kAElems + (wave * C::kWCopies + j) * 512);
+      copy_to_lds<WPOL>(wbase, wrange, voff_w[j] + kb, sbase + C::kAElems + (wave * C::kWCopies + j) * 512);
 #pragma unroll
     for (int i = 0; i < C::kACopies; ++i)
       copy_to_lds(abase, arange, voff_a[i] + kb, sbase + (wave * C::kACopies + i) * 512);
@@ -306,14 +310,20 @@ __global__ __launch_bounds__(kPickThreads) void lmhead_pick_kernel(LmArgs a, int
 
 int vocab_tiles(int V) { return (V + kBN - 1) / kBN; }
 
+constexpr int kNonTemporal = 2;  // cache-policy bit of a buffer access (gfx950: nt)
+
 template <int RW, int CW, int NWR, int BK, int STAGES>
 hipError_t launch_cfg(const LmArgs& a, uint64_t* keys, hipStream_t stream) {
   using C = LCfg<RW, CW, NWR, BK, STAGES>;
   const int nvt = vocab_tiles(a.V);
   const int nmt = (a.M + C::kBM - 1) / C::kBM;
   const long grid = static_cast<long>(nvt) * nmt;
-  hipLaunchKernelGGL((lmhead_score_kernel<RW, CW, NWR, BK, STAGES>), dim3(static_cast<unsigned>(grid)),
-                     dim3(C::kThreads), 0, stream, a, nmt, nvt, keys);
+  if (nmt == 1)
+    hipLaunchKernelGGL((lmhead_score_kernel<RW, CW, NWR, BK, STAGES, kNonTemporal>), dim3(static_cast<unsigned>(grid)),
+                       dim3(C::kThreads), 0, stream, a, nmt, nvt, keys);
+  else
+    hipLaunchKernelGGL((lmhead_score_kernel<RW, CW, NWR, BK, STAGES, 0>), dim3(static_cast<unsigned>(grid)),
+                       dim3(C::kThreads), 0, stream, a, nmt, nvt, keys);
   return hipGetLastError();
 }
 
