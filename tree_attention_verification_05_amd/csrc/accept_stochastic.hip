@@ -31,7 +31,9 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMinChunk = 8192;       // stats: floats per workgroup at least
-constexpr int kTargetBlocks = 1024;   // enough workgroups to keep HBM busy
+constexpr int kTargetBlocks = 1024;   // enough workgroups to keep HBM busy,
+constexpr int kTargetBlocksManyRows = 2048;  // twice as many from 512 rows on
+constexpr long kManyRows = 512;
 constexpr int kDrawMinChunk = 2048;   // draw: floats per workgroup at least
 constexpr int kDrawMaxChunk = 16384;  // draw: at most (sizes the LDS bitmap)
 constexpr int kPickThreads = 256;
@@ -42,7 +44,8 @@ struct Split {
 };
 
 Split split_rows(long rows, int V, int min_chunk, int max_chunk) {
-  long c = (kTargetBlocks + rows - 1) / rows;
+  const long target = rows >= kManyRows ? kTargetBlocksManyRows : kTargetBlocks;
+  long c = (target + rows - 1) / rows;
   const long cmax = (V + min_chunk - 1) / min_chunk;
   const long cmin = (V + max_chunk - 1) / max_chunk;
   if (c > cmax) c = cmax;
