@@ -113,8 +113,12 @@ __device__ __forceinline__ int count_greater(const uint64_t* a, int q0, int q1, 
 __device__ __forceinline__ int row_level(int r, int topk) { return r == 0 ? 0 : 1 + (r - 1) / topk; }
 __device__ __forceinline__ int row_slot(int r, int topk) { return r == 0 ? 0 : (r - 1) % topk; }
 
+// Six waves per SIMD: the 8192-entry variant fits in 80 registers (a
+// 12-byte spill) instead of 82, so six workgroups instead of five share a
+// compute unit and more loads are in flight (batched workload 146 -> 137 us,
+// chain 111 -> 101 us; seven waves spill 40 bytes and lose 10 %).
 template <bool kVec, int kPer4>
-__global__ __launch_bounds__(kChunkThreads) void dtree_chunk_kernel(
+__global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(6))) void dtree_chunk_kernel(
     const float* __restrict__ logits, int depth, int topk, int V, int R, int C,
     float2* __restrict__ stats, uint64_t* __restrict__ keys) {
   __shared__ float s_m[kChunkThreads / 64], s_s[kChunkThreads / 64];
