@@ -46,20 +46,6 @@ Split split_for(int B, int N, int V) {
   return s;
 }
 
-// Orders floats as unsigned integers; -0.0 and +0.0 map to the same value.
-__device__ __forceinline__ uint32_t ordered(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-// Larger key = larger value, then lower index.
-__device__ __forceinline__ uint64_t make_key(float v, int idx) {
-  return (static_cast<uint64_t>(ordered(v)) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(idx));
-}
-__device__ __forceinline__ int key_index(uint64_t k) {
-  return static_cast<int>(~static_cast<uint32_t>(k & 0xFFFFFFFFu));
-}
-
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   for (int o = 32; o > 0; o >>= 1) {
     const uint64_t w = __shfl_xor(v, o, 64);
@@ -177,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int
   }
   __syncthreads();
   for (int i = tid; i < N; i += kThreads) {
-    const int am = key_index(s_key[i]);
+    const int am = static_cast<int>(key_index(s_key[i]));
     s_am[i] = am;
     if (a.target_argmax) a.target_argmax[base + i] = am;
   }

@@ -103,17 +103,6 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2)
   m = M;
 }
 
-// Orders non-negative floats (and everything else) as unsigned integers.
-__device__ __forceinline__ uint32_t ordered(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-// Larger key = larger value, then lower index.
-__device__ __forceinline__ uint64_t make_key(float v, int idx) {
-  return (static_cast<uint64_t>(ordered(v)) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(idx));
-}
-
 __global__ __launch_bounds__(kThreads) void stoch_stats_kernel(const float* __restrict__ logits, int V,
                                                                float k2, int chunk, int chunks,
                                                                float2* __restrict__ stats) {

@@ -68,8 +68,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-#define LDS_AS __attribute__((address_space(3)))
-#define CONST_AS __attribute__((address_space(4)))
 
 constexpr int kTile = 32;             // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -160,28 +158,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 // in-flight LDS copies and would drain them all (vmcnt(0)) before it; the
 // caller instead waits with lds_wait_operands, which the copies into other
 // buffers never block.
+// The destination is an output bound to the caller's register (no value is
+// returned, so no temporary stands between the read and the wait).
 template <int OFF>
-__device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t addr) {
+__device__ __forceinline__ void ds_read_tr16_b64(u32x2& dst, uint32_t addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-  u32x2 v;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-  return v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF));
 }
-
-// One wave copies 64 x 16 bytes from a buffer (base, range in bytes;
-// per-lane byte offset) into LDS: lane l's bytes land at dst + 16 l.  Reads
-// past the range return zeros.  POLICY is the copy's cache policy: 0, or 2
-// (non-temporal) for data that no other workgroup reads again.  (A plain
-// device function: lambdas would also be compiled for the host, which has no
-// buffer resources.)
-template <int POLICY = 0>
-__device__ __forceinline__ void copy_to_lds(const char* base, int range, int voff, uint16_t* dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, range, 0x00020000),
-      (LDS_AS void*)dst, 16, voff, 0, 0, POLICY);
-}
-
-constexpr int kNonTemporal = 2;  // cache-policy bit of a buffer access (gfx950: nt)
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -191,16 +174,25 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// s_waitcnt lgkmcnt(0) taking the transpose-read results as operands, so no
-// use of them is scheduled above the wait (device-only: the register
-// constraints do not exist on the host side of the compilation).
-__device__ __forceinline__ void lds_wait_operands(u32x4 (&v)[2][4]) {
+// s_waitcnt lgkmcnt(0) taking the transpose-read destinations themselves as
+// operands, so that no use of them is scheduled above the wait.  The asm
+// reads' outputs are bound to exactly these registers and nothing is built
+// from them before the wait: the compiler takes an asm output as written when
+// the asm statement ends, so any copy or repacking of a destination placed
+// before the wait would read the register before the LDS data arrived.
+// (device-only: the register constraints do not exist on the host side of
+// the compilation)
+__device__ __forceinline__ void lds_wait_operands(u32x2 (&v)[2][4][2]) {
   asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]),
-                 "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]));
+               : "+v"(v[0][0][0]), "+v"(v[0][0][1]), "+v"(v[0][1][0]), "+v"(v[0][1][1]),
+                 "+v"(v[0][2][0]), "+v"(v[0][2][1]), "+v"(v[0][3][0]), "+v"(v[0][3][1]),
+                 "+v"(v[1][0][0]), "+v"(v[1][0][1]), "+v"(v[1][1][0]), "+v"(v[1][1][1]),
+                 "+v"(v[1][2][0]), "+v"(v[1][2][1]), "+v"(v[1][3][0]), "+v"(v[1][3][1]));
 }
-__device__ __forceinline__ void lds_wait_operands(u32x4 (&v)[2][2]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]), "+v"(v[1][1]));
+__device__ __forceinline__ void lds_wait_operands(u32x2 (&v)[2][2][2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0][0][0]), "+v"(v[0][0][1]), "+v"(v[0][1][0]), "+v"(v[0][1][1]),
+                 "+v"(v[1][0][0]), "+v"(v[1][0][1]), "+v"(v[1][1][0]), "+v"(v[1][1][1]));
 }
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding:
@@ -517,7 +509,8 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
           kop[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(
               static_cast<uintptr_t>(kaddr[kk & 3] + kNextBytes + (kk >> 2) * 128));
         // V^T operands of this tile, read now so the reads overlap the softmax
-        u32x4 vop[2][C::kDb];
+        // vtr[kc2][db][0 / 1]: keys 16 kc2 .. + 7 / 16 kc2 + 8 .. + 15
+        u32x2 vtr[2][C::kDb][2];
         static_for<0, 2>([&](auto kc2_c) {
           constexpr int kc2 = decltype(kc2_c)::value;
           static_for<0, C::kDb>([&](auto db_c) {
@@ -527,12 +520,8 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
             constexpr int kHi = kLo + 2 * 8 * D;
             // the offset field holds 16 bits: far stages step the base by 64 KB
             constexpr int kLoB = kLo >= 65536 ? 65536 : 0, kHiB = kHi >= 65536 ? 65536 : 0;
-            const u32x2 lo = ds_read_tr16_b64<kLo - kLoB>(vaddr[db & 1] + kLoB);
-            const u32x2 hi = ds_read_tr16_b64<kHi - kHiB>(vaddr[db & 1] + kHiB);
-            vop[kc2][db][0] = lo[0];
-            vop[kc2][db][1] = lo[1];
-            vop[kc2][db][2] = hi[0];
-            vop[kc2][db][3] = hi[1];
+            ds_read_tr16_b64<kLo - kLoB>(vtr[kc2][db][0], vaddr[db & 1] + kLoB);
+            ds_read_tr16_b64<kHi - kHiB>(vtr[kc2][db][1], vaddr[db & 1] + kHiB);
           });
         });
         if (tb + kTile > P) {  // the tile reaches the tree slots or the end: mask
@@ -580,15 +569,17 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
         // the transpose reads above are invisible to the compiler's wait
         // tracking: wait for them here, with their results as operands so that
         // no use can be scheduled above the wait
-        lds_wait_operands(vop);
-        // O^T += V^T P^T over the two 16-key chunks of the tile
+        lds_wait_operands(vtr);
+        // O^T += V^T P^T over the two 16-key chunks of the tile (the V^T
+        // operands are assembled from the transpose reads only now)
     #pragma unroll
         for (int kc2 = 0; kc2 < 2; ++kc2) {
           const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kc2]);
     #pragma unroll
-          for (int db = 0; db < C::kDb; ++db)
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[kc2][db]), pb,
-                                                              acc[db], 0, 0, 0);
+          for (int db = 0; db < C::kDb; ++db) {
+            const u32x4 vop = {vtr[kc2][db][0][0], vtr[kc2][db][0][1], vtr[kc2][db][1][0], vtr[kc2][db][1][1]};
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop), pb, acc[db], 0, 0, 0);
+          }
         }
     };
     // S^T of the piece's first tile

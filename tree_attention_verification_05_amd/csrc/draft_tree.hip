@@ -50,27 +50,6 @@ static_assert(kMaxChunks <= 64, "one lane per chunk in the row merge");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Orders floats as unsigned integers; -0.0 and +0.0 map to the same value.
-__device__ __forceinline__ uint32_t ordered(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float unordered(uint32_t o) {
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-// Larger key = larger value, then lower index.  Every key of a real entry is
-// nonzero; 0 marks "none".
-__device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
-  return (static_cast<uint64_t>(ordered(v)) << 32) | static_cast<uint32_t>(~idx);
-}
-__device__ __forceinline__ uint32_t key_index(uint64_t k) {
-  return ~static_cast<uint32_t>(k & 0xFFFFFFFFu);
-}
-__device__ __forceinline__ float key_value(uint64_t k) {
-  return unordered(static_cast<uint32_t>(k >> 32));
-}
-
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;

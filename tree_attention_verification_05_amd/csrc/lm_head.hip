@@ -35,7 +35,6 @@
 namespace tv {
 namespace {
 
-#define LDS_AS __attribute__((address_space(3)))
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -68,47 +67,24 @@ struct LCfg {
   __device__ static constexpr int swz(int r) { return BK == 64 ? (r & 7) : ((r >> 1) & 3); }
 };
 
-// Orders floats as unsigned integers; -0.0 and +0.0 map to the same value.
-__device__ __forceinline__ uint32_t ordered(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float unordered(uint32_t o) {
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-// Larger key = larger score, then lower index.
-__device__ __forceinline__ uint64_t make_key(float v, int idx) {
-  return (static_cast<uint64_t>(ordered(v)) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(idx));
-}
-
-// One wave copies 64 x 16 bytes from a buffer (base, range in bytes; per-lane
-// byte offset) into LDS: lane l's bytes land at dst + 16 l.  Reads past the
-// range return zeros.  POLICY: the copy's cache policy (0, or kNonTemporal
-// for data no other workgroup reads again).
-template <int POLICY = 0>
-__device__ __forceinline__ void copy_to_lds(const char* base, int range, int voff, uint16_t* dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, range, 0x00020000),
-      (LDS_AS void*)dst, 16, voff, 0, 0, POLICY);
-}
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ds_read_b128 as inline assembly at a byte address plus an immediate
 // offset.  The compiler cannot tell a plain LDS read from the LDS copies in
 // flight and would wait for all of them (vmcnt(0)) before it, which would
 // drain the prefetch; these reads are instead waited for by wait_operands.
+// The destination is an output bound to the caller's register: no value is
+// returned, so no temporary (whose copy the compiler could place before the
+// wait, reading the register before the data arrived) stands between the
+// read and its wait.
 template <int OFF>
-__device__ __forceinline__ u32x4 ds_read_b128(uint32_t addr) {
+__device__ __forceinline__ void ds_read_b128(u32x4& dst, uint32_t addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-  return v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF));
 }
 
-// s_waitcnt lgkmcnt(0) taking the operands of one hidden step as operands,
-// so no use of them is scheduled above the wait.
+// s_waitcnt lgkmcnt(0) taking the read destinations of one hidden step as
+// operands, so no use of them is scheduled above the wait.
 template <int CW, int RW>
 __device__ __forceinline__ void wait_operands(u32x4 (&w)[CW], u32x4 (&x)[RW]) {
   static_assert((CW == 2 || CW == 4) && (RW == 2 || RW == 4), "operand counts");
@@ -237,11 +213,11 @@ __global__ __launch_bounds__((LCfg<RW, CW, NWR, BK, STAGES>::kThreads)) void lmh
       const uint32_t ch = ((2 * s + ohalf) ^ oswz) * 16;
       static_for<0, CW>([&](auto cw_c) {
         constexpr int cw = decltype(cw_c)::value;
-        wvr[s & 1][cw] = ds_read_b128<cw * 32 * C::kRowBytes>(wrow + ch);
+        ds_read_b128<cw * 32 * C::kRowBytes>(wvr[s & 1][cw], wrow + ch);
       });
       static_for<0, RW>([&](auto rw_c) {
         constexpr int rw = decltype(rw_c)::value;
-        xv[s & 1][rw] = ds_read_b128<rw * 32 * C::kRowBytes>(arow + ch);
+        ds_read_b128<rw * 32 * C::kRowBytes>(xv[s & 1][rw], arow + ch);
       });
     };
     read_step(std::integral_constant<int, 0>{});
@@ -310,7 +286,6 @@ __global__ __launch_bounds__(kPickThreads) void lmhead_pick_kernel(LmArgs a, int
 
 int vocab_tiles(int V) { return (V + kBN - 1) / kBN; }
 
-constexpr int kNonTemporal = 2;  // cache-policy bit of a buffer access (gfx950: nt)
 
 template <int RW, int CW, int NWR, int BK, int STAGES>
 hipError_t launch_cfg(const LmArgs& a, uint64_t* keys, hipStream_t stream) {

@@ -36,6 +36,43 @@ __device__ __forceinline__ void report(int32_t* dev_status, int bits) {
   if (dev_status) atomicOr(dev_status, bits);
 }
 
+// ---- ordered 64-bit selection keys (one definition for every kernel that
+// picks a maximum with the lowest index winning ties) ----
+// Orders floats as unsigned integers; -0.0 and +0.0 map to the same value.
+__device__ __forceinline__ uint32_t ordered(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unordered(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+// Larger key = larger value, then lower index.  Every key of a finite value
+// is nonzero, so 0 can mark "none".
+__device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
+  return (static_cast<uint64_t>(ordered(v)) << 32) | static_cast<uint32_t>(~idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~static_cast<uint32_t>(k & 0xFFFFFFFFu); }
+__device__ __forceinline__ float key_value(uint64_t k) { return unordered(static_cast<uint32_t>(k >> 32)); }
+
+// ---- LDS copies straight from a buffer (gfx950 buffer_load ... lds) ----
+#define LDS_AS __attribute__((address_space(3)))
+#define CONST_AS __attribute__((address_space(4)))
+constexpr int kNonTemporal = 2;  // cache-policy bit of a buffer access (gfx950: nt)
+
+// One wave copies 64 x 16 bytes from a buffer (base, range in bytes;
+// per-lane byte offset) into LDS: lane l's bytes land at dst + 16 l.  Reads
+// past the range return zeros.  POLICY is the copy's cache policy: 0, or
+// kNonTemporal for data that no other workgroup reads again.  (A plain
+// device function: lambdas would also be compiled for the host, which has no
+// buffer resources.)
+template <int POLICY = 0>
+__device__ __forceinline__ void copy_to_lds(const char* base, int range, int voff, uint16_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, range, 0x00020000),
+      (LDS_AS void*)dst, 16, voff, 0, 0, POLICY);
+}
+
 // ---- launchers (each defined in its kernel translation unit) ----
 hipError_t launch_tree_mask(const int32_t* parents, int B, int N, uint64_t* mask, int32_t* depth,
                             int32_t* dev_status, hipStream_t stream);
