@@ -66,10 +66,41 @@ def attention_tolerance(dtype):
     return (2e-2, 1e-2) if dtype == torch.bfloat16 else (1e-4, 1e-4)
 
 
-def check_attention(gpu_out: torch.Tensor, ref: np.ndarray, seqs, dtype):
+def relative_l2_bound(dtype):
+    """Per-sequence bound on ||gpu - oracle||_2 / ||oracle||_2.
+
+    bf16: an output passes through at most three round-to-nearest-even bf16
+    roundings that the oracle does not make -- the softmax weights before the
+    P V product, the normalised partial state of a split key range, and the
+    final output.  Each has relative error at most 2^-8 and, over many
+    elements, a root-mean-square of at most 2^-8 / sqrt(3); three independent
+    ones give sqrt(3) * 2^-8 / sqrt(3) = 2^-8 = 3.9e-3, so 4e-3.  The
+    per-element bound alone is loose at long prefixes, where |out| shrinks as
+    1 / sqrt(prefix length) (about 0.01 at 32768 keys, half the absolute
+    tolerance): the relative L2 error is what shows a mis-weighted piece or a
+    dropped key there.
+    fp32: only summation order differs; 1e-5."""
+    return 4e-3 if dtype == torch.bfloat16 else 1e-5
+
+
+# worst relative L2 error per checked case, reported at the end of the run
+# (tests/conftest.py prints it and, if TV_PARITY_SUMMARY names a file, writes
+# it there as JSON)
+RESULTS = {}
+
+
+def record(label: str, **fields) -> None:
+    RESULTS.setdefault(label, {}).update(fields)
+
+
+def check_attention(gpu_out: torch.Tensor, ref: np.ndarray, seqs, dtype, label: str = ""):
+    """Element-wise tolerance and per-sequence relative L2 error against the
+    oracle on sequences ``seqs``; returns the worst relative L2 error."""
     atol, rtol = attention_tolerance(dtype)
+    rel_max = relative_l2_bound(dtype)
     g = host_f(gpu_out)
     worst = 0.0
+    worst_abs = 0.0
     for b in seqs:
         diff = np.abs(g[b] - ref[b])
         bound = atol + rtol * np.abs(ref[b])
@@ -77,10 +108,14 @@ def check_attention(gpu_out: torch.Tensor, ref: np.ndarray, seqs, dtype):
         if bad.any():
             idx = np.argwhere(bad)[0]
             raise AssertionError(
-                f"seq {b}: {int(bad.sum())} elements outside tolerance; first at node,head,dim="
+                f"{label} seq {b}: {int(bad.sum())} elements outside tolerance; first at node,head,dim="
                 f"{tuple(idx)}: gpu {g[b][tuple(idx)]} oracle {ref[b][tuple(idx)]}")
-        rel = np.linalg.norm(g[b] - ref[b]) / max(np.linalg.norm(ref[b]), 1e-30)
-        worst = max(worst, float(rel))
+        rel = float(np.linalg.norm(g[b] - ref[b]) / max(np.linalg.norm(ref[b]), 1e-30))
+        assert rel <= rel_max, f"{label} seq {b}: relative L2 error {rel:.3e} > {rel_max:.1e}"
+        worst = max(worst, rel)
+        worst_abs = max(worst_abs, float(diff.max()))
+    if label:
+        record(label, seqs=len(list(seqs)), rel_l2=worst, max_abs=worst_abs)
     return worst
 
 

@@ -111,8 +111,20 @@ def decision_margin(gen, parents, topk: int, depth: int, ignore_exact_ties: bool
 
 def check_valid(rows, parents, tokens, scores, N: int, topk: int, root_token: int):
     """Validity of a construction result whose decisions may differ from the
-    oracle's at near ties."""
+    oracle's at near ties.
+
+    Shape: a tree in level order whose every node is one of its parent row's
+    topk tokens, scored as its parent plus that token's log-probability, in
+    descending score order within each level.  Selection: every candidate is
+    regenerated from the tree's own frontiers (the first topk nodes of each
+    level, whose ranks name the drafter rows of the next level), and up to
+    SCORE_ATOL + DECISION_TOL
+      * no candidate left out of the tree scores above the lowest kept node
+        (the kept set is the best N - 1 of all generated nodes), and
+      * no candidate of a level outside that level's first topk nodes scores
+        above the topk-th of them (each frontier is its level's top-k)."""
     depth = rows.shape[0]
+    tol = SCORE_ATOL + DECISION_TOL
     assert parents[0] == -1 and tokens[0] == root_token and scores[0] == 0
     level = np.zeros(N, dtype=np.int64)
     for i in range(1, N):
@@ -120,19 +132,48 @@ def check_valid(rows, parents, tokens, scores, N: int, topk: int, root_token: in
         assert 0 <= p < i
         level[i] = level[p] + 1
         assert level[i] >= level[i - 1] and level[i] <= depth
-    base = {l: int(np.argmax(level == l)) for l in range(1, depth + 1) if (level == l).any()}
+    by_level = {l: [i for i in range(N) if level[i] == l] for l in range(depth + 1)}
+    lps = {}
+
+    def row_logp(l, j):
+        if (l, j) not in lps:
+            lps[l, j] = O.log_softmax(rows[l, j])
+        return lps[l, j]
+
     seen = set()
     for i in range(1, N):
         l, p = int(level[i]), int(parents[i])
-        j = 0 if l == 1 else p - base[l - 1]       # the parent's rank within its level
+        j = 0 if l == 1 else by_level[l - 1].index(p)       # the parent's rank within its level
         assert 0 <= j < topk
-        lp = O.log_softmax(rows[l - 1, j])
+        lp = row_logp(l - 1, j)
         assert tokens[i] in set(O.top_tokens(lp, topk).tolist())
         assert abs(scores[i] - (scores[p] + lp[tokens[i]])) <= SCORE_ATOL
         assert (p, int(tokens[i])) not in seen
         seen.add((p, int(tokens[i])))
         if i > 1 and level[i - 1] == l:
             assert scores[i] <= scores[i - 1] + SCORE_ATOL
+    if N == 1:
+        return
+    s_min = float(scores[1:].min())
+    for l in range(1, depth + 1):
+        frontier = [0] if l == 1 else by_level[l - 1][:topk]
+        cands = []
+        for j, p in enumerate(frontier):
+            lp = row_logp(l - 1, j)
+            for t in O.top_tokens(lp, topk):
+                cands.append((float(scores[p] + lp[t]), p, int(t)))
+        for sc, p, t in cands:
+            assert (p, t) in seen or sc <= s_min + tol, (
+                f"level {l}: candidate (parent {p}, token {t}) scores {sc:.6f}, left out of a tree "
+                f"whose lowest kept score is {s_min:.6f}")
+        nodes = by_level[l]
+        if len(nodes) >= topk:
+            kth = float(scores[nodes[topk - 1]])
+            top = {(int(parents[i]), int(tokens[i])) for i in nodes[:topk]}
+            for sc, p, t in cands:
+                assert (p, t) in top or sc <= kth + tol, (
+                    f"level {l}: candidate (parent {p}, token {t}) scores {sc:.6f} above the "
+                    f"frontier's lowest {kth:.6f}")
 
 
 def compare_sequence(rows, N, topk, root_token, gp, gt, gs, ignore_exact_ties=False) -> bool:
@@ -242,29 +283,24 @@ def test_draft_tree_repeated_top_values():
         compare_sequence(lg[b], N, topk, int(root[b]), gp[b], gt[b], gs[b], ignore_exact_ties=True)
 
 
-FULL = [(2, None), (3, [0, 5, 13, 21, 31]), (4, None), (5, [0, 1, 64, 127])]
-
-
 @pytest.mark.gpu
-@pytest.mark.parametrize("cfg,sample", FULL, ids=[f"config{c}" for c, _ in FULL])
-def test_draft_tree_parity_full_size(cfg, sample):
-    """The workloads at full size, in the launch the benchmark times; the
-    oracle checks a sample of the sequences."""
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_draft_tree_parity_full_size(cfg):
+    """The workloads at full size, in the launch the benchmark times; every
+    sequence is compared exactly where all its decisions are clear, and
+    checked for validity and selection (check_valid) where one is not."""
     spec = W.CONFIGS[cfg]
     x = W.draft_tree_inputs(spec, 0)
     lg = x["draft_logits"].numpy()
     root = x["root_tokens"].numpy()
     print(f"draft tree {spec.name}: shape {tuple(lg.shape)}", flush=True)
     gp, gt, gs = run_gpu(lg, spec.N, root)
-    seqs = range(spec.B) if sample is None else sample
     exact = [compare_sequence(lg[b], spec.N, x["topk"], int(root[b]), gp[b], gt[b], gs[b])
-             for b in seqs]
-    print(f"exactly compared {sum(exact)} of {len(exact)} sequences", flush=True)
-    assert sum(exact) >= (len(exact) + 1) // 2
-    # every sequence: a valid tree whose node 0 is the root token
-    assert (gp[:, 0] == -1).all() and (gt[:, 0] == root).all()
-    for b in range(spec.B):
-        assert ((gp[b, 1:] >= 0) & (gp[b, 1:] < np.arange(1, spec.N))).all()
+             for b in range(spec.B)]
+    print(f"exactly compared {sum(exact)} of {len(exact)} sequences; the rest hold near ties and "
+          f"passed the validity and selection checks", flush=True)
+    from gpu_util import record
+    record(f"draft_tree full{cfg}", seqs=len(exact), exact=sum(exact))
 
 
 @pytest.mark.gpu

@@ -1,19 +1,29 @@
 """GPU parity of tv_lm_head_argmax against the oracle.
 
-Scores are bf16 products summed in fp32 on the GPU and in float64 by the
-oracle.  Each row's best score must match the oracle's within
-1e-3 * (1 + |score|); the chosen index must equal the oracle's unless the
-oracle scores the GPU's choice within 2e-3 * (1 + |score|) of its own best
-(a near tie that fp32 rounding may flip), which at most one row per case
-may do.  Small cases compare every row; full-size workloads compare sampled
-rows, the oracle run over vocabulary slices to bound its float64 memory."""
+The GPU multiplies bf16 values (each product exact in fp32) and sums H of
+them in fp32; the oracle sums in float64.  The fp32 sum of H products x_i y_i
+differs from the exact one by at most lambda * sqrt(H) * u * sum |x_i y_i|
+(u = 2^-24) except with probability 2 exp(-lambda^2 / 2) per entry, whatever
+the summation order (the probabilistic bound of Higham and Mary, "A new
+approach to probabilistic rounding error analysis", 2019); lambda = 8 makes a
+false failure about 1e-14 per entry.  With tol(r, v) that bound for row r and
+vocabulary entry v:
+
+* the GPU's maximum score for row r must be within tol(r, g) of the oracle's
+  score of the GPU's choice g;
+* g must equal the oracle's choice o, unless the oracle scores them within
+  tol(r, g) + tol(r, o) of each other (a near tie that the fp32 rounding may
+  flip), which is reported.
+
+Every row of every case is compared, the full-size workloads included; the
+oracle runs over vocabulary slices to bound its float64 memory."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import log
+from gpu_util import log, record
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +48,17 @@ def oracle_rows(h_rows, w, slab=16384):
     return out
 
 
+LAMBDA = 8.0
+U32 = 2.0 ** -24
+
+
+def accumulation_tol(h_row: np.ndarray, w_rows: np.ndarray) -> np.ndarray:
+    """Probabilistic fp32 accumulation bound of the H-term dot products of
+    one hidden row with some weight rows (float64 inputs)."""
+    H = h_row.shape[0]
+    return LAMBDA * np.sqrt(H) * U32 * (np.abs(w_rows) @ np.abs(h_row))
+
+
 def check(hidden, weight, rows=None, label=""):
     """hidden [M, H] and weight [V, H] bf16 host tensors."""
     M, H = hidden.shape
@@ -47,23 +68,28 @@ def check(hidden, weight, rows=None, label=""):
     torch.cuda.synchronize()
     am, mx = am.cpu().numpy(), mx.cpu().numpy()
     rows = np.arange(M) if rows is None else np.asarray(rows)
-    h = hidden.float().numpy()[rows]
+    h = hidden.float().numpy()[rows].astype(np.float64)
     w = weight.float().numpy()
     sc = oracle_rows(h, w)
     ref_am = np.argmax(sc, axis=1)
-    ref_mx = sc[np.arange(len(rows)), ref_am]
-    np.testing.assert_array_less(np.abs(mx[rows] - ref_mx), 1e-3 * (1 + np.abs(ref_mx)))
-    differ = 0
+    near = []
     for i, r in enumerate(rows):
-        if am[r] == ref_am[i]:
-            continue
-        g = int(am[r])
+        g, o = int(am[r]), int(ref_am[i])
         assert 0 <= g < V, f"{label} row {r}: index {g} out of range"
-        gap = ref_mx[i] - sc[i, g]
-        assert gap <= 2e-3 * (1 + abs(ref_mx[i])), (
-            f"{label} row {r}: gpu {g} (oracle score {sc[i, g]:.6f}), oracle {ref_am[i]} ({ref_mx[i]:.6f})")
-        differ += 1
-    assert differ <= 1, f"{label}: {differ} rows differ at near ties"
+        tol_g, tol_o = accumulation_tol(h[i], w[[g, o]].astype(np.float64))
+        assert abs(float(mx[r]) - sc[i, g]) <= tol_g, (
+            f"{label} row {r}: gpu max {mx[r]:.7f}, oracle score of that entry {sc[i, g]:.7f}, "
+            f"bound {tol_g:.2e}")
+        if g == o:
+            continue
+        gap = sc[i, o] - sc[i, g]
+        assert gap <= tol_g + tol_o, (
+            f"{label} row {r}: gpu {g} (oracle score {sc[i, g]:.7f}), oracle {o} ({sc[i, o]:.7f}), "
+            f"gap {gap:.2e} > {tol_g + tol_o:.2e}")
+        near.append((int(r), g, o, float(gap)))
+    if near:
+        log(f"[lm_head] {label}: {len(near)} rows differ at near ties: {near[:5]}")
+    record(f"lm_head {label}", rows=len(rows), near_ties=len(near))
     return am, mx
 
 
@@ -111,18 +137,14 @@ def test_small_workload_feeds_greedy_acceptance():
     am, _ = T.tv_lm_head_argmax(hid.cuda(), wt.cuda())
     torch.cuda.synchronize()
     assert tuple(am.shape) == (s.B, s.N)
-    lg = O.lm_head_logits(hid.float().numpy().reshape(-1, hid.shape[-1]), wt.float().numpy())
-    ref = np.argmax(lg, axis=1).reshape(s.B, s.N)
-    assert (am.cpu().numpy() == ref).mean() > 0.99
+    am_flat, _ = check(hid.reshape(-1, hid.shape[-1]), wt, label="small2")
+    assert np.array_equal(am.cpu().numpy().reshape(-1), am_flat)
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_full_size(cfg):
     """The full workload's rows (B * N) against its LM head, in the launch
-    configuration the benchmark times; 12 sampled rows checked."""
+    configuration the benchmark times; every row checked."""
     spec = W.CONFIGS[cfg]
     hid, wt = W.lm_head_inputs(spec)
-    hid = hid.reshape(-1, hid.shape[-1])
-    M = hid.shape[0]
-    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(cfg).choice(M, 10, replace=False)]))
-    check(hid, wt, rows=rows, label=f"full{cfg}")
+    check(hid.reshape(-1, hid.shape[-1]), wt, label=f"full{cfg}")
