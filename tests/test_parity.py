@@ -349,3 +349,24 @@ def test_accept_workspace_reused_across_batch_sizes():
         torch.cuda.synchronize()
         ref = O.accept_greedy(w.logits.numpy(), w.draft_tokens, w.parents)
         check_accept(dict(accept_len=al, accepted_nodes=an, bonus=bt, argmax=am), ref)
+
+
+def test_accept_workspace_per_stream():
+    """Acceptance calls on two streams at once: each stream gets its own
+    cached workspace, and both results stay exact."""
+    from tree_attention_verification_05_amd import _lib
+    cases = [W.make_small(3, seed=11, dense=False), W.make_small(5, seed=12, dense=False)]
+    inputs = [(w.logits.cuda(), torch.from_numpy(w.draft_tokens).cuda(), torch.from_numpy(w.parents).cuda())
+              for w in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for s, x in zip(streams, inputs):
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            outs.append(T.tv_accept_greedy(*x))
+    torch.cuda.synchronize()
+    keys = {k for k in _lib._accept_ws if k[1] in (streams[0].cuda_stream, streams[1].cuda_stream) and k[2] == 0}
+    assert len(keys) == 2
+    for w, (al, an, bt, am) in zip(cases, outs):
+        ref = O.accept_greedy(w.logits.numpy(), w.draft_tokens, w.parents)
+        check_accept(dict(accept_len=al, accepted_nodes=an, bonus=bt, argmax=am), ref)

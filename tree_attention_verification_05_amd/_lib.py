@@ -127,17 +127,24 @@ def _tv_dtype(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-_accept_ws: Dict[Tuple[int, int], torch.Tensor] = {}
+_accept_ws: Dict[Tuple[int, int, int], torch.Tensor] = {}
 
 
 def accept_workspace(device: torch.device, nbytes: int, kind: int = 0) -> torch.Tensor:
     """A workspace for tv_accept_greedy (kind 0), tv_accept_stochastic
     (kind 1), tv_lm_head_argmax (kind 2) or tv_build_draft_tree (kind 3),
-    kept per device and kind and grown when a call needs more (the
-    library needs no initial contents: everything a call reads from it is
-    written earlier in the same call)."""
+    kept per device, current stream and kind, and grown when a call needs
+    more (the library needs no initial contents: everything a call reads from
+    it is written earlier in the same call).
+
+    One buffer per stream: calls on one stream run in order, so they may
+    share it; calls on different streams get different buffers, and a buffer
+    is only ever used on the stream that allocated it, which is the stream the
+    caching allocator orders its reuse against when a grown buffer replaces
+    it.  Callers that pass their own workspace to calls running concurrently
+    on several streams must pass one per stream."""
     idx = device.index if device.index is not None else torch.cuda.current_device()
-    key = (idx, kind)
+    key = (idx, torch.cuda.current_stream(idx).cuda_stream, kind)
     ws = _accept_ws.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
