@@ -34,8 +34,9 @@
  *     is t in [0, prefix_lens[b]); tree node i's key/value sit at
  *     t = prefix_lens[b] + i and must be written before tv_tree_attention.
  *   - All pointers are DEVICE pointers to caller-owned memory; the library
- *     allocates nothing and keeps no global mutable state.  Integers are
- *     int32 row-major.
+ *     allocates nothing and keeps no global mutable state, except the static
+ *     scratch buffer of tv_accept_greedy_noalloc (and the per-device address
+ *     of it, looked up once).  Integers are int32 row-major.
  *   - Every call checks its scalar arguments on the host, returns a status
  *     and, on TV_OK, has enqueued its kernels on `stream` (asynchronous; no
  *     host synchronisation).  On any error other than TV_ERR_LAUNCH nothing is
@@ -70,7 +71,10 @@ typedef enum {
   TV_ERR_UNSUPPORTED = 4, /* D not in {64, 128}, block_size != 16, or H % 64 != 0 */
   TV_ERR_ALIGN = 5,       /* q, out, cache, logits or workspace pointer not 16-byte aligned */
   TV_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the queried size */
-  TV_ERR_LAUNCH = 7       /* the HIP runtime reported an error at launch */
+  TV_ERR_LAUNCH = 7,      /* the HIP runtime reported an error at launch */
+  TV_ERR_TOO_LARGE = 8    /* the sizes need more scratch than
+                             TV_ACCEPT_NOALLOC_SCRATCH_BYTES (allocation-free
+                             variant only) */
 } tv_status;
 
 typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
@@ -187,6 +191,37 @@ TV_API tv_status tv_accept_greedy(const float* logits, const int32_t* draft_toke
                            int32_t* accepted_nodes, int32_t* bonus_token, int32_t* target_argmax,
                            void* workspace, size_t workspace_bytes, int32_t* dev_status,
                            hipStream_t stream);
+
+/* Scratch bytes the library holds, per GPU, for tv_accept_greedy_noalloc. */
+#define TV_ACCEPT_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+
+/*
+ * tv_accept_greedy_noalloc -- tv_accept_greedy for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation, arguments and
+ * outputs, without the workspace argument.  Its per-chunk keys live in a
+ * static scratch buffer of TV_ACCEPT_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends (its device address
+ * is looked up on the first call for a device; nothing is allocated by any
+ * call).  The outputs are bit-identical to tv_accept_greedy's.
+ *
+ *   stream  selects the GPU (the scratch of that stream's device is used).
+ * Calls whose sizes need more than the buffer holds
+ * (tv_accept_greedy_workspace_size(B, N, V) > TV_ACCEPT_NOALLOC_SCRATCH_BYTES,
+ * i.e. more than 524288 chunk keys: about half a million rows of logits) are
+ * refused with TV_ERR_TOO_LARGE.  Every call on one GPU shares that GPU's
+ * buffer: calls that may overlap on one GPU (different streams, or different
+ * host threads) race on it and must be ordered by the caller; calls on one
+ * stream are ordered already.
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_ALIGN, TV_ERR_TOO_LARGE,
+ * TV_ERR_LAUNCH (also when the buffer's address cannot be looked up).
+ * Device: as tv_accept_greedy.
+ */
+TV_API tv_status tv_accept_greedy_noalloc(const float* logits, const int32_t* draft_tokens,
+                                          const int32_t* parents, int32_t B, int32_t N, int32_t V,
+                                          int32_t* accept_len, int32_t* accepted_nodes,
+                                          int32_t* bonus_token, int32_t* target_argmax,
+                                          int32_t* dev_status, hipStream_t stream);
 
 /*
  * Workspace bytes tv_accept_stochastic needs (per-chunk row statistics, one

@@ -28,10 +28,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert lib.tv_status_string(s).decode().startswith(
             ["TV_OK", "TV_ERR_NULL", "TV_ERR_SHAPE", "TV_ERR_DTYPE", "TV_ERR_UNSUPPORTED",
-             "TV_ERR_ALIGN", "TV_ERR_WORKSPACE", "TV_ERR_LAUNCH"][s])
+             "TV_ERR_ALIGN", "TV_ERR_WORKSPACE", "TV_ERR_LAUNCH", "TV_ERR_TOO_LARGE"][s])
     assert lib.tv_version() >= 100
 
 
@@ -85,6 +85,25 @@ def test_accept_host_checks():
     need = lib.tv_accept_greedy_workspace_size(2, 8, 1000)
     assert need > 0
     assert call(ws=None) == 6 and call(wsb=need - 1) == 6
+
+
+def test_accept_noalloc_host_checks():
+    """The allocation-free variant's host checks, and its size limit: sizes
+    whose chunk keys exceed the static scratch are refused before anything
+    touches a device."""
+    f = lib.tv_accept_greedy_noalloc
+    args = lambda **kw: [kw.get("lg", P16), kw.get("dt", P16), kw.get("par", P16), kw.get("B", 2),
+                         kw.get("N", 8), kw.get("V", 1000), kw.get("al", P16), kw.get("an", P16),
+                         kw.get("bt", P16), None, None, None]
+    assert f(*args(lg=None)) == 1 and f(*args(al=None)) == 1 and f(*args(bt=None)) == 1
+    assert f(*args(B=0)) == 2 and f(*args(N=257)) == 2 and f(*args(V=0)) == 2
+    assert f(*args(lg=P16 + 4)) == 5
+    limit = T.TV_ACCEPT_NOALLOC_SCRATCH_BYTES
+    # 2048 sequences of 256 nodes: one key per row, 4 MiB exactly, still fits
+    assert lib.tv_accept_greedy_workspace_size(2048, 256, 1000) == limit
+    # one more sequence does not
+    assert lib.tv_accept_greedy_workspace_size(2049, 256, 1000) > limit
+    assert f(*args(B=2049, N=256)) == T.TV_ERR_TOO_LARGE
 
 
 def test_compact_host_checks():

@@ -6,6 +6,8 @@ names as the C ABI in ``include/tv.h``:
 * ``tv_build_tree_mask``  -- ancestor-or-self bitmask of every tree node
 * ``tv_tree_attention``   -- tree-masked attention over the paged prefix
 * ``tv_accept_greedy``    -- target argmax and the longest accepted path
+* ``tv_accept_greedy_noalloc`` -- the same without a workspace, for callers
+  that cannot allocate (a static per-GPU scratch buffer serves instead)
 * ``tv_accept_stochastic`` -- accepted path and bonus token at temperature
   > 0 (speculative sampling over the tree, random numbers passed in)
 * ``tv_kv_compact``       -- move the accepted path's K/V after the prefix
@@ -26,13 +28,16 @@ from ._lib import (  # noqa: F401
     TV_DEV_BAD_RANDOM,
     TV_DEV_BAD_TOKEN,
     TV_DEV_BAD_TREE,
+    TV_ACCEPT_NOALLOC_SCRATCH_BYTES,
     TV_DEV_UNSUPPORTED,
+    TV_ERR_TOO_LARGE,
     TV_F32,
     TV_MAX_NODES,
     TVError,
     header_functions,
     lib,
     tv_accept_greedy,
+    tv_accept_greedy_noalloc,
     tv_accept_stochastic,
     tv_build_draft_tree,
     tv_build_tree_mask,

@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libtv.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "tv.h")
 
 TV_OK = 0
+TV_ERR_TOO_LARGE = 8
+TV_ACCEPT_NOALLOC_SCRATCH_BYTES = 4 << 20
 TV_F32, TV_BF16 = 0, 1
 TV_DEV_BAD_TREE, TV_DEV_BAD_CACHE, TV_DEV_BAD_TOKEN = 1, 2, 4
 TV_DEV_BAD_RANDOM, TV_DEV_UNSUPPORTED = 8, 16
@@ -56,6 +58,8 @@ def _load() -> ctypes.CDLL:
         "tv_accept_greedy_workspace_size": (_c_size, [_c_i32] * 3),
         "tv_accept_greedy": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_ptr,
                                       _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr, _c_ptr]),
+        "tv_accept_greedy_noalloc": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_ptr,
+                                              _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
         "tv_accept_stochastic_workspace_size": (_c_size, [_c_i32] * 3),
         "tv_accept_stochastic": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32,
                                           _c_i32, _c_i32, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr,
@@ -252,6 +256,30 @@ def tv_accept_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, parents: 
         _ptr(accepted_nodes), _ptr(bonus_token), _ptr(target_argmax), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(dev_status), _stream(logits)))
     return accept_len, accepted_nodes, bonus_token, target_argmax
+
+
+def tv_accept_greedy_noalloc(logits: torch.Tensor, draft_tokens: torch.Tensor, parents: torch.Tensor,
+                             accept_len: torch.Tensor, accepted_nodes: torch.Tensor,
+                             bonus_token: torch.Tensor, target_argmax: Optional[torch.Tensor] = None,
+                             dev_status: Optional[torch.Tensor] = None) -> None:
+    """tv_accept_greedy without a workspace (the library's static scratch
+    serves instead) and without allocating: every output is the caller's.
+    logits fp32 [B, N, V]; draft_tokens, parents, accepted_nodes (and
+    target_argmax, if given) int32 [B, N]; accept_len, bonus_token int32 [B]."""
+    _dev(logits, "logits", torch.float32)
+    B, N, V = logits.shape
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, N))
+    _dev(parents, "parents", torch.int32, (B, N))
+    _dev(accept_len, "accept_len", torch.int32, (B,))
+    _dev(accepted_nodes, "accepted_nodes", torch.int32, (B, N))
+    _dev(bonus_token, "bonus_token", torch.int32, (B,))
+    if target_argmax is not None:
+        _dev(target_argmax, "target_argmax", torch.int32, (B, N))
+    if dev_status is not None:
+        _dev(dev_status, "dev_status", torch.int32)
+    _check("tv_accept_greedy_noalloc", lib.tv_accept_greedy_noalloc(
+        _ptr(logits), _ptr(draft_tokens), _ptr(parents), B, N, V, _ptr(accept_len),
+        _ptr(accepted_nodes), _ptr(bonus_token), _ptr(target_argmax), _ptr(dev_status), _stream(logits)))
 
 
 def tv_accept_stochastic(logits: torch.Tensor, draft_tokens: torch.Tensor, parents: torch.Tensor,

@@ -12,6 +12,8 @@
 // sequence's N rows to the target argmax, validate the tree and the draft
 // tokens, and find the longest accepted path (smallest node sequence among
 // equals).  The workspace needs no initialisation.
+#include <mutex>
+
 #include "tv_internal.h"
 
 namespace tv {
@@ -254,6 +256,49 @@ hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(accept_walk_kernel, dim3(a.B), dim3(kThreads), 0, stream, a, s.chunks);
   return hipGetLastError();
+}
+
+// ---------------- scratch of the allocation-free variant ----------------
+// tv_accept_greedy_noalloc keeps its scan keys in this file-scope device
+// array instead of a caller workspace.  Every GPU the library runs on holds
+// its own copy until the process ends.  In host code `scratch` names a host
+// stand-in, not device memory: the device address of each GPU's copy is
+// looked up once per device with that device current, and only that address
+// is handed to the kernels (as the workspace pointer of launch_accept).  The
+// keys need no initial contents (each one a call reads is written earlier in
+// the same call), so nothing is cleared between calls.
+static __device__ __align__(256) uint64_t scratch[kAcceptScratchBytes / sizeof(uint64_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t accept_static_scratch(hipStream_t stream, void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    int cur = 0;
+    hipError_t r = hipGetDevice(&cur);
+    const bool other = r == hipSuccess && cur != dev;
+    if (other) r = hipSetDevice(dev);
+    void* p = nullptr;
+    if (r == hipSuccess) r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (other) {
+      const hipError_t back = hipSetDevice(cur);
+      if (r == hipSuccess) r = back;
+    }
+    g_scratch_ptr[dev] = r == hipSuccess ? p : nullptr;
+    g_scratch_err[dev] = r;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev] != hipSuccess ? g_scratch_err[dev]
+                                          : (*ptr ? hipSuccess : hipErrorInvalidSymbol);
 }
 
 }  // namespace tv

@@ -27,6 +27,7 @@ const char* tv_status_string(tv_status s) {
     case TV_ERR_ALIGN: return "TV_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
     case TV_ERR_WORKSPACE: return "TV_ERR_WORKSPACE: workspace missing or too small";
     case TV_ERR_LAUNCH: return "TV_ERR_LAUNCH: kernel launch failed";
+    case TV_ERR_TOO_LARGE: return "TV_ERR_TOO_LARGE: the sizes need more scratch than the static buffer holds";
   }
   return "unknown tv_status";
 }
@@ -119,6 +120,33 @@ tv_status tv_accept_greedy(const float* logits, const int32_t* draft_tokens, con
   a.bonus_token = bonus_token;
   a.target_argmax = target_argmax;
   a.workspace = workspace;
+  a.dev_status = dev_status;
+  return launched(launch_accept(a, stream));
+}
+
+tv_status tv_accept_greedy_noalloc(const float* logits, const int32_t* draft_tokens, const int32_t* parents,
+                                   int32_t B, int32_t N, int32_t V, int32_t* accept_len,
+                                   int32_t* accepted_nodes, int32_t* bonus_token, int32_t* target_argmax,
+                                   int32_t* dev_status, hipStream_t stream) {
+  if (!logits || !draft_tokens || !parents || !accept_len || !accepted_nodes || !bonus_token)
+    return TV_ERR_NULL;
+  if (B <= 0 || N <= 0 || N > TV_MAX_NODES || V <= 0) return TV_ERR_SHAPE;
+  if (!aligned16(logits)) return TV_ERR_ALIGN;
+  if (accept_workspace_bytes(B, N, V) > kAcceptScratchBytes) return TV_ERR_TOO_LARGE;
+  void* scratch = nullptr;
+  if (accept_static_scratch(stream, &scratch) != hipSuccess) return TV_ERR_LAUNCH;
+  AcceptArgs a;
+  a.logits = logits;
+  a.draft_tokens = draft_tokens;
+  a.parents = parents;
+  a.B = B;
+  a.N = N;
+  a.V = V;
+  a.accept_len = accept_len;
+  a.accepted_nodes = accepted_nodes;
+  a.bonus_token = bonus_token;
+  a.target_argmax = target_argmax;
+  a.workspace = scratch;
   a.dev_status = dev_status;
   return launched(launch_accept(a, stream));
 }

@@ -115,6 +115,10 @@ struct AcceptArgs {
 };
 size_t accept_workspace_bytes(int B, int N, int V);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+// the allocation-free variant's static scratch: its size, and the device
+// address of the copy on the device of `stream` (looked up on first use)
+constexpr size_t kAcceptScratchBytes = TV_ACCEPT_NOALLOC_SCRATCH_BYTES;
+hipError_t accept_static_scratch(hipStream_t stream, void** ptr);
 
 struct StochArgs {
   const float* logits;
