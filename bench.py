@@ -5,10 +5,11 @@ attention over the paged prefix, greedy acceptance over the target logits,
 and KV compaction of the accepted paths, each one libtv call on the current
 stream.  Inputs are synthetic (seeded) and resident in HBM before timing.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--workloads 3,4,5]
 
 Prints ONE JSON line.  `value` is verified tree tokens per second
-(B * N / mean step time).  Before every timed step a 1 GiB read-only pass
+(B * N / mean step time) of the main workload (--config, default the
+Llama-3-8B-shaped layer).  Before every timed step a 1 GiB read-only pass
 over a scratch buffer evicts the 256 MB Infinity Cache and the L2 (outside
 the step's events), so every step reads its inputs from HBM; the flush only
 reads, so it leaves no dirty lines whose write-back would land inside the
@@ -17,14 +18,19 @@ with an event between every call gives the per-call times.  Compaction
 rewrites the tree slots in place; later steps accept the same paths and move
 the same number of rows, so the work per step is unchanged.
 
+The other workloads named by --workloads (default: the batched-serving,
+long-context and 70B-chain workloads, where the attention targets sit) are
+measured in the same run with the same protocol and reported under
+`workloads`, each with its attention roofline fraction against its target.
+
 The tree K/V write (rotary positions and paged append of the step's new
 rows, the path's upstream neighbour), stochastic acceptance (temperature
 > 0, the alternative to the greedy call) and the target's LM head fused with
 the greedy choice (bf16 hidden states and weight of the workload's model,
 hidden 4096 / 3584 / 8192) and the draft-tree construction that produces
 the step's parents and tokens (the drafter's scores of every level, fp32)
-are timed on their own, K calls after an eviction each, and reported under
-`extra_calls`; they are not part of `value`.
+are timed on the main workload on their own, K calls after an eviction each,
+and reported under `extra_calls`; they are not part of `value`.
 """
 from __future__ import annotations
 
@@ -62,6 +68,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="workload 1..5 (default 2: Llama-3-8B-shaped layer, EAGLE-2 60-node tree)")
+    ap.add_argument("--workloads", default="3,4,5",
+                    help="other workloads timed in the same run (comma list, or 'none')")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--oracle-seconds", type=float, default=12.0,
                     help="host time budget of the CPU-oracle baseline (0 disables it)")
@@ -118,6 +126,149 @@ def step_work(w, accept_len, accepted_nodes):
     }
 
 
+# the benchmark spec's attention targets: HBM fraction on the memory-bound workloads,
+# bf16 matrix-core fraction on the one above the ridge
+TARGETS = {3: ("hbm", 0.60), 4: ("mfma", 0.40), 5: ("hbm", 0.60)}
+STEP_CALLS = ["tv_build_tree_mask", "tv_tree_attention", "tv_accept_greedy", "tv_kv_compact"]
+TIME_BASE = ("mean HIP-event time of each call, events recorded on the launch stream around the "
+             "call's launches (for attention: main kernel, launch gap and merge kernel), one "
+             "eviction before every step")
+
+
+class StepBench:
+    """The four calls of one workload's step on device-resident inputs,
+    with its buffers allocated once."""
+
+    def __init__(self, T, W, cfg: int, seed: int, dev):
+        import torch
+        self.T, self.torch, self.dev = T, torch, dev
+        w = W.make_config(cfg, seed=seed)
+        self.w, self.spec = w, w.spec
+        B, N, V = w.spec.B, w.spec.N, w.spec.V
+        self.q, self.k, self.v = w.q.to(dev), w.k_cache.to(dev), w.v_cache.to(dev)
+        self.table = torch.from_numpy(w.block_table).to(dev)
+        self.prefix = torch.from_numpy(w.prefix_lens).to(dev)
+        self.parents = torch.from_numpy(w.parents).to(dev)
+        self.draft = torch.from_numpy(w.draft_tokens).to(dev)
+        self.logits = w.logits.to(dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        Wd = (N + 63) // 64
+        self.mask = torch.empty((B, N, Wd), dtype=torch.int64, device=dev)
+        self.depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(self.q)
+        self.dt = T.TV_BF16 if self.q.dtype == torch.bfloat16 else T.TV_F32
+        ws_bytes = T.tv_tree_attention_workspace_size(B, N, w.spec.Hq, w.spec.Hkv, w.spec.D,
+                                                      w.max_prefix_len, self.dt)
+        self.attn_ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        self.acc_len = torch.empty(B, dtype=torch.int32, device=dev)
+        self.acc_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.bonus = torch.empty(B, dtype=torch.int32, device=dev)
+        self.am = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.new_lens = torch.empty(B, dtype=torch.int32, device=dev)
+        self.acc_ws = torch.zeros(max(int(T.lib.tv_accept_greedy_workspace_size(B, N, V)), 16),
+                                  dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+
+    def run_step(self, ev=None):
+        T, st = self.T, self.stream
+        if ev is not None:
+            ev[0].record(st)
+        T.tv_build_tree_mask(self.parents, mask=self.mask, depth=self.depth, dev_status=self.status)
+        if ev is not None:
+            ev[1].record(st)
+        T.tv_tree_attention(self.q, self.k, self.v, self.table, self.prefix, self.w.max_prefix_len,
+                            self.mask, out=self.out, workspace=self.attn_ws, dev_status=self.status)
+        if ev is not None:
+            ev[2].record(st)
+        T.tv_accept_greedy(self.logits, self.draft, self.parents, accept_len=self.acc_len,
+                           accepted_nodes=self.acc_nodes, bonus_token=self.bonus,
+                           target_argmax=self.am, workspace=self.acc_ws, dev_status=self.status)
+        if ev is not None:
+            ev[3].record(st)
+        T.tv_kv_compact(self.k, self.v, self.table, self.prefix, self.acc_nodes, self.acc_len,
+                        new_lens=self.new_lens, dev_status=self.status)
+        if ev is not None:
+            ev[4].record(st)
+
+    def measure(self, steps: int, warmup: int, evict):
+        """W warm-up steps, then exactly K timed steps (one event pair each,
+        an eviction before each outside the events), then K more steps with
+        an event between every call.  Returns the per-workload record."""
+        import numpy as np
+        torch = self.torch
+        for _ in range(warmup):
+            self.run_step()
+        torch.cuda.synchronize()
+        if int(self.status.item()) != 0:
+            raise RuntimeError(f"device status {int(self.status.item())} on generated inputs")
+        step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        for s in range(steps):
+            evict()
+            step_ev[s][0].record(self.stream)
+            self.run_step()
+            step_ev[s][1].record(self.stream)
+        torch.cuda.synchronize()
+        self.t_wall = time.perf_counter() - t_wall
+        self.step_ms = np.array([step_ev[s][0].elapsed_time(step_ev[s][1]) for s in range(steps)])
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        for s in range(steps):
+            evict()
+            self.run_step(evs[s])
+        torch.cuda.synchronize()
+        self.per = np.array([[evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(4)]
+                             for s in range(steps)])  # ms
+        return self.record()
+
+    def record(self):
+        import numpy as np
+        spec, w = self.spec, self.w
+        B, N = spec.B, spec.N
+        ms = float(self.step_ms.mean())
+        al = self.acc_len.cpu().numpy()
+        work = step_work(w, al, self.acc_nodes.cpu().numpy())
+        kern = {}
+        for j, n in enumerate(STEP_CALLS):
+            t_us = float(self.per[:, j].mean()) * 1e3
+            byt = work[n]["bytes"]
+            kern[n] = {"us": round(t_us, 3), "us_median": round(float(np.median(self.per[:, j])) * 1e3, 3),
+                       "bytes": int(byt), "GB_s": round(byt / (t_us * 1e-6) / 1e9, 1)}
+            if work[n].get("flops"):
+                kern[n]["flops"] = int(work[n]["flops"])
+                kern[n]["TFLOP_s"] = round(work[n]["flops"] / (t_us * 1e-6) / 1e12, 2)
+                kern[n]["bound"] = work[n]["bound"]
+        a = kern["tv_tree_attention"]
+        a["hbm_frac"] = round(a["GB_s"] / HBM_PEAK_GBS, 4)
+        a["mfma_frac"] = round(a["TFLOP_s"] / BF16_PEAK_TFLOPS, 4)
+        a["frac"] = a["mfma_frac"] if a["bound"] == "mfma" else a["hbm_frac"]
+        a["traffic"] = measured_traffic("tv_tree_attention", spec.name)
+        # acceptance statistics of the step (the pages' evaluation reports the
+        # mean acceptance length and the accepted count per draft position)
+        depth_max = int(al.max()) if B else 0
+        per_depth = [int((al >= d).sum()) for d in range(1, max(depth_max, 1) + 1)]
+        return {
+            "workload": spec.name, "batch": B, "tree_nodes": N, "q_heads": spec.Hq,
+            "kv_heads": spec.Hkv, "head_dim": spec.D, "vocab": spec.V,
+            "prefix_len": [int(w.prefix_lens.min()), int(w.prefix_lens.max())],
+            "ms_per_step": round(ms, 5),
+            "ms_per_step_median": round(float(np.median(self.step_ms)), 5),
+            "ms_per_step_min": round(float(self.step_ms.min()), 5),
+            "tree_tokens_per_s": round(B * N / (ms * 1e-3), 1),
+            "accepted_tokens_per_s": round(float((al + 1).sum()) / (ms * 1e-3), 1),
+            "mean_accept_len": round(float(al.mean()), 4),
+            "accepted_per_depth": per_depth,
+            "kernels": kern,
+            "dtype": "bf16" if self.dt == self.T.TV_BF16 else "f32",
+        }
+
+    def free(self):
+        for n in list(vars(self)):
+            if isinstance(getattr(self, n), self.torch.Tensor):
+                delattr(self, n)
+        self.torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -133,88 +284,21 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = W.make_config(args.config, seed=args.seed)
-    spec = w.spec
-    B, N, V = spec.B, spec.N, spec.V
-
-    q, k, v = w.q.to(dev), w.k_cache.to(dev), w.v_cache.to(dev)
-    table = torch.from_numpy(w.block_table).to(dev)
-    prefix = torch.from_numpy(w.prefix_lens).to(dev)
-    parents = torch.from_numpy(w.parents).to(dev)
-    draft = torch.from_numpy(w.draft_tokens).to(dev)
-    logits = w.logits.to(dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-    Wd = (N + 63) // 64
-    mask = torch.empty((B, N, Wd), dtype=torch.int64, device=dev)
-    depth = torch.empty((B, N), dtype=torch.int32, device=dev)
-    out = torch.empty_like(q)
-    dt = T.TV_BF16 if q.dtype == torch.bfloat16 else T.TV_F32
-    ws_bytes = T.tv_tree_attention_workspace_size(B, N, spec.Hq, spec.Hkv, spec.D,
-                                                  w.max_prefix_len, dt)
-    attn_ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    acc_len = torch.empty(B, dtype=torch.int32, device=dev)
-    acc_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
-    bonus = torch.empty(B, dtype=torch.int32, device=dev)
-    am = torch.empty((B, N), dtype=torch.int32, device=dev)
-    new_lens = torch.empty(B, dtype=torch.int32, device=dev)
-    acc_ws = torch.zeros(max(int(T.lib.tv_accept_greedy_workspace_size(B, N, V)), 16),
-                         dtype=torch.uint8, device=dev)
     flush = None if args.no_flush else torch.empty(256 * 1024 * 1024, dtype=torch.float32,
                                                    device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def run_step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        T.tv_build_tree_mask(parents, mask=mask, depth=depth, dev_status=status)
-        if ev is not None:
-            ev[1].record(stream)
-        T.tv_tree_attention(q, k, v, table, prefix, w.max_prefix_len, mask, out=out,
-                            workspace=attn_ws, dev_status=status)
-        if ev is not None:
-            ev[2].record(stream)
-        T.tv_accept_greedy(logits, draft, parents, accept_len=acc_len, accepted_nodes=acc_nodes,
-                           bonus_token=bonus, target_argmax=am, workspace=acc_ws,
-                           dev_status=status)
-        if ev is not None:
-            ev[3].record(stream)
-        T.tv_kv_compact(k, v, table, prefix, acc_nodes, acc_len, new_lens=new_lens,
-                        dev_status=status)
-        if ev is not None:
-            ev[4].record(stream)
-
-    for _ in range(args.warmup):
-        run_step()
-    torch.cuda.synchronize()
-    if int(status.item()) != 0:
-        raise RuntimeError(f"device status {int(status.item())} on generated inputs")
 
     def evict():
         if flush is not None:
             flush.sum()  # reads 1 GiB, writes a scalar
 
-    # ---- timed region: exactly K steps, each after an eviction outside its events ----
-    step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    for s in range(args.steps):
-        evict()
-        step_ev[s][0].record(stream)
-        run_step()
-        step_ev[s][1].record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    step_ms = np.array([step_ev[s][0].elapsed_time(step_ev[s][1]) for s in range(args.steps)])
-    ms_per_step = float(step_ms.mean())
-
-    # ---- per-call times: K more steps with events between the calls ----
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for s in range(args.steps):
-        evict()
-        run_step(evs[s])
-    torch.cuda.synchronize()
-    per = np.array([[evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(4)]
-                    for s in range(args.steps)])  # ms
+    sb = StepBench(T, W, args.config, args.seed, dev)
+    w, spec = sb.w, sb.spec
+    B, N, V = spec.B, spec.N, spec.V
+    main_rec = sb.measure(args.steps, args.warmup, evict)
+    ms_per_step = main_rec["ms_per_step"]
+    stream = sb.stream
+    q, k, v, depth, table, prefix, status = sb.q, sb.k, sb.v, sb.depth, sb.table, sb.prefix, sb.status
+    logits, parents, dt = sb.logits, sb.parents, sb.dt
 
     # ---- the tree K/V write (the step's upstream neighbour, before the mask
     # and attention): timed on its own, K calls after an eviction each ----
@@ -234,6 +318,7 @@ def main():
         kvw_ev[s][1].record(stream)
     torch.cuda.synchronize()
     kvw_ms = np.array([e[0].elapsed_time(e[1]) for e in kvw_ev])
+    del k_new, v_new, q_rot
 
     # ---- stochastic acceptance (temperature > 0), the alternative to the
     # greedy call: timed on its own, K calls after an eviction each; chains
@@ -266,6 +351,7 @@ def main():
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item())} after the stochastic call")
     s_al_h = s_al.cpu().numpy()
+    del s_tok, s_u, s_e, s_q, s_ws
 
     # ---- the target's LM head fused with the greedy choice (upstream of the
     # acceptance walk; the [B, N, V] scores are never written) ----
@@ -311,13 +397,13 @@ def main():
         dt_ev[s][1].record(stream)
     torch.cuda.synchronize()
     dt_ms = np.array([e[0].elapsed_time(e[1]) for e in dt_ev])
-    del d_lg
+    del d_lg, d_ws
 
     # back-to-back steps with warm caches, for reference
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
-        run_step()
+        sb.run_step()
     e1.record(stream)
     torch.cuda.synchronize()
     warm_ms = e0.elapsed_time(e1) / args.steps
@@ -329,19 +415,9 @@ def main():
         for _ in range(3):
             torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
+        del src, dst
 
-    names = ["tv_build_tree_mask", "tv_tree_attention", "tv_accept_greedy", "tv_kv_compact"]
-    work = step_work(w, acc_len.cpu().numpy(), acc_nodes.cpu().numpy())
-    kern = {}
-    for j, n in enumerate(names):
-        t_us = float(per[:, j].mean()) * 1e3
-        byt = work[n]["bytes"]
-        kern[n] = {"us": round(t_us, 3), "us_median": round(float(np.median(per[:, j])) * 1e3, 3),
-                   "bytes": int(byt),
-                   "GB_s": round(byt / (t_us * 1e-6) / 1e9, 1)}
-        if work[n].get("flops"):
-            kern[n]["flops"] = int(work[n]["flops"])
-            kern[n]["TFLOP_s"] = round(work[n]["flops"] / (t_us * 1e-6) / 1e12, 2)
+    kern = main_rec["kernels"]
 
     # the tree K/V write, outside the step: its own time and algorithmic bytes
     elt = 2 if dt == T.TV_BF16 else 4
@@ -395,8 +471,9 @@ def main():
         "frac": round(dt_bytes / (dt_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bound": "hbm",
         "depth": dx["depth"], "topk": dx["topk"], "rows": int(dt_rows), "in_step": False}
 
-    # roofline of the dominant call
-    dom = max(names, key=lambda n: kern[n]["us"])
+    # roofline of the dominant call of the main workload's step
+    work = step_work(w, sb.acc_len.cpu().numpy(), sb.acc_nodes.cpu().numpy())
+    dom = max(STEP_CALLS, key=lambda n: kern[n]["us"])
     d_us = kern[dom]["us"]
     bound = work[dom].get("bound", "hbm")
     if bound == "mfma":
@@ -407,38 +484,78 @@ def main():
         achieved = work[dom]["bytes"] / (d_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = dom
     roof["traffic"] = measured_traffic(dom, spec.name)
+    roof["kernel"] = dom
+    roof["time_base"] = TIME_BASE
 
+    main_tokens = main_rec.pop("tree_tokens_per_s")
     result = {
         "metric": METRIC,
-        "value": round(B * N / (ms_per_step * 1e-3), 1),
+        "value": main_tokens,
         "unit": "tree-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "ms_per_step_median": round(float(np.median(step_ms)), 5),
-        "ms_per_step_min": round(float(step_ms.min()), 5),
+        "ms_per_step": ms_per_step,
+        "ms_per_step_median": main_rec.pop("ms_per_step_median"),
+        "ms_per_step_min": main_rec.pop("ms_per_step_min"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dt == T.TV_BF16 else "f32",
+        "dtype": main_rec.pop("dtype"),
         "data": "synthetic",
         "config": {"workload": spec.name, "batch": B, "tree_nodes": N, "q_heads": spec.Hq,
                    "kv_heads": spec.Hkv, "head_dim": spec.D, "vocab": V,
-                   "prefix_len": [int(w.prefix_lens.min()), int(w.prefix_lens.max())],
+                   "prefix_len": main_rec["prefix_len"],
                    "block_size": spec.block_size, "cache_flushed_between_steps": flush is not None},
         "roofline": roof,
         "kernels": kern,
+        "accepted_tokens_per_s": main_rec["accepted_tokens_per_s"],
+        "mean_accept_len": main_rec["mean_accept_len"],
+        "accepted_per_depth": main_rec["accepted_per_depth"],
         "extra_calls": extra,
         "warm_cache_ms_per_step": round(warm_ms, 5),
-        "wall_s_timed_region": round(t_wall, 4),
-        "mean_accept_len": float(acc_len.float().mean().item()),
+        "wall_s_timed_region": round(sb.t_wall, 4),
     }
+    w_main = w
+    sb.free()
+    del logits, parents, q, k, v, depth, table, prefix, status
+
+    # ---- the other workloads, same protocol, same run ----
+    others = {}
+    for cfg in parse_workloads(args.workloads, args.config):
+        t0 = time.perf_counter()
+        ob = StepBench(T, W, cfg, args.seed, dev)
+        rec = ob.measure(args.steps, args.warmup, evict)
+        ob.free()
+        del ob
+        if cfg in TARGETS:
+            bnd, tgt = TARGETS[cfg]
+            a = rec["kernels"]["tv_tree_attention"]
+            got = a["hbm_frac"] if bnd == "hbm" else a["mfma_frac"]
+            rec["attention_target"] = {"bound": bnd, "frac": tgt, "achieved_frac": got, "met": got >= tgt}
+        rec["wall_s"] = round(time.perf_counter() - t0, 2)
+        others[str(cfg)] = rec
+    if others:
+        result["workloads"] = others
+        result["workloads_time_base"] = TIME_BASE
+
     if args.oracle_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(w, args.oracle_seconds)
+        result["cpu_baseline"] = cpu_baseline(w_main, args.oracle_seconds)
     print(json.dumps(result), flush=True)
+
+
+def parse_workloads(text: str, main_cfg: int):
+    if not text or text.lower() == "none":
+        return []
+    out = []
+    for tok in text.split(","):
+        c = int(tok)
+        if c not in (1, 2, 3, 4, 5):
+            raise SystemExit(f"--workloads: no workload {c}")
+        if c != main_cfg and c not in out:
+            out.append(c)
+    return out
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -495,7 +612,21 @@ def cpu_baseline(w, seconds: float):
             "kind": "oracle",
             "sample": f"{done_steps} single-sequence passes (mask, attention, acceptance, "
                       f"compaction) of the same workload in {el:.1f} s, float64 NumPy",
-            "host_cpus": os.cpu_count()}
+            "precision": "float64 (inputs are the same bf16 values, upcast exactly)",
+            "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":
