@@ -49,15 +49,17 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "tree_attention_verification_05_amd", "csrc")
+# the sources each call's kernels are built from (the shared device helpers
+# included): counter runs taken on other sources are not reported
 KERNEL_SOURCES = {
-    "tv_tree_attention": ["attn_mfma.hip"],
-    "tv_accept_greedy": ["accept.hip"],
-    "tv_kv_compact": ["kv_compact.hip"],
-    "tv_build_tree_mask": ["tree_mask.hip"],
-    "tv_tree_kv_write": ["tree_kv_write.hip"],
-    "tv_accept_stochastic": ["accept_stochastic.hip"],
-    "tv_lm_head_argmax": ["lm_head.hip"],
-    "tv_build_draft_tree": ["draft_tree.hip"],
+    "tv_tree_attention": ["attn_mfma.hip", "attn_rowwave.hip", "tv_internal.h"],
+    "tv_accept_greedy": ["accept.hip", "tv_internal.h"],
+    "tv_kv_compact": ["kv_compact.hip", "tv_internal.h"],
+    "tv_build_tree_mask": ["tree_mask.hip", "tv_internal.h"],
+    "tv_tree_kv_write": ["tree_kv_write.hip", "tv_internal.h"],
+    "tv_accept_stochastic": ["accept_stochastic.hip", "tv_internal.h"],
+    "tv_lm_head_argmax": ["lm_head.hip", "tv_internal.h"],
+    "tv_build_draft_tree": ["draft_tree.hip", "tv_internal.h"],
 }
 
 
