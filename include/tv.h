@@ -27,9 +27,13 @@
  *     vocab V.  W = ceil(N / 64) mask words per node.
  *   - parents[b][0] == -1 and 0 <= parents[b][i] < i for i >= 1.
  *   - Paged K/V cache: k_cache and v_cache are [num_blocks][Hkv][block_size][D]
- *     row-major (within a block, the block_size slots of KV head 0, then of
- *     head 1, ...: one head's keys of a block are one contiguous run).
- *     Logical position t of sequence b lives in block
+ *     row-major by default (head-major: within a block, the block_size slots
+ *     of KV head 0, then of head 1, ...: one head's keys of a block are one
+ *     contiguous run), or [num_blocks][block_size][Hkv][D] (token-major: a
+ *     slot's Hkv heads together) when the calls that take a cache get
+ *     TV_KV_TOKEN_MAJOR OR'd into their dtype argument.  Both hold the same
+ *     rows; head-major lets one copy instruction fetch a head's keys in one
+ *     contiguous run.  Logical position t of sequence b lives in block
  *     block_table[b][t / block_size], slot t % block_size.  Sequence b's prefix
  *     is t in [0, prefix_lens[b]); tree node i's key/value sit at
  *     t = prefix_lens[b] + i and must be written before tv_tree_attention.
@@ -67,7 +71,8 @@ typedef enum {
   TV_ERR_NULL = 1,        /* a required pointer is NULL */
   TV_ERR_SHAPE = 2,       /* a size <= 0, Hq % Hkv != 0, N > TV_MAX_NODES, or the
                              block table cannot hold max_prefix_len + N positions */
-  TV_ERR_DTYPE = 3,       /* dtype is neither TV_F32 nor TV_BF16 */
+  TV_ERR_DTYPE = 3,       /* dtype (without TV_KV_TOKEN_MAJOR) is neither TV_F32 nor
+                             TV_BF16, or the flag is given to a call without a cache */
   TV_ERR_UNSUPPORTED = 4, /* D not in {64, 128}, block_size != 16, or H % 64 != 0 */
   TV_ERR_ALIGN = 5,       /* q, out, cache, logits or workspace pointer not 16-byte aligned */
   TV_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the queried size */
@@ -78,6 +83,12 @@ typedef enum {
 } tv_status;
 
 typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+
+/* Cache-layout flag for the dtype argument of tv_tree_attention,
+ * tv_kv_compact and tv_tree_kv_write: the caches are token-major
+ * [num_blocks][block_size][Hkv][D] instead of head-major
+ * [num_blocks][Hkv][block_size][D].  Pass (tv_dtype)(TV_BF16 | TV_KV_TOKEN_MAJOR). */
+#define TV_KV_TOKEN_MAJOR 0x100
 
 /* device status bits */
 #define TV_DEV_BAD_TREE 1   /* parents[b][0] != -1 or parents[b][i] not in [0, i) */
@@ -111,13 +122,14 @@ TV_API tv_status tv_build_tree_mask(const int32_t* parents, int32_t B, int32_t N
                              int32_t* depth, int32_t* dev_status, hipStream_t stream);
 
 /*
- * Workspace bytes tv_tree_attention needs for these sizes (0 when the key
- * range is not split).  The workspace holds the split schedule and the
- * partial softmax state of every split (row maxima and sums in fp32, the
- * normalised partial outputs in bf16), and needs no initialisation.
+ * Workspace bytes tv_tree_attention needs for these sizes, either dtype and
+ * either cache layout (0 when the key range is not split; the fp32 path uses
+ * none).  The workspace holds the split schedule and the partial softmax
+ * state of every split (row maxima and sums in fp32, the normalised partial
+ * outputs in bf16), and needs no initialisation.
  */
 TV_API size_t tv_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                                        int32_t max_prefix_len, tv_dtype dtype);
+                                        int32_t max_prefix_len);
 
 /*
  * tv_tree_attention -- tree-masked attention of every draft node over the
@@ -132,15 +144,16 @@ TV_API size_t tv_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq,
  *   out[b][i][h] = sum_t softmax_t(scale * <q[b][i][h], k[t][kh]>) * v[t][kh].
  *
  *   q            [B][N][Hq][D], dtype, device, 16-byte aligned.
- *   k_cache, v_cache  [num_blocks][Hkv][block_size][D], dtype, device, 16-byte
- *                aligned; read only.
+ *   k_cache, v_cache  [num_blocks][Hkv][block_size][D] (or token-major, see
+ *                TV_KV_TOKEN_MAJOR), dtype, device, 16-byte aligned; read only.
  *   block_table  [B][max_blocks] int32, device.
  *   prefix_lens  [B] int32, device; every entry <= max_prefix_len (host int).
  *   mask         [B][N][W] uint64, device (as written by tv_build_tree_mask).
  *   out          [B][N][Hq][D], dtype, device, 16-byte aligned, written.
  *   scale        softmax scale; <= 0 selects 1/sqrt(D).
  *   dtype        TV_BF16 (fp32 accumulation, bf16 output rounded to nearest
- *                even) or TV_F32 (fp32 throughout).
+ *                even) or TV_F32 (fp32 throughout), optionally OR'd with
+ *                TV_KV_TOKEN_MAJOR.
  *   workspace    device buffer of at least
  *                tv_tree_attention_workspace_size(...) bytes, 16-byte aligned
  *                (may be NULL if that size is 0).
@@ -327,7 +340,8 @@ TV_API tv_status tv_lm_head_argmax(const void* hidden, const void* weight, int32
  * their bytes.  The path must be strictly increasing and start at node 0 (as
  * tv_accept_greedy writes it).
  *
- *   k_cache, v_cache  [num_blocks][Hkv][block_size][D], dtype, device, 16-byte
+ *   k_cache, v_cache  [num_blocks][Hkv][block_size][D] (or token-major with
+ *                     TV_KV_TOKEN_MAJOR in dtype), dtype, device, 16-byte
  *                     aligned, updated in place.
  *   new_lens          [B] int32, written (may be NULL): P_b + L.
  * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_DTYPE, TV_ERR_UNSUPPORTED,
@@ -366,6 +380,7 @@ TV_API tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks,
  *                 may be q itself (in place).
  *   k_cache, v_cache, block_table, prefix_lens: as for tv_tree_attention;
  *                 the caches are updated in place.
+ *   dtype         TV_BF16 or TV_F32, optionally OR'd with TV_KV_TOKEN_MAJOR.
  *   rope_theta    rotary base (> 0), e.g. 500000 for Llama 3.
  * Errors: TV_ERR_NULL, TV_ERR_SHAPE (also rope_theta <= 0), TV_ERR_DTYPE,
  * TV_ERR_UNSUPPORTED, TV_ERR_ALIGN, TV_ERR_LAUNCH.  Device: TV_DEV_BAD_TREE

@@ -56,6 +56,8 @@ def attn(**kw):
 def test_attention_host_checks():
     assert attn(q=None) == 1 and attn(mask=None) == 1 and attn(out=None) == 1
     assert attn(dt=7) == 3
+    # the layout flag combines with a dtype; other bits do not
+    assert attn(dt=0x200 | 1) == 3 and attn(dt=0x100 | 7) == 3
     assert attn(Hq=6, Hkv=4) == 2 and attn(B=0) == 2 and attn(N=300) == 2
     assert attn(mpl=57) == 2          # 57 + 8 > 4 blocks * 16
     assert attn(D=96) == 4 and attn(bs=32) == 4
@@ -63,7 +65,7 @@ def test_attention_host_checks():
 
 
 def test_attention_workspace_check():
-    need = lib.tv_tree_attention_workspace_size(4, 64, 28, 4, 128, 32768, 1)
+    need = lib.tv_tree_attention_workspace_size(4, 64, 28, 4, 128, 32768)
     if need:
         assert attn(B=4, N=64, Hq=28, Hkv=4, mpl=32768, mb=2100, ws=None, wsb=0) == 6
         assert attn(B=4, N=64, Hq=28, Hkv=4, mpl=32768, mb=2100, ws=P16, wsb=need - 1) == 6
@@ -116,7 +118,7 @@ def test_compact_host_checks():
         return f(a["k"], a["v"], a["nb"], a["table"], a["mb"], a["bs"], a["pl"], a["an"], a["al"],
                  a["B"], a["N"], a["Hkv"], a["D"], a["dt"], a["nl"], a["st"], a["s"])
     assert call(k=None) == 1 and call(an=None) == 1
-    assert call(dt=2) == 3
+    assert call(dt=2) == 3 and call(dt=0x100 | 2) == 3 and call(dt=0x400 | 1) == 3
     assert call(N=0) == 2 and call(Hkv=0) == 2
     assert call(D=80) == 4 and call(bs=8) == 4
     assert call(v=P16 + 2) == 5
@@ -178,6 +180,8 @@ def test_lm_head_host_checks():
         return f(a["h"], a["w"], a["M"], a["H"], a["V"], a["dt"], a["am"], a["mx"], a["ws"], a["wsb"], a["s"])
     assert call(h=None) == 1 and call(w=None) == 1 and call(am=None) == 1
     assert call(dt=0) == 3
+    # the cache-layout flag belongs to the calls that take a cache
+    assert call(dt=0x100 | 1) == 3
     assert call(M=0) == 2 and call(V=0) == 2 and call(H=0) == 2 and call(H=1 << 21) == 2
     assert call(H=4000) == 4
     assert call(h=P16 + 2) == 5 and call(w=P16 + 8) == 5

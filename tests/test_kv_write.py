@@ -39,7 +39,12 @@ def _close(gpu, ref, dtype, what):
         raise AssertionError(f"{what}: {int(bad.sum())} elements off; first {idx}: gpu {g[idx]} oracle {ref[idx]}")
 
 
-def check_write(w, in_place=False, label=""):
+def _swap_layout(t: torch.Tensor) -> torch.Tensor:
+    """[num_blocks, Hkv, 16, D] <-> [num_blocks, 16, Hkv, D]."""
+    return t.permute(0, 2, 1, 3).contiguous()
+
+
+def check_write(w, in_place=False, label="", token_major=False):
     s = w.spec
     theta = W.rope_theta(s)
     k_new, v_new = W.tree_kv_inputs(s)
@@ -52,8 +57,16 @@ def check_write(w, in_place=False, label=""):
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     _, depth = T.tv_build_tree_mask(torch.from_numpy(w.parents).to(dev))
     q_out = q if in_place else None
-    qo = T.tv_tree_kv_write(q, k_new.to(dev), v_new.to(dev), depth, kc, vc, table, prefix, theta,
-                            q_out=q_out, dev_status=status)
+    if token_major:
+        # the call writes token-major caches; the checks below read them back
+        # in head-major order
+        kt, vt = _swap_layout(kc), _swap_layout(vc)
+        qo = T.tv_tree_kv_write(q, k_new.to(dev), v_new.to(dev), depth, kt, vt, table, prefix, theta,
+                                q_out=q_out, dev_status=status, token_major=True)
+        kc, vc = _swap_layout(kt), _swap_layout(vt)
+    else:
+        qo = T.tv_tree_kv_write(q, k_new.to(dev), v_new.to(dev), depth, kc, vc, table, prefix, theta,
+                                q_out=q_out, dev_status=status)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     q_rot, k_rot, pos = O.tree_kv_write(w.q.float().numpy(), k_new.float().numpy(), w.parents,
@@ -86,6 +99,13 @@ def test_small_configs(i):
 @pytest.mark.parametrize("i", [2, 3, 4, 5])
 def test_full_configs(i):
     check_write(W.make_config(i), label=f"full{i}")
+
+
+@pytest.mark.parametrize("i", [1, 3])
+def test_token_major_caches(i):
+    """Token-major caches ([num_blocks, 16, Hkv, D]): the same rows written,
+    every other byte kept (fp32 and bf16)."""
+    check_write(W.make_small(i), label=f"small{i} token-major", token_major=True)
 
 
 def test_in_place_queries():

@@ -285,6 +285,49 @@ def test_shared_sibling_tokens_longest_path():
     verify(w, label="shared-siblings")
 
 
+def token_major(t: torch.Tensor) -> torch.Tensor:
+    """[num_blocks, Hkv, 16, D] <-> [num_blocks, 16, Hkv, D] (the swap is its
+    own inverse)."""
+    return t.permute(0, 2, 1, 3).contiguous()
+
+
+@pytest.mark.parametrize("which", ["small1", "small3", "full2", "full3", "full4"])
+def test_token_major_cache_layout(which):
+    """The step on token-major caches ([num_blocks, 16, Hkv, D], selected by
+    the TV_KV_TOKEN_MAJOR flag): attention is bit-identical to the same call
+    on head-major caches (only the copy source addresses differ) and within
+    the oracle's bounds; acceptance and compaction are bit-exact against the
+    oracle, the compacted caches compared once put back in head-major order.
+    Covers the fp32 path (small1), one sequence in fixed pieces (full2),
+    balanced shares (small3, full3) and four row chunks per KV head (full4)."""
+    w = W.make_small(int(which[-1])) if which.startswith("small") else full(int(which[-1]))
+    log(f"[parity] token-major {which} {w.spec.name} B={w.B} N={w.N}")
+    d = upload(w)
+    st = d["status"]
+    mask, _ = T.tv_build_tree_mask(d["parents"], dev_status=st)
+    out_hm = T.tv_tree_attention(d["q"], d["k"], d["v"], d["table"], d["prefix"], w.max_prefix_len, mask,
+                                 dev_status=st)
+    k_tm, v_tm = token_major(d["k"]), token_major(d["v"])
+    del d["k"], d["v"]
+    out_tm = T.tv_tree_attention(d["q"], k_tm, v_tm, d["table"], d["prefix"], w.max_prefix_len, mask,
+                                 dev_status=st, token_major=True)
+    al, an, bt, am = T.tv_accept_greedy(d["logits"], d["draft"], d["parents"], dev_status=st)
+    nl = T.tv_kv_compact(k_tm, v_tm, d["table"], d["prefix"], an, al, dev_status=st, token_major=True)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(out_tm.view(torch.int16) if out_tm.dtype == torch.bfloat16 else out_tm.view(torch.int32),
+                       out_hm.view(torch.int16) if out_hm.dtype == torch.bfloat16 else out_hm.view(torch.int32))
+    seqs = list(range(w.B))
+    check_attention(out_tm, oracle_attention(w, seqs), seqs, w.q.dtype, label=f"token-major {which}")
+    aref = O.accept_greedy(w.logits.numpy(), w.draft_tokens, w.parents)
+    check_accept(dict(argmax=am, accept_len=al, accepted_nodes=an, bonus=bt), aref)
+    kref, vref, nlref = O.kv_compact(raw_bits(w.k_cache), raw_bits(w.v_cache), w.block_table, w.prefix_lens,
+                                     aref["accepted_nodes"], aref["accept_len"])
+    assert np.array_equal(nl.cpu().numpy(), nlref)
+    assert np.array_equal(raw_bits(token_major(k_tm)), kref)
+    assert np.array_equal(raw_bits(token_major(v_tm)), vref)
+
+
 def test_repeated_runs_bitwise_identical():
     w = W.make_small(2)
     d = upload(w)

@@ -32,6 +32,7 @@ from ._lib import (  # noqa: F401
     TV_DEV_UNSUPPORTED,
     TV_ERR_TOO_LARGE,
     TV_F32,
+    TV_KV_TOKEN_MAJOR,
     TV_MAX_NODES,
     TVError,
     header_functions,

@@ -23,6 +23,7 @@ TV_OK = 0
 TV_ERR_TOO_LARGE = 8
 TV_ACCEPT_NOALLOC_SCRATCH_BYTES = 4 << 20
 TV_F32, TV_BF16 = 0, 1
+TV_KV_TOKEN_MAJOR = 0x100  # dtype flag: caches [num_blocks, 16, Hkv, D] instead of [num_blocks, Hkv, 16, D]
 TV_DEV_BAD_TREE, TV_DEV_BAD_CACHE, TV_DEV_BAD_TOKEN = 1, 2, 4
 TV_DEV_BAD_RANDOM, TV_DEV_UNSUPPORTED = 8, 16
 TV_MAX_NODES = 256
@@ -50,7 +51,7 @@ def _load() -> ctypes.CDLL:
         "tv_status_string": (ctypes.c_char_p, [_c_i32]),
         "tv_version": (ctypes.c_int, []),
         "tv_build_tree_mask": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
-        "tv_tree_attention_workspace_size": (_c_size, [_c_i32] * 6 + [_c_i32]),
+        "tv_tree_attention_workspace_size": (_c_size, [_c_i32] * 6),
         "tv_tree_attention": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_ptr, _c_i32, _c_i32,
                                        _c_ptr, _c_i32, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32,
                                        _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_ptr, _c_size,
@@ -179,24 +180,39 @@ def tv_build_tree_mask(parents: torch.Tensor, mask: Optional[torch.Tensor] = Non
     return mask, depth
 
 
-def tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len, dtype) -> int:
-    return int(lib.tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len, dtype))
+def tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len) -> int:
+    return int(lib.tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len))
+
+
+def _cache_dims(k_cache: torch.Tensor, token_major: bool):
+    """(num_blocks, Hkv, block_size, D) of a cache in either layout."""
+    if k_cache.dim() != 4:
+        raise ValueError("caches must be 4-d")
+    if token_major:
+        nb, bs, Hkv, D = k_cache.shape  # [num_blocks, block_size, Hkv, D]
+    else:
+        nb, Hkv, bs, D = k_cache.shape  # [num_blocks, Hkv, block_size, D]
+    return nb, Hkv, bs, D
 
 
 def tv_tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       block_table: torch.Tensor, prefix_lens: torch.Tensor, max_prefix_len: int,
                       mask: torch.Tensor, out: Optional[torch.Tensor] = None, scale: float = 0.0,
                       workspace: Optional[torch.Tensor] = None,
-                      dev_status: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """q [B, N, Hq, D]; caches [num_blocks, Hkv, 16, D] (bf16 or fp32, same as
-    q); block_table int32 [B, max_blocks]; prefix_lens int32 [B]; mask from
-    tv_build_tree_mask.  Returns out [B, N, Hq, D] in q's dtype."""
+                      dev_status: Optional[torch.Tensor] = None,
+                      token_major: bool = False) -> torch.Tensor:
+    """q [B, N, Hq, D]; caches [num_blocks, Hkv, 16, D] (token_major:
+    [num_blocks, 16, Hkv, D]; bf16 or fp32, same as q); block_table int32
+    [B, max_blocks]; prefix_lens int32 [B]; mask from tv_build_tree_mask.
+    Returns out [B, N, Hq, D] in q's dtype."""
     dt = _tv_dtype(q)
     _dev(q, "q", q.dtype)
     B, N, Hq, D = q.shape
-    nb, Hkv, bs, D2 = k_cache.shape  # [num_blocks, Hkv, block_size, D]
-    _dev(k_cache, "k_cache", q.dtype, (nb, Hkv, bs, D))
-    _dev(v_cache, "v_cache", q.dtype, (nb, Hkv, bs, D))
+    nb, Hkv, bs, _ = _cache_dims(k_cache, token_major)
+    _dev(k_cache, "k_cache", q.dtype, k_cache.shape)
+    _dev(v_cache, "v_cache", q.dtype, k_cache.shape)
+    if k_cache.shape[3] != D:
+        raise ValueError("cache rows must have q's head dim")
     _dev(block_table, "block_table", torch.int32)
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_blocks]")
@@ -205,7 +221,7 @@ def tv_tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype, q.shape)
-    need = tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len, dt)
+    need = tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len) if dt == TV_BF16 else 0
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -214,7 +230,8 @@ def tv_tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _check("tv_tree_attention", lib.tv_tree_attention(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_table), block_table.shape[1], bs,
         _ptr(prefix_lens), int(max_prefix_len), _ptr(mask), _ptr(out), B, N, Hq, Hkv, D,
-        float(scale), dt, _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(q)))
+        float(scale), dt | (TV_KV_TOKEN_MAJOR if token_major else 0), _ptr(workspace), ws_bytes,
+        _ptr(dev_status), _stream(q)))
     return out
 
 
@@ -397,10 +414,12 @@ def tv_build_draft_tree(draft_logits: torch.Tensor, N: int,
 def tv_kv_compact(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                   prefix_lens: torch.Tensor, accepted_nodes: torch.Tensor,
                   accept_len: torch.Tensor, new_lens: Optional[torch.Tensor] = None,
-                  dev_status: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Compacts the accepted path's K/V in place; returns new_lens int32 [B]."""
+                  dev_status: Optional[torch.Tensor] = None, token_major: bool = False) -> torch.Tensor:
+    """Compacts the accepted path's K/V in place (caches [num_blocks, Hkv, 16,
+    D], or [num_blocks, 16, Hkv, D] with token_major); returns new_lens int32
+    [B]."""
     dt = _tv_dtype(k_cache)
-    nb, Hkv, bs, D = k_cache.shape  # [num_blocks, Hkv, block_size, D]
+    nb, Hkv, bs, D = _cache_dims(k_cache, token_major)
     _dev(k_cache, "k_cache", k_cache.dtype)
     _dev(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
     _dev(accepted_nodes, "accepted_nodes", torch.int32)
@@ -417,27 +436,30 @@ def tv_kv_compact(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: tor
         _dev(dev_status, "dev_status", torch.int32)
     _check("tv_kv_compact", lib.tv_kv_compact(
         _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_table), block_table.shape[1], bs,
-        _ptr(prefix_lens), _ptr(accepted_nodes), _ptr(accept_len), B, N, Hkv, D, dt,
-        _ptr(new_lens), _ptr(dev_status), _stream(k_cache)))
+        _ptr(prefix_lens), _ptr(accepted_nodes), _ptr(accept_len), B, N, Hkv, D,
+        dt | (TV_KV_TOKEN_MAJOR if token_major else 0), _ptr(new_lens), _ptr(dev_status), _stream(k_cache)))
     return new_lens
 
 
 def tv_tree_kv_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, depth: torch.Tensor,
                      k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                      prefix_lens: torch.Tensor, rope_theta: float, q_out: Optional[torch.Tensor] = None,
-                     dev_status: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     dev_status: Optional[torch.Tensor] = None, token_major: bool = False) -> torch.Tensor:
     """q [B, N, Hq, D]; k_new, v_new [B, N, Hkv, D]; depth int32 [B, N] (from
-    tv_build_tree_mask); caches [num_blocks, Hkv, 16, D] updated in place at
-    positions P_b + i.  Returns the rotated queries (q_out, may be q)."""
+    tv_build_tree_mask); caches [num_blocks, Hkv, 16, D] (token_major:
+    [num_blocks, 16, Hkv, D]) updated in place at positions P_b + i.  Returns
+    the rotated queries (q_out, may be q)."""
     dt = _tv_dtype(q)
     _dev(q, "q", q.dtype)
     B, N, Hq, D = q.shape
-    nb, Hkv, bs, D2 = k_cache.shape  # [num_blocks, Hkv, block_size, D]
+    nb, Hkv, bs, D2 = _cache_dims(k_cache, token_major)
     _dev(k_new, "k_new", q.dtype, (B, N, Hkv, D))
     _dev(v_new, "v_new", q.dtype, (B, N, Hkv, D))
     _dev(depth, "depth", torch.int32, (B, N))
-    _dev(k_cache, "k_cache", q.dtype, (nb, Hkv, bs, D))
-    _dev(v_cache, "v_cache", q.dtype, (nb, Hkv, bs, D))
+    _dev(k_cache, "k_cache", q.dtype, k_cache.shape)
+    _dev(v_cache, "v_cache", q.dtype, k_cache.shape)
+    if D2 != D:
+        raise ValueError("cache rows must have q's head dim")
     _dev(block_table, "block_table", torch.int32)
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_blocks]")
@@ -450,5 +472,5 @@ def tv_tree_kv_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, 
     _check("tv_tree_kv_write", lib.tv_tree_kv_write(
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(depth), _ptr(q_out), _ptr(k_cache), _ptr(v_cache), nb,
         _ptr(block_table), block_table.shape[1], bs, _ptr(prefix_lens), B, N, Hq, Hkv, D,
-        float(rope_theta), dt, _ptr(dev_status), _stream(q)))
+        float(rope_theta), dt | (TV_KV_TOKEN_MAJOR if token_major else 0), _ptr(dev_status), _stream(q)))
     return q_out

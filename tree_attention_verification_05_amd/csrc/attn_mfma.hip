@@ -364,15 +364,16 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   // (all in one 16-token block); lane l writes chunk position l % kChunks of
   // key i*kKeysPerCopy + l / kChunks.  The source address is a wave-uniform
   // block-and-head base plus a per-thread offset fixed for the whole kernel.
-  // (byte offsets within one block of one head; the block and head go into
-  // the buffer descriptor)
+  // (byte offsets from the block's row of head kh at slot 0; the block and
+  // head go into the buffer descriptor, and consecutive slots of a head are
+  // kv_slot_rows rows apart)
   int off_k[C::kCopiesPerWave], off_v[C::kCopiesPerWave];
   {
     const int ckey = lane / C::kChunks, cpos = lane % C::kChunks;
 #pragma unroll
     for (int jj = 0; jj < C::kCopiesPerWave; ++jj) {
       const int key = (jj * NW + wave) * C::kKeysPerCopy + ckey;
-      const int row = (key & 15) * D;
+      const int row = (key & 15) * a.kv_slot_rows * D;
       off_k[jj] = (row + (cpos ^ (key & 7)) * 8) * 2;
       off_v[jj] = (row + (cpos ^ (2 * (key & 3))) * 8) * 2;
     }
@@ -457,12 +458,12 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     const bool bad_len = Praw < 0 || Praw > a.max_prefix_len;
     const int P = clamp_prefix(a, Praw);
     const int nblk = (P + a.N + kBlockSize - 1) / kBlockSize;
-    // buffer descriptors per (cache, block): base = the block's first row of
-    // head kh; the range ends with that head's rows, so a stray offset reads
-    // zeros
+    // buffer descriptors per (cache, block): base = the block's row of head
+    // kh at slot 0; the range ends with that head's last slot row, so a stray
+    // offset reads zeros
     const long block_bytes = block_stride * 2;
-    const long head_bytes = static_cast<long>(kh) * kBlockSize * D * 2;
-    const int range = kBlockSize * D * 2;
+    const long head_bytes = static_cast<long>(kh) * a.kv_head_rows * D * 2;
+    const int range = ((kBlockSize - 1) * a.kv_slot_rows + 1) * D * 2;
     auto issue_tile = [&](int stage, int tile, int b0, int b1) __attribute__((always_inline)) {
       const int e0 = tile * 2;
       b0 = e0 < nblk ? b0 : 0;

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_rowwave_kernel(AttnArgs a) {
   for (int t0 = 0; t0 < total; t0 += 64) {
     const int t = t0 + lane;
     float s = -INFINITY;
-    long long crow = -1;  // cache row ((block * Hkv + kh) * block_size + slot) of this lane's key
+    long long crow = -1;  // cache row (D elements) of this lane's key in head kh
     if (t < total) {
       bool vis = true;
       if (t >= P) {
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_rowwave_kernel(AttnArgs a) {
         vis = false;
       }
       if (vis) {
-        crow = (static_cast<long long>(blk) * a.Hkv + kh) * kBlockSize + t % kBlockSize;
+        crow = kv_row(blk, kh, t % kBlockSize, a.Hkv, a.kv_head_rows, a.kv_slot_rows);
         const long long base = crow * D;
         float dot = 0.f;
         for (int d = 0; d < D; ++d) dot += qs[wave][d] * Elt<T>::load(kc + base + d);

@@ -4,8 +4,8 @@
 // rolled back to the accepted tokens).
 //
 // One workgroup per sequence.  Each thread owns 16-byte columns of a token's
-// K/V (both caches, every KV head; in the [block][head][slot][dim] layout a
-// token's head h sits block_size rows after its head h - 1) and walks the
+// K/V (both caches, every KV head; a token's head h sits kv_head_rows rows
+// after its head h - 1) and walks the
 // path in ascending order, reading source rows before writing destinations.  For a strictly increasing path
 // with path[j] >= j, a destination j is never the source of a later step, and
 // the source path[j] of step j is rewritten (as destination) only by the later
@@ -55,9 +55,9 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CompactArgs a) {
         bad |= TV_DEV_BAD_CACHE;
         continue;
       }
-      // row (block * Hkv + head) * block_size + slot, at head 0
-      s_src[j] = static_cast<long long>(bs) * a.Hkv * kBlockSize + ts % kBlockSize;
-      s_dst[j] = static_cast<long long>(bd) * a.Hkv * kBlockSize + td % kBlockSize;
+      // the token's row at head 0
+      s_src[j] = kv_row(bs, 0, ts % kBlockSize, a.Hkv, a.kv_head_rows, a.kv_slot_rows);
+      s_dst[j] = kv_row(bd, 0, td % kBlockSize, a.Hkv, a.kv_head_rows, a.kv_slot_rows);
     }
   }
   if (bad) atomicOr(&s_bad, bad);
@@ -79,8 +79,8 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CompactArgs a) {
   for (int c = tid; c < 2 * cols; c += kThreads) {
     int4* base = reinterpret_cast<int4*>(c < cols ? a.k_cache : a.v_cache);
     const int cc = c < cols ? c : c - cols;
-    // head cc / dq sits (cc / dq) * block_size rows after head 0
-    const long long col = static_cast<long long>(cc / dq) * kBlockSize * dq + cc % dq;
+    // head cc / dq sits (cc / dq) * kv_head_rows rows after head 0
+    const long long col = static_cast<long long>(cc / dq) * a.kv_head_rows * dq + cc % dq;
     for (int j0 = 1; j0 < s_L; j0 += 8) {
       // every lane loads eight rows (steps past L or without a move read
       // column col of block 0, head 0, slot 0, which is in bounds), so the

@@ -10,7 +10,7 @@
 // reduced to fp32 (cos, sin) in LDS; each thread then turns four (x[j],
 // x[j + D/2]) pairs of one head at a time, reading both halves before
 // writing them, so q_out may alias q.  The rotated key and the value go to
-// logical position P_b + i of the paged cache ([block][head][slot][dim]).
+// logical position P_b + i of the paged cache (either layout).
 // The step is a stream of small rows: HBM-bound.
 #include <math.h>
 
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void tree_kv_write_kernel(KvWriteArgs a) 
         y2[e] = x2[e] * c + x1[e] * s;
       }
       T* dst = is_q ? qo + row * D
-                    : kc + ((static_cast<size_t>(blk) * a.Hkv + (row - a.Hq)) * kBlockSize + slot) * D;
+                    : kc + kv_row(blk, row - a.Hq, slot, a.Hkv, a.kv_head_rows, a.kv_slot_rows) * D;
       Vec4<T>::store(dst + j, y1);
       Vec4<T>::store(dst + j + h, y2);
     } else if (write_cache) {
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void tree_kv_write_kernel(KvWriteArgs a) 
       const int head = v_it / (D / 4), j = (v_it % (D / 4)) * 4;
       float x[4];
       Vec4<T>::load(vn + head * D + j, x);
-      Vec4<T>::store(vc + ((static_cast<size_t>(blk) * a.Hkv + head) * kBlockSize + slot) * D + j, x);
+      Vec4<T>::store(vc + kv_row(blk, head, slot, a.Hkv, a.kv_head_rows, a.kv_slot_rows) * D + j, x);
     }
   }
 }

@@ -22,7 +22,7 @@ const char* tv_status_string(tv_status s) {
     case TV_OK: return "TV_OK";
     case TV_ERR_NULL: return "TV_ERR_NULL: a required pointer is NULL";
     case TV_ERR_SHAPE: return "TV_ERR_SHAPE: sizes are inconsistent or out of range";
-    case TV_ERR_DTYPE: return "TV_ERR_DTYPE: dtype must be TV_F32 or TV_BF16";
+    case TV_ERR_DTYPE: return "TV_ERR_DTYPE: dtype must be TV_F32 or TV_BF16 (with TV_KV_TOKEN_MAJOR only where a cache is taken)";
     case TV_ERR_UNSUPPORTED: return "TV_ERR_UNSUPPORTED: D must be 64 or 128, block_size 16, and H a multiple of 64";
     case TV_ERR_ALIGN: return "TV_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
     case TV_ERR_WORKSPACE: return "TV_ERR_WORKSPACE: workspace missing or too small";
@@ -42,9 +42,9 @@ tv_status tv_build_tree_mask(const int32_t* parents, int32_t B, int32_t N, uint6
 }
 
 size_t tv_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                                        int32_t max_prefix_len, tv_dtype dtype) {
-  if (dtype != TV_BF16 || B <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
-      max_prefix_len < 0 || (D != 64 && D != 128))
+                                        int32_t max_prefix_len) {
+  // the bf16 path's need; the fp32 path needs none
+  if (B <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_prefix_len < 0 || (D != 64 && D != 128))
     return 0;
   return attention_mfma_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len);
 }
@@ -56,6 +56,8 @@ tv_status tv_tree_attention(const void* q, const void* k_cache, const void* v_ca
                             int32_t Hkv, int32_t D, float scale, tv_dtype dtype, void* workspace,
                             size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !block_table || !prefix_lens || !mask || !out) return TV_ERR_NULL;
+  const bool token_major = (dtype & TV_KV_TOKEN_MAJOR) != 0;
+  dtype = static_cast<tv_dtype>(dtype & ~TV_KV_TOKEN_MAJOR);
   if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
   if (B <= 0 || N <= 0 || N > TV_MAX_NODES || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
       num_blocks <= 0 || max_blocks <= 0 || max_prefix_len < 0)
@@ -66,7 +68,7 @@ tv_status tv_tree_attention(const void* q, const void* k_cache, const void* v_ca
     return TV_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return TV_ERR_ALIGN;
-  const size_t need = tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len, dtype);
+  const size_t need = dtype == TV_BF16 ? tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need)) return TV_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return TV_ERR_ALIGN;
 
@@ -86,6 +88,9 @@ tv_status tv_tree_attention(const void* q, const void* k_cache, const void* v_ca
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.D = D;
+  const KvLayout lay = kv_layout(token_major, Hkv);
+  a.kv_head_rows = lay.head_rows;
+  a.kv_slot_rows = lay.slot_rows;
   a.scale = scale > 0.f ? scale : 1.f / sqrtf(static_cast<float>(D));
   a.workspace = workspace;
   a.dev_status = dev_status;
@@ -258,6 +263,8 @@ tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks, const 
                         int32_t* dev_status, hipStream_t stream) {
   if (!k_cache || !v_cache || !block_table || !prefix_lens || !accepted_nodes || !accept_len)
     return TV_ERR_NULL;
+  const bool token_major = (dtype & TV_KV_TOKEN_MAJOR) != 0;
+  dtype = static_cast<tv_dtype>(dtype & ~TV_KV_TOKEN_MAJOR);
   if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
   if (B <= 0 || N <= 0 || N > TV_MAX_NODES || Hkv <= 0 || num_blocks <= 0 || max_blocks <= 0)
     return TV_ERR_SHAPE;
@@ -277,6 +284,9 @@ tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks, const 
   a.N = N;
   a.Hkv = Hkv;
   a.D = D;
+  const KvLayout lay = kv_layout(token_major, Hkv);
+  a.kv_head_rows = lay.head_rows;
+  a.kv_slot_rows = lay.slot_rows;
   a.elt_bytes = dtype == TV_F32 ? 4 : 2;
   a.new_lens = new_lens;
   a.dev_status = dev_status;
@@ -291,6 +301,8 @@ tv_status tv_tree_kv_write(const void* q, const void* k_new, const void* v_new, 
                            hipStream_t stream) {
   if (!q || !k_new || !v_new || !depth || !q_out || !k_cache || !v_cache || !block_table || !prefix_lens)
     return TV_ERR_NULL;
+  const bool token_major = (dtype & TV_KV_TOKEN_MAJOR) != 0;
+  dtype = static_cast<tv_dtype>(dtype & ~TV_KV_TOKEN_MAJOR);
   if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
   if (B <= 0 || N <= 0 || N > TV_MAX_NODES || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || num_blocks <= 0 ||
       max_blocks <= 0 || !(rope_theta > 0.f))
@@ -317,6 +329,9 @@ tv_status tv_tree_kv_write(const void* q, const void* k_new, const void* v_new, 
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.D = D;
+  const KvLayout lay = kv_layout(token_major, Hkv);
+  a.kv_head_rows = lay.head_rows;
+  a.kv_slot_rows = lay.slot_rows;
   a.theta = rope_theta;
   a.dev_status = dev_status;
   return launched(launch_tree_kv_write(a, dtype, stream));

@@ -11,6 +11,26 @@ namespace tv {
 
 constexpr int kBlockSize = 16;   // tokens per paged-cache block
 
+// Paged-cache layout.  A block holds kBlockSize slots of Hkv heads, each a
+// row of D elements; the row of (block, head, slot) is
+//   block * kBlockSize * Hkv + head * head_rows + slot * slot_rows.
+// Head-major blocks ([block][head][slot][D], the default) keep one head's
+// slots together: head_rows = kBlockSize, slot_rows = 1.  Token-major blocks
+// ([block][slot][head][D]) keep one slot's heads together: head_rows = 1,
+// slot_rows = Hkv.
+struct KvLayout {
+  int head_rows;
+  int slot_rows;
+};
+inline KvLayout kv_layout(bool token_major, int Hkv) {
+  return token_major ? KvLayout{1, Hkv} : KvLayout{kBlockSize, 1};
+}
+__host__ __device__ __forceinline__ long long kv_row(long long block, int head, int slot, int Hkv, int head_rows,
+                                                     int slot_rows) {
+  return block * kBlockSize * Hkv + static_cast<long long>(head) * head_rows +
+         static_cast<long long>(slot) * slot_rows;
+}
+
 // ---- bf16 helpers (storage is the raw 16-bit pattern) ----
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
@@ -89,6 +109,7 @@ struct AttnArgs {
   const uint64_t* mask;
   void* out;
   int B, N, Hq, Hkv, D;
+  int kv_head_rows, kv_slot_rows;  // cache layout (KvLayout)
   float scale;
   void* workspace;
   int32_t* dev_status;
@@ -171,6 +192,7 @@ struct CompactArgs {
   const int32_t* accepted_nodes;
   const int32_t* accept_len;
   int B, N, Hkv, D;
+  int kv_head_rows, kv_slot_rows;  // cache layout (KvLayout)
   int elt_bytes;
   int32_t* new_lens;
   int32_t* dev_status;
@@ -190,6 +212,7 @@ struct KvWriteArgs {
   int max_blocks;
   const int32_t* prefix_lens;
   int B, N, Hq, Hkv, D;
+  int kv_head_rows, kv_slot_rows;  // cache layout (KvLayout)
   float theta;
   int32_t* dev_status;
 };
