@@ -1,9 +1,11 @@
 """Throughput of one verification step on one GPU.
 
 A step is one pass of the whole path over one batch: tree mask, tree-masked
-attention over the paged prefix, greedy acceptance over the target logits,
-and KV compaction of the accepted paths, each one libtv call on the current
-stream.  Inputs are synthetic (seeded) and resident in HBM before timing.
+attention over the paged prefix, then greedy acceptance over the target
+logits with the KV compaction of the accepted paths (one call,
+tv_accept_greedy_compact: the workgroup that walks a sequence moves its
+rows), each on the current stream.  Inputs are synthetic (seeded) and
+resident in HBM before timing.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--workloads 3,4,5]
 
@@ -53,8 +55,9 @@ CSRC = os.path.join(ROOT, "tree_attention_verification_05_amd", "csrc")
 # included): counter runs taken on other sources are not reported
 KERNEL_SOURCES = {
     "tv_tree_attention": ["attn_mfma.hip", "attn_rowwave.hip", "tv_internal.h"],
-    "tv_accept_greedy": ["accept.hip", "tv_internal.h"],
-    "tv_kv_compact": ["kv_compact.hip", "tv_internal.h"],
+    "tv_accept_greedy": ["accept.hip", "kv_compact_rows.h", "tv_internal.h"],
+    "tv_accept_greedy_compact": ["accept.hip", "kv_compact_rows.h", "tv_internal.h"],
+    "tv_kv_compact": ["kv_compact.hip", "kv_compact_rows.h", "tv_internal.h"],
     "tv_build_tree_mask": ["tree_mask.hip", "tv_internal.h"],
     "tv_tree_kv_write": ["tree_kv_write.hip", "tv_internal.h"],
     "tv_accept_stochastic": ["accept_stochastic.hip", "tv_internal.h"],
@@ -118,28 +121,35 @@ def step_work(w, accept_len, accepted_nodes):
         path = accepted_nodes[b, :L]
         moved += int((path != np.arange(L)).sum())
     row_bytes = s.Hkv * s.D * elt
+    accept_bytes = B * N * s.V * 4 + B * N * 4 * 3 + B * (N + 2) * 4
+    compact_bytes = moved * 2 * 2 * row_bytes + B * (N + 3) * 4
     return {
         "tv_build_tree_mask": {"bytes": B * N * (4 + 8 * Wd + 4)},
         "tv_tree_attention": {"bytes": attn_bytes, "flops": attn_flops,
                               "bound": "mfma" if attn_flops / attn_bytes > RIDGE_FLOP_PER_BYTE
                               else "hbm"},
-        "tv_accept_greedy": {"bytes": B * N * s.V * 4 + B * N * 4 * 3 + B * (N + 2) * 4},
-        "tv_kv_compact": {"bytes": moved * 2 * 2 * row_bytes + B * (N + 3) * 4},
+        "tv_accept_greedy": {"bytes": accept_bytes},
+        "tv_kv_compact": {"bytes": compact_bytes},
+        # the fused call moves what the two do, less the path and length
+        # arrays the compaction would read back
+        "tv_accept_greedy_compact": {"bytes": accept_bytes + compact_bytes - B * (N + 1) * 4},
     }
 
 
 # the benchmark spec's attention targets: HBM fraction on the memory-bound workloads,
 # bf16 matrix-core fraction on the one above the ridge
 TARGETS = {3: ("hbm", 0.60), 4: ("mfma", 0.40), 5: ("hbm", 0.60)}
-STEP_CALLS = ["tv_build_tree_mask", "tv_tree_attention", "tv_accept_greedy", "tv_kv_compact"]
+# the step: mask, attention, then acceptance with the compaction of its
+# accepted paths in the same call (the walking workgroup moves the rows)
+STEP_CALLS = ["tv_build_tree_mask", "tv_tree_attention", "tv_accept_greedy_compact"]
 TIME_BASE = ("mean HIP-event time of each call, events recorded on the launch stream around the "
              "call's launches (for attention: main kernel, launch gap and merge kernel), one "
              "eviction before every step")
 
 
 class StepBench:
-    """The four calls of one workload's step on device-resident inputs,
-    with its buffers allocated once."""
+    """The calls of one workload's step on device-resident inputs, with its
+    buffers allocated once."""
 
     def __init__(self, T, W, cfg: int, seed: int, dev):
         import torch
@@ -182,15 +192,12 @@ class StepBench:
                             self.mask, out=self.out, workspace=self.attn_ws, dev_status=self.status)
         if ev is not None:
             ev[2].record(st)
-        T.tv_accept_greedy(self.logits, self.draft, self.parents, accept_len=self.acc_len,
-                           accepted_nodes=self.acc_nodes, bonus_token=self.bonus,
-                           target_argmax=self.am, workspace=self.acc_ws, dev_status=self.status)
+        T.tv_accept_greedy_compact(self.logits, self.draft, self.parents, self.k, self.v, self.table, self.prefix,
+                                   accept_len=self.acc_len, accepted_nodes=self.acc_nodes, bonus_token=self.bonus,
+                                   target_argmax=self.am, new_lens=self.new_lens, workspace=self.acc_ws,
+                                   dev_status=self.status)
         if ev is not None:
             ev[3].record(st)
-        T.tv_kv_compact(self.k, self.v, self.table, self.prefix, self.acc_nodes, self.acc_len,
-                        new_lens=self.new_lens, dev_status=self.status)
-        if ev is not None:
-            ev[4].record(st)
 
     def measure(self, steps: int, warmup: int, evict):
         """W warm-up steps, then exactly K timed steps (one event pair each,
@@ -214,12 +221,13 @@ class StepBench:
         torch.cuda.synchronize()
         self.t_wall = time.perf_counter() - t_wall
         self.step_ms = np.array([step_ev[s][0].elapsed_time(step_ev[s][1]) for s in range(steps)])
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        ncalls = len(STEP_CALLS)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)] for _ in range(steps)]
         for s in range(steps):
             evict()
             self.run_step(evs[s])
         torch.cuda.synchronize()
-        self.per = np.array([[evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(4)]
+        self.per = np.array([[evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(ncalls)]
                              for s in range(steps)])  # ms
         return self.record()
 

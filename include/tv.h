@@ -85,7 +85,8 @@ typedef enum {
 typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 
 /* Cache-layout flag for the dtype argument of tv_tree_attention,
- * tv_kv_compact and tv_tree_kv_write: the caches are token-major
+ * tv_kv_compact, tv_accept_greedy_compact and tv_tree_kv_write: the caches
+ * are token-major
  * [num_blocks][block_size][Hkv][D] instead of head-major
  * [num_blocks][Hkv][block_size][D].  Pass (tv_dtype)(TV_BF16 | TV_KV_TOKEN_MAJOR). */
 #define TV_KV_TOKEN_MAJOR 0x100
@@ -354,6 +355,29 @@ TV_API tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks,
                         const int32_t* accepted_nodes, const int32_t* accept_len, int32_t B,
                         int32_t N, int32_t Hkv, int32_t D, tv_dtype dtype, int32_t* new_lens,
                         int32_t* dev_status, hipStream_t stream);
+
+/*
+ * tv_accept_greedy_compact -- tv_accept_greedy followed by tv_kv_compact of
+ * its accepted paths, in one call: the workgroup that walks a sequence also
+ * moves that sequence's accepted K/V rows, so the step needs one launch
+ * fewer.  ("P-EAGLE", 技术原理和实现方式 steps 3-4 and 技术难点和解决方案;
+ * "EAGLE代码实现原理", KV缓存优化: copy(indices, prev_length).)
+ *
+ * Outputs, caches and new_lens are exactly those of tv_accept_greedy and
+ * then tv_kv_compact(accepted_nodes, accept_len) on the same arguments: the
+ * same bytes, the same device status bits.  Arguments are those of the two
+ * calls (workspace: tv_accept_greedy_workspace_size(B, N, V) bytes; dtype
+ * and the cache layout flag as for tv_kv_compact).
+ * Errors: the union of both calls' host errors.
+ */
+TV_API tv_status tv_accept_greedy_compact(const float* logits, const int32_t* draft_tokens,
+                                          const int32_t* parents, int32_t B, int32_t N, int32_t V,
+                                          int32_t* accept_len, int32_t* accepted_nodes, int32_t* bonus_token,
+                                          int32_t* target_argmax, void* workspace, size_t workspace_bytes,
+                                          void* k_cache, void* v_cache, int32_t num_blocks,
+                                          const int32_t* block_table, int32_t max_blocks, int32_t block_size,
+                                          const int32_t* prefix_lens, int32_t Hkv, int32_t D, tv_dtype dtype,
+                                          int32_t* new_lens, int32_t* dev_status, hipStream_t stream);
 
 /*
  * tv_tree_kv_write -- rotate the step's queries and new keys to their tree

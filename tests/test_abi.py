@@ -169,6 +169,27 @@ def test_accept_stochastic_host_checks():
     assert call(ws=P16 + 8) == 5
 
 
+def test_accept_compact_host_checks():
+    """The fused acceptance-and-compaction call: the union of both calls'
+    host checks (nothing is launched on an error)."""
+    f = lib.tv_accept_greedy_compact
+    need = lib.tv_accept_greedy_workspace_size(2, 8, 1000)
+
+    def call(**kw):
+        a = dict(lg=P16, dt=P16, par=P16, B=2, N=8, V=1000, al=P16, an=P16, bt=P16, am=None, ws=P16, wsb=need,
+                 k=P16, v=P16, nb=10, table=P16, mb=4, bs=16, pl=P16, Hkv=2, D=128, dty=1, nl=None, st=None, s=None)
+        a.update(kw)
+        return f(a["lg"], a["dt"], a["par"], a["B"], a["N"], a["V"], a["al"], a["an"], a["bt"], a["am"], a["ws"],
+                 a["wsb"], a["k"], a["v"], a["nb"], a["table"], a["mb"], a["bs"], a["pl"], a["Hkv"], a["D"],
+                 a["dty"], a["nl"], a["st"], a["s"])
+    assert call(lg=None) == 1 and call(bt=None) == 1 and call(k=None) == 1 and call(pl=None) == 1
+    assert call(V=0) == 2 and call(N=257) == 2 and call(Hkv=0) == 2 and call(nb=0) == 2
+    assert call(dty=2) == 3 and call(dty=0x200 | 1) == 3
+    assert call(D=96) == 4 and call(bs=32) == 4
+    assert call(lg=P16 + 4) == 5 and call(k=P16 + 8) == 5
+    assert call(ws=None) == 6 and call(wsb=need - 1) == 6
+
+
 def test_lm_head_host_checks():
     f = lib.tv_lm_head_argmax
     need = lib.tv_lm_head_argmax_workspace_size(60, 4096, 128256)

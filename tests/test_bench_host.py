@@ -51,3 +51,6 @@ def test_step_work_by_hand():
     assert work["tv_accept_greedy"]["bytes"] == 2 * 3 * 10 * 4 + 2 * 3 * 4 * 3 + 2 * 5 * 4
     # a chain's accepted path is the identity: nothing moves
     assert work["tv_kv_compact"]["bytes"] == 2 * 6 * 4
+    # fused: both, less the path (N entries) and length the compaction reads back
+    assert work["tv_accept_greedy_compact"]["bytes"] == (work["tv_accept_greedy"]["bytes"]
+                                                         + work["tv_kv_compact"]["bytes"] - 2 * 4 * 4)

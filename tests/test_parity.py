@@ -373,6 +373,59 @@ def test_device_status_bits():
     assert int(st.item()) & T.TV_DEV_BAD_CACHE
 
 
+@pytest.mark.parametrize("which", ["small1", "small2", "small3", "small4", "small5", "full2", "full3", "full5",
+                                   "small3-token-major", "statuses"])
+def test_accept_compact_fused(which):
+    """tv_accept_greedy_compact against the two separate calls on copies of
+    the same inputs: identical outputs, caches, new lengths and device status
+    bits, byte for byte; and against the oracle.  'statuses' plants a bad
+    tree (sequence 1), an out-of-range token (2) and a block id outside the
+    cache in the tree region (3): the separate calls and the fused one must
+    report and write the same."""
+    tm = which.endswith("token-major")
+    if which == "statuses":
+        w = W.make_small(3, seed=7)
+        par, draft, table = w.parents.copy(), w.draft_tokens.copy(), w.block_table.copy()
+        par[1, 3] = 5
+        draft[2, 4] = w.spec.V
+        table[3, int(w.prefix_lens[3]) // 16] = w.num_blocks
+        w.parents, w.draft_tokens, w.block_table = par, draft, table
+    elif which.startswith("small"):
+        w = W.make_small(int(which[5]))
+    else:
+        w = full(int(which[-1]))
+    log(f"[parity] accept+compact {which} {w.spec.name} B={w.B} N={w.N}")
+    d = upload(w)
+    k2, v2 = d["k"].clone(), d["v"].clone()
+    if tm:
+        d["k"], d["v"] = token_major(d["k"]), token_major(d["v"])
+        k2, v2 = token_major(k2), token_major(v2)
+    st1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    al, an, bt, am = T.tv_accept_greedy(d["logits"], d["draft"], d["parents"], dev_status=st1)
+    nl = T.tv_kv_compact(d["k"], d["v"], d["table"], d["prefix"], an, al, dev_status=st1, token_major=tm)
+    al2, an2, bt2, am2, nl2 = T.tv_accept_greedy_compact(d["logits"], d["draft"], d["parents"], k2, v2, d["table"],
+                                                         d["prefix"], dev_status=st2, token_major=tm)
+    torch.cuda.synchronize()
+    assert int(st1.item()) == int(st2.item())
+    for x, y in ((al, al2), (an, an2), (bt, bt2), (am, am2)):
+        assert torch.equal(x, y)
+    ok = [b for b in range(w.B) if which != "statuses" or b not in (3,)]
+    assert torch.equal(nl[ok], nl2[ok])  # a sequence left untouched gets no new length from either call
+    assert np.array_equal(raw_bits(d["k"]), raw_bits(k2)) and np.array_equal(raw_bits(d["v"]), raw_bits(v2))
+    if which == "statuses":
+        assert int(st2.item()) == T.TV_DEV_BAD_TREE | T.TV_DEV_BAD_TOKEN | T.TV_DEV_BAD_CACHE
+        return
+    assert int(st2.item()) == 0
+    aref = O.accept_greedy(w.logits.numpy(), w.draft_tokens, w.parents)
+    check_accept(dict(argmax=am2, accept_len=al2, accepted_nodes=an2, bonus=bt2), aref)
+    kref, vref, nlref = O.kv_compact(raw_bits(w.k_cache), raw_bits(w.v_cache), w.block_table, w.prefix_lens,
+                                     aref["accepted_nodes"], aref["accept_len"])
+    assert np.array_equal(nl2.cpu().numpy(), nlref)
+    kk, vv = (token_major(k2), token_major(v2)) if tm else (k2, v2)
+    assert np.array_equal(raw_bits(kk), kref) and np.array_equal(raw_bits(vv), vref)
+
+
 def test_python_binding_rejects_host_tensors():
     w = W.make_small(1)
     with pytest.raises(ValueError):

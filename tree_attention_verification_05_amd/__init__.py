@@ -38,6 +38,7 @@ from ._lib import (  # noqa: F401
     header_functions,
     lib,
     tv_accept_greedy,
+    tv_accept_greedy_compact,
     tv_accept_greedy_noalloc,
     tv_accept_stochastic,
     tv_build_draft_tree,

@@ -57,6 +57,10 @@ def _load() -> ctypes.CDLL:
                                        _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_ptr, _c_size,
                                        _c_ptr, _c_ptr]),
         "tv_accept_greedy_workspace_size": (_c_size, [_c_i32] * 3),
+        "tv_accept_greedy_compact": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
+                                              _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_i32, _c_ptr,
+                                              _c_i32, _c_i32, _c_ptr, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
+                                              _c_ptr]),
         "tv_accept_greedy": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_ptr,
                                       _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr, _c_ptr]),
         "tv_accept_greedy_noalloc": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_ptr,
@@ -235,16 +239,10 @@ def tv_tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     return out
 
 
-def tv_accept_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, parents: torch.Tensor,
-                     accept_len: Optional[torch.Tensor] = None,
-                     accepted_nodes: Optional[torch.Tensor] = None,
-                     bonus_token: Optional[torch.Tensor] = None,
-                     target_argmax: Optional[torch.Tensor] = None, want_argmax: bool = True,
-                     workspace: Optional[torch.Tensor] = None,
-                     dev_status: Optional[torch.Tensor] = None):
-    """logits fp32 [B, N, V]; draft_tokens, parents int32 [B, N].  Returns
-    (accept_len [B], accepted_nodes [B, N], bonus_token [B], target_argmax
-    [B, N] or None), all int32."""
+def _accept_outputs(logits, draft_tokens, parents, accept_len, accepted_nodes, bonus_token, target_argmax,
+                    want_argmax):
+    """Checks of the greedy acceptance inputs; the outputs, allocated when
+    not given."""
     _dev(logits, "logits", torch.float32)
     B, N, V = logits.shape
     _dev(draft_tokens, "draft_tokens", torch.int32, (B, N))
@@ -263,6 +261,22 @@ def tv_accept_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, parents: 
     _dev(bonus_token, "bonus_token", torch.int32, (B,))
     if target_argmax is not None:
         _dev(target_argmax, "target_argmax", torch.int32, (B, N))
+    return B, N, V, accept_len, accepted_nodes, bonus_token, target_argmax
+
+
+def tv_accept_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, parents: torch.Tensor,
+                     accept_len: Optional[torch.Tensor] = None,
+                     accepted_nodes: Optional[torch.Tensor] = None,
+                     bonus_token: Optional[torch.Tensor] = None,
+                     target_argmax: Optional[torch.Tensor] = None, want_argmax: bool = True,
+                     workspace: Optional[torch.Tensor] = None,
+                     dev_status: Optional[torch.Tensor] = None):
+    """logits fp32 [B, N, V]; draft_tokens, parents int32 [B, N].  Returns
+    (accept_len [B], accepted_nodes [B, N], bonus_token [B], target_argmax
+    [B, N] or None), all int32."""
+    B, N, V, accept_len, accepted_nodes, bonus_token, target_argmax = _accept_outputs(
+        logits, draft_tokens, parents, accept_len, accepted_nodes, bonus_token, target_argmax, want_argmax)
+    dev = logits.device
     need = int(lib.tv_accept_greedy_workspace_size(B, N, V))
     if workspace is None:
         workspace = accept_workspace(dev, need)
@@ -439,6 +453,44 @@ def tv_kv_compact(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: tor
         _ptr(prefix_lens), _ptr(accepted_nodes), _ptr(accept_len), B, N, Hkv, D,
         dt | (TV_KV_TOKEN_MAJOR if token_major else 0), _ptr(new_lens), _ptr(dev_status), _stream(k_cache)))
     return new_lens
+
+
+def tv_accept_greedy_compact(logits: torch.Tensor, draft_tokens: torch.Tensor, parents: torch.Tensor,
+                             k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                             prefix_lens: torch.Tensor, accept_len: Optional[torch.Tensor] = None,
+                             accepted_nodes: Optional[torch.Tensor] = None,
+                             bonus_token: Optional[torch.Tensor] = None,
+                             target_argmax: Optional[torch.Tensor] = None, want_argmax: bool = True,
+                             new_lens: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                             dev_status: Optional[torch.Tensor] = None, token_major: bool = False):
+    """tv_accept_greedy, then tv_kv_compact of the accepted paths, in one
+    call.  Returns (accept_len, accepted_nodes, bonus_token, target_argmax or
+    None, new_lens)."""
+    B, N, V, accept_len, accepted_nodes, bonus_token, target_argmax = _accept_outputs(
+        logits, draft_tokens, parents, accept_len, accepted_nodes, bonus_token, target_argmax, want_argmax)
+    dev = logits.device
+    dt = _tv_dtype(k_cache)
+    nb, Hkv, bs, D = _cache_dims(k_cache, token_major)
+    _dev(k_cache, "k_cache", k_cache.dtype)
+    _dev(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
+    _dev(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _dev(prefix_lens, "prefix_lens", torch.int32, (B,))
+    if new_lens is None:
+        new_lens = torch.empty(B, dtype=torch.int32, device=dev)
+    _dev(new_lens, "new_lens", torch.int32, (B,))
+    need = int(lib.tv_accept_greedy_workspace_size(B, N, V))
+    if workspace is None:
+        workspace = accept_workspace(dev, need)
+    if dev_status is not None:
+        _dev(dev_status, "dev_status", torch.int32)
+    _check("tv_accept_greedy_compact", lib.tv_accept_greedy_compact(
+        _ptr(logits), _ptr(draft_tokens), _ptr(parents), B, N, V, _ptr(accept_len), _ptr(accepted_nodes),
+        _ptr(bonus_token), _ptr(target_argmax), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_table), block_table.shape[1], bs, _ptr(prefix_lens), Hkv, D,
+        dt | (TV_KV_TOKEN_MAJOR if token_major else 0), _ptr(new_lens), _ptr(dev_status), _stream(logits)))
+    return accept_len, accepted_nodes, bonus_token, target_argmax, new_lens
 
 
 def tv_tree_kv_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, depth: torch.Tensor,

@@ -12,9 +12,13 @@
 // sequence's N rows to the target argmax, validate the tree and the draft
 // tokens, and find the longest accepted path (smallest node sequence among
 // equals).  The workspace needs no initialisation.
+// With compaction fused (tv_accept_greedy_compact), the same workgroup then
+// moves the accepted path's K/V rows into place: the prefix length and the
+// block-table entries of the tree region are loaded with the tree, so once
+// the path is known only the row copies remain.
 #include <mutex>
 
-#include "tv_internal.h"
+#include "kv_compact_rows.h"
 
 namespace tv {
 namespace {
@@ -119,10 +123,15 @@ __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int
   __shared__ int s_ok[TV_MAX_NODES], s_dep[TV_MAX_NODES], s_on[TV_MAX_NODES];
   __shared__ int s_bad, s_dmax, s_path[TV_MAX_NODES];
   __shared__ unsigned long long s_key[TV_MAX_NODES];
+  // fused compaction: block ids of the tree region, and each step's rows
+  __shared__ int s_tab[TV_MAX_NODES / kBlockSize + 2], s_cbad;
+  __shared__ long long s_src[TV_MAX_NODES], s_dst[TV_MAX_NODES];
 
   const int N = a.N, V = a.V;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const CompactArgs& c = a.compact;
+  const bool fuse = c.k_cache != nullptr;
   const uint64_t* keys = static_cast<const uint64_t*>(a.workspace);
   const size_t base = static_cast<size_t>(b) * N;
   // every (node, chunk) key of the sequence is contiguous in the workspace;
@@ -145,7 +154,15 @@ __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int
   if (tid == 0) {
     s_bad = 0;
     s_dmax = 0;
+    s_cbad = 0;
   }
+  // fused compaction: the tree region's block ids, P_b / 16 .. (P_b + N - 1) / 16
+  const int P = fuse ? c.prefix_lens[b] : 0;
+  const bool p_ok = P >= 0 && static_cast<long>(P) + N <= static_cast<long>(c.max_blocks) * kBlockSize;
+  const int tab0 = P / kBlockSize;
+  if (fuse && p_ok)
+    for (int i = tid; i <= (P + N - 1) / kBlockSize - tab0; i += kThreads)
+      s_tab[i] = c.block_table[static_cast<size_t>(b) * c.max_blocks + tab0 + i];
   __syncthreads();
   // fold the keys per node with LDS max (further rounds of eight per thread
   // when N * chunks exceeds eight per thread)
@@ -179,12 +196,42 @@ __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int
   }
   if (bad) atomicOr(&s_bad, bad);
   __syncthreads();
+  // compaction of steps 0 .. L-1 of s_path (the fused call only)
+  auto compact = [&](int L) __attribute__((always_inline)) {
+    int cbad = p_ok ? 0 : TV_DEV_BAD_CACHE;
+    if (!cbad) {
+      for (int j = tid; j < L; j += kThreads) {
+        const int ts = P + s_path[j], td = P + j;
+        const int bs = s_tab[ts / kBlockSize - tab0], bd = s_tab[td / kBlockSize - tab0];
+        if (bs < 0 || bs >= c.num_blocks || bd < 0 || bd >= c.num_blocks) {
+          cbad |= TV_DEV_BAD_CACHE;
+          continue;
+        }
+        s_src[j] = kv_row(bs, 0, ts % kBlockSize, c.Hkv, c.kv_head_rows, c.kv_slot_rows);
+        s_dst[j] = kv_row(bd, 0, td % kBlockSize, c.Hkv, c.kv_head_rows, c.kv_slot_rows);
+      }
+    }
+    if (cbad) atomicOr(&s_cbad, cbad);
+    __syncthreads();
+    if (s_cbad) {  // the sequence is left untouched
+      if (tid == 0) report(a.dev_status, s_cbad);
+      return;
+    }
+    if (tid == 0 && c.new_lens) c.new_lens[b] = P + L;
+    compact_copy_columns(c, s_src, s_dst, L, tid, kThreads);
+  };
+
   if (s_bad) {
     if (tid == 0) report(a.dev_status, s_bad);
     for (int i = tid; i < N; i += kThreads) a.accepted_nodes[base + i] = (i == 0) ? 0 : -1;
     if (tid == 0) {
       a.accept_len[b] = 0;
       a.bonus_token[b] = s_am[0];
+      s_path[0] = 0;
+    }
+    if (fuse) {
+      __syncthreads();
+      compact(1);  // the root alone: nothing moves, the new length is P_b + 1
     }
     return;
   }
@@ -238,6 +285,7 @@ __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int
     a.accept_len[b] = dmax;
     a.bonus_token[b] = s_am[s_path[dmax]];
   }
+  if (fuse) compact(dmax + 1);
 }
 
 }  // namespace

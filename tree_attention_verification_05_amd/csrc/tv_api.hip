@@ -113,7 +113,7 @@ tv_status tv_accept_greedy(const float* logits, const int32_t* draft_tokens, con
   if (B <= 0 || N <= 0 || N > TV_MAX_NODES || V <= 0) return TV_ERR_SHAPE;
   if (!aligned16(logits)) return TV_ERR_ALIGN;
   if (!workspace || workspace_bytes < accept_workspace_bytes(B, N, V)) return TV_ERR_WORKSPACE;
-  AcceptArgs a;
+  AcceptArgs a{};  // no compaction
   a.logits = logits;
   a.draft_tokens = draft_tokens;
   a.parents = parents;
@@ -140,7 +140,7 @@ tv_status tv_accept_greedy_noalloc(const float* logits, const int32_t* draft_tok
   if (accept_workspace_bytes(B, N, V) > kAcceptScratchBytes) return TV_ERR_TOO_LARGE;
   void* scratch = nullptr;
   if (accept_static_scratch(stream, &scratch) != hipSuccess) return TV_ERR_LAUNCH;
-  AcceptArgs a;
+  AcceptArgs a{};  // no compaction
   a.logits = logits;
   a.draft_tokens = draft_tokens;
   a.parents = parents;
@@ -256,13 +256,15 @@ tv_status tv_build_draft_tree(const float* draft_logits, int32_t B, int32_t dept
   return launched(launch_draft_tree(a, stream));
 }
 
-tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks, const int32_t* block_table,
-                        int32_t max_blocks, int32_t block_size, const int32_t* prefix_lens,
-                        const int32_t* accepted_nodes, const int32_t* accept_len, int32_t B,
-                        int32_t N, int32_t Hkv, int32_t D, tv_dtype dtype, int32_t* new_lens,
-                        int32_t* dev_status, hipStream_t stream) {
-  if (!k_cache || !v_cache || !block_table || !prefix_lens || !accepted_nodes || !accept_len)
-    return TV_ERR_NULL;
+}  // extern "C"
+
+// Host checks of a compaction's cache arguments, and its argument record
+// (tv_kv_compact and the fused acceptance call).
+static tv_status make_compact_args(void* k_cache, void* v_cache, int32_t num_blocks, const int32_t* block_table,
+                                   int32_t max_blocks, int32_t block_size, const int32_t* prefix_lens, int32_t B,
+                                   int32_t N, int32_t Hkv, int32_t D, tv_dtype dtype, int32_t* new_lens,
+                                   int32_t* dev_status, CompactArgs* out) {
+  if (!k_cache || !v_cache || !block_table || !prefix_lens) return TV_ERR_NULL;
   const bool token_major = (dtype & TV_KV_TOKEN_MAJOR) != 0;
   dtype = static_cast<tv_dtype>(dtype & ~TV_KV_TOKEN_MAJOR);
   if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
@@ -271,15 +273,14 @@ tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks, const 
   if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
   if (block_size != kBlockSize) return TV_ERR_UNSUPPORTED;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return TV_ERR_ALIGN;
-  CompactArgs a;
+  CompactArgs& a = *out;
+  a = CompactArgs{};
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.num_blocks = num_blocks;
   a.block_table = block_table;
   a.max_blocks = max_blocks;
   a.prefix_lens = prefix_lens;
-  a.accepted_nodes = accepted_nodes;
-  a.accept_len = accept_len;
   a.B = B;
   a.N = N;
   a.Hkv = Hkv;
@@ -290,7 +291,55 @@ tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks, const 
   a.elt_bytes = dtype == TV_F32 ? 4 : 2;
   a.new_lens = new_lens;
   a.dev_status = dev_status;
+  return TV_OK;
+}
+
+extern "C" {
+
+tv_status tv_kv_compact(void* k_cache, void* v_cache, int32_t num_blocks, const int32_t* block_table,
+                        int32_t max_blocks, int32_t block_size, const int32_t* prefix_lens,
+                        const int32_t* accepted_nodes, const int32_t* accept_len, int32_t B,
+                        int32_t N, int32_t Hkv, int32_t D, tv_dtype dtype, int32_t* new_lens,
+                        int32_t* dev_status, hipStream_t stream) {
+  if (!accepted_nodes || !accept_len) return TV_ERR_NULL;
+  CompactArgs a;
+  const tv_status st = make_compact_args(k_cache, v_cache, num_blocks, block_table, max_blocks, block_size,
+                                         prefix_lens, B, N, Hkv, D, dtype, new_lens, dev_status, &a);
+  if (st != TV_OK) return st;
+  a.accepted_nodes = accepted_nodes;
+  a.accept_len = accept_len;
   return launched(launch_kv_compact(a, stream));
+}
+
+tv_status tv_accept_greedy_compact(const float* logits, const int32_t* draft_tokens, const int32_t* parents,
+                                   int32_t B, int32_t N, int32_t V, int32_t* accept_len, int32_t* accepted_nodes,
+                                   int32_t* bonus_token, int32_t* target_argmax, void* workspace,
+                                   size_t workspace_bytes, void* k_cache, void* v_cache, int32_t num_blocks,
+                                   const int32_t* block_table, int32_t max_blocks, int32_t block_size,
+                                   const int32_t* prefix_lens, int32_t Hkv, int32_t D, tv_dtype dtype,
+                                   int32_t* new_lens, int32_t* dev_status, hipStream_t stream) {
+  if (!logits || !draft_tokens || !parents || !accept_len || !accepted_nodes || !bonus_token)
+    return TV_ERR_NULL;
+  if (B <= 0 || N <= 0 || N > TV_MAX_NODES || V <= 0) return TV_ERR_SHAPE;
+  AcceptArgs a{};
+  const tv_status st = make_compact_args(k_cache, v_cache, num_blocks, block_table, max_blocks, block_size,
+                                         prefix_lens, B, N, Hkv, D, dtype, new_lens, dev_status, &a.compact);
+  if (st != TV_OK) return st;
+  if (!aligned16(logits)) return TV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < accept_workspace_bytes(B, N, V)) return TV_ERR_WORKSPACE;
+  a.logits = logits;
+  a.draft_tokens = draft_tokens;
+  a.parents = parents;
+  a.B = B;
+  a.N = N;
+  a.V = V;
+  a.accept_len = accept_len;
+  a.accepted_nodes = accepted_nodes;
+  a.bonus_token = bonus_token;
+  a.target_argmax = target_argmax;
+  a.workspace = workspace;
+  a.dev_status = dev_status;
+  return launched(launch_accept(a, stream));
 }
 
 tv_status tv_tree_kv_write(const void* q, const void* k_new, const void* v_new, const int32_t* depth,

@@ -122,6 +122,21 @@ hipError_t launch_attention_rowwave(const AttnArgs& a, tv_dtype dtype, hipStream
 size_t attention_mfma_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int max_prefix_len);
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
 
+struct CompactArgs {
+  void* k_cache;
+  void* v_cache;
+  int num_blocks;
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* prefix_lens;
+  const int32_t* accepted_nodes;
+  const int32_t* accept_len;
+  int B, N, Hkv, D;
+  int kv_head_rows, kv_slot_rows;  // cache layout (KvLayout)
+  int elt_bytes;
+  int32_t* new_lens;
+  int32_t* dev_status;
+};
 struct AcceptArgs {
   const float* logits;
   const int32_t* draft_tokens;
@@ -133,6 +148,9 @@ struct AcceptArgs {
   int32_t* target_argmax;
   void* workspace;
   int32_t* dev_status;
+  // compaction of the accepted path by the walking workgroup (k_cache NULL:
+  // walk only)
+  CompactArgs compact;
 };
 size_t accept_workspace_bytes(int B, int N, int V);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
@@ -182,21 +200,6 @@ struct DraftTreeArgs {
 size_t draft_tree_workspace_bytes(int B, int depth, int topk, int V);
 hipError_t launch_draft_tree(const DraftTreeArgs& a, hipStream_t stream);
 
-struct CompactArgs {
-  void* k_cache;
-  void* v_cache;
-  int num_blocks;
-  const int32_t* block_table;
-  int max_blocks;
-  const int32_t* prefix_lens;
-  const int32_t* accepted_nodes;
-  const int32_t* accept_len;
-  int B, N, Hkv, D;
-  int kv_head_rows, kv_slot_rows;  // cache layout (KvLayout)
-  int elt_bytes;
-  int32_t* new_lens;
-  int32_t* dev_status;
-};
 hipError_t launch_kv_compact(const CompactArgs& a, hipStream_t stream);
 
 struct KvWriteArgs {
