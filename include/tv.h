@@ -84,9 +84,9 @@ typedef enum {
 
 typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 
-/* Cache-layout flag for the dtype argument of tv_tree_attention,
- * tv_kv_compact, tv_accept_greedy_compact and tv_tree_kv_write: the caches
- * are token-major
+/* Cache-layout flag for the dtype argument of tv_tree_attention (and
+ * tv_tree_attention_parents), tv_kv_compact, tv_accept_greedy_compact and
+ * tv_tree_kv_write: the caches are token-major
  * [num_blocks][block_size][Hkv][D] instead of head-major
  * [num_blocks][Hkv][block_size][D].  Pass (tv_dtype)(TV_BF16 | TV_KV_TOKEN_MAJOR). */
 #define TV_KV_TOKEN_MAJOR 0x100
@@ -167,6 +167,31 @@ TV_API tv_status tv_tree_attention(const void* q, const void* k_cache, const voi
                             const uint64_t* mask, void* out, int32_t B, int32_t N, int32_t Hq,
                             int32_t Hkv, int32_t D, float scale, tv_dtype dtype, void* workspace,
                             size_t workspace_bytes, int32_t* dev_status, hipStream_t stream);
+
+/*
+ * tv_tree_attention_parents -- tv_tree_attention with the tree given as its
+ * parent array instead of the masks: each wave of the attention kernels
+ * builds the ancestor-or-self masks of the tree's nodes itself, while its
+ * first K/V tiles are in flight, so a step needs no tv_build_tree_mask
+ * launch before attention.  ("vLLM-TreeEagle" README, 核心组件 item 1 and
+ * 技术创新点 1: one pass under a mask built at run time for any tree.)
+ *
+ *   parents  [B][N] int32, device, as for tv_build_tree_mask; N <= 64.
+ *   Every other argument, the output and the workspace are tv_tree_attention's;
+ *   the output is bit-identical to tv_build_tree_mask followed by
+ *   tv_tree_attention.
+ * Errors: those of tv_tree_attention, and TV_ERR_UNSUPPORTED for N > 64.
+ * Device: TV_DEV_BAD_CACHE as tv_tree_attention; TV_DEV_BAD_TREE for a
+ * parent array that is not a tree (the sequence is then attended with no
+ * tree key visible, as with the mask tv_build_tree_mask leaves it).
+ */
+TV_API tv_status tv_tree_attention_parents(const void* q, const void* k_cache, const void* v_cache,
+                                           int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                                           int32_t block_size, const int32_t* prefix_lens,
+                                           int32_t max_prefix_len, const int32_t* parents, void* out, int32_t B,
+                                           int32_t N, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                                           tv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                           int32_t* dev_status, hipStream_t stream);
 
 /*
  * Workspace bytes tv_accept_greedy needs (per-chunk partial maxima).  The

@@ -64,6 +64,25 @@ def test_attention_host_checks():
     assert attn(q=P16 + 8) == 5 and attn(k=P16 + 2) == 5 and attn(out=P16 + 4) == 5
 
 
+def test_attention_from_parents_host_checks():
+    """The parents variant: the attention checks, a NULL parent array, and
+    trees of more than 64 nodes (one wave builds the masks) refused."""
+    f = lib.tv_tree_attention_parents
+
+    def call(**kw):
+        a = dict(q=P16, k=P16, v=P16, nb=10, table=P16, mb=8, bs=16, pl=P16, mpl=40, par=P16,
+                 out=P16, B=1, N=8, Hq=8, Hkv=2, D=128, scale=0.0, dt=1, ws=None, wsb=0, st=None,
+                 stream=None)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["nb"], a["table"], a["mb"], a["bs"], a["pl"], a["mpl"], a["par"],
+                 a["out"], a["B"], a["N"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["dt"], a["ws"], a["wsb"],
+                 a["st"], a["stream"])
+    assert call(par=None) == 1 and call(q=None) == 1
+    assert call(dt=7) == 3 and call(D=96) == 4
+    assert call(N=65) == 4 and call(N=300) == 2
+    assert call(q=P16 + 8) == 5
+
+
 def test_attention_workspace_check():
     need = lib.tv_tree_attention_workspace_size(4, 64, 28, 4, 128, 32768)
     if need:

@@ -373,6 +373,50 @@ def test_device_status_bits():
     assert int(st.item()) & T.TV_DEV_BAD_CACHE
 
 
+@pytest.mark.parametrize("which", ["small1", "small2", "small3", "small4", "small5", "full2", "full3", "full4",
+                                   "full5", "small3-token-major", "bad-tree", "n64"])
+def test_attention_from_parents(which):
+    """tv_tree_attention_parents (masks built in the attention kernels from
+    the parent array) against tv_build_tree_mask + tv_tree_attention on the
+    same inputs: bit-identical outputs and device status, and within the
+    oracle's bounds.  'bad-tree' breaks sequence 1's tree (its nodes then see
+    no tree key, as the mask kernel leaves them); 'n64' is the largest tree
+    one wave handles."""
+    tm = which.endswith("token-major")
+    if which == "bad-tree":
+        w = W.make_small(3, seed=11)
+        par = w.parents.copy()
+        par[1, 4] = 7
+        w.parents = par
+    elif which == "n64":
+        w = _variant(3, name="n64", tag=121, tree=("uniform", 64, 9), B=3)
+        assert w.N == 64
+    elif which.startswith("small"):
+        w = W.make_small(int(which[5]))
+    else:
+        w = full(int(which[-1]))
+    log(f"[parity] attention from parents {which} {w.spec.name} B={w.B} N={w.N}")
+    d = upload(w)
+    if tm:
+        d["k"], d["v"] = token_major(d["k"]), token_major(d["v"])
+    st1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mask, _ = T.tv_build_tree_mask(d["parents"], dev_status=st1)
+    out1 = T.tv_tree_attention(d["q"], d["k"], d["v"], d["table"], d["prefix"], w.max_prefix_len, mask,
+                               dev_status=st1, token_major=tm)
+    out2 = T.tv_tree_attention_parents(d["q"], d["k"], d["v"], d["table"], d["prefix"], w.max_prefix_len,
+                                       d["parents"], dev_status=st2, token_major=tm)
+    torch.cuda.synchronize()
+    assert int(st1.item()) == int(st2.item())
+    assert np.array_equal(raw_bits(out1), raw_bits(out2))
+    if which == "bad-tree":
+        assert int(st2.item()) == T.TV_DEV_BAD_TREE
+        return
+    assert int(st2.item()) == 0
+    seqs = list(range(w.B))
+    check_attention(out2, oracle_attention(w, seqs), seqs, w.q.dtype, label=f"from parents {which}")
+
+
 @pytest.mark.parametrize("which", ["small1", "small2", "small3", "small4", "small5", "full2", "full3", "full5",
                                    "small3-token-major", "statuses"])
 def test_accept_compact_fused(which):

@@ -46,6 +46,7 @@ from ._lib import (  # noqa: F401
     tv_kv_compact,
     tv_lm_head_argmax,
     tv_tree_attention,
+    tv_tree_attention_parents,
     tv_tree_attention_workspace_size,
     tv_tree_kv_write,
 )

@@ -56,6 +56,10 @@ def _load() -> ctypes.CDLL:
                                        _c_ptr, _c_i32, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32,
                                        _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_ptr, _c_size,
                                        _c_ptr, _c_ptr]),
+        "tv_tree_attention_parents": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_ptr, _c_i32, _c_i32,
+                                               _c_ptr, _c_i32, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32,
+                                               _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_ptr, _c_size,
+                                               _c_ptr, _c_ptr]),
         "tv_accept_greedy_workspace_size": (_c_size, [_c_i32] * 3),
         "tv_accept_greedy_compact": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
                                               _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_i32, _c_ptr,
@@ -209,6 +213,24 @@ def tv_tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     [num_blocks, 16, Hkv, D]; bf16 or fp32, same as q); block_table int32
     [B, max_blocks]; prefix_lens int32 [B]; mask from tv_build_tree_mask.
     Returns out [B, N, Hq, D] in q's dtype."""
+    return _tree_attention(q, k_cache, v_cache, block_table, prefix_lens, max_prefix_len, mask, None, out,
+                           scale, workspace, dev_status, token_major)
+
+
+def tv_tree_attention_parents(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_table: torch.Tensor, prefix_lens: torch.Tensor, max_prefix_len: int,
+                              parents: torch.Tensor, out: Optional[torch.Tensor] = None, scale: float = 0.0,
+                              workspace: Optional[torch.Tensor] = None,
+                              dev_status: Optional[torch.Tensor] = None,
+                              token_major: bool = False) -> torch.Tensor:
+    """tv_tree_attention with the tree's parents (int32 [B, N], N <= 64) in
+    place of the masks, which the attention kernels build themselves."""
+    return _tree_attention(q, k_cache, v_cache, block_table, prefix_lens, max_prefix_len, None, parents, out,
+                           scale, workspace, dev_status, token_major)
+
+
+def _tree_attention(q, k_cache, v_cache, block_table, prefix_lens, max_prefix_len, mask, parents, out, scale,
+                    workspace, dev_status, token_major):
     dt = _tv_dtype(q)
     _dev(q, "q", q.dtype)
     B, N, Hq, D = q.shape
@@ -221,7 +243,10 @@ def tv_tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_blocks]")
     _dev(prefix_lens, "prefix_lens", torch.int32, (B,))
-    _dev(mask, "mask", (torch.int64, torch.uint64), (B, N, (N + 63) // 64))
+    if mask is not None:
+        _dev(mask, "mask", (torch.int64, torch.uint64), (B, N, (N + 63) // 64))
+    else:
+        _dev(parents, "parents", torch.int32, (B, N))
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype, q.shape)
@@ -231,10 +256,11 @@ def tv_tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if dev_status is not None:
         _dev(dev_status, "dev_status", torch.int32)
-    _check("tv_tree_attention", lib.tv_tree_attention(
+    name = "tv_tree_attention" if mask is not None else "tv_tree_attention_parents"
+    _check(name, getattr(lib, name)(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_table), block_table.shape[1], bs,
-        _ptr(prefix_lens), int(max_prefix_len), _ptr(mask), _ptr(out), B, N, Hq, Hkv, D,
-        float(scale), dt | (TV_KV_TOKEN_MAJOR if token_major else 0), _ptr(workspace), ws_bytes,
+        _ptr(prefix_lens), int(max_prefix_len), _ptr(mask if mask is not None else parents), _ptr(out), B, N, Hq,
+        Hkv, D, float(scale), dt | (TV_KV_TOKEN_MAJOR if token_major else 0), _ptr(workspace), ws_bytes,
         _ptr(dev_status), _stream(q)))
     return out
 

@@ -414,9 +414,11 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     const int r_me = row0 + col;
     bf16x8 qreg[C::kKs];
     uint64_t mw[4];
+    const int node = (r_me < R ? r_me : R - 1) / g;
+    int par_me = -1;  // without masks: this lane's node of the tree (lane < N), its parent
     {
       const int rr = r_me < R ? r_me : R - 1;
-      const int node = rr / g, hg = rr % g;
+      const int hg = rr % g;
       const u32x4* qp = reinterpret_cast<const u32x4*>(
           static_cast<const uint16_t*>(a.q) +
           ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D);
@@ -426,9 +428,15 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
         if (r_me < R) v = qp[kk * 2 + hh];
         qreg[kk] = __builtin_bit_cast(bf16x8, v);
       }
-      const uint64_t* mrow = a.mask + (static_cast<size_t>(b) * a.N + node) * W;
+      if (a.mask) {
+        const uint64_t* mrow = a.mask + (static_cast<size_t>(b) * a.N + node) * W;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) mw[w] = (w < W) ? mrow[w] : 0ull;
+        for (int w = 0; w < 4; ++w) mw[w] = (w < W) ? mrow[w] : 0ull;
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mw[w] = 0ull;
+        if (lane < a.N) par_me = a.parents[static_cast<size_t>(b) * a.N + lane];
+      }
     }
 
     // ---- block ids: scalar loads through the constant address space, which
@@ -625,6 +633,15 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
 #pragma unroll
     for (int i = 0; i < C::kStages - 1; ++i)
       if (t0 + i < t1) issue_tile(i, t0 + i, pid[2 * i], pid[2 * i + 1]);
+    if (!a.mask && t1 * kTile > P) {
+      // masks from the parents, while the first tiles are in flight (only
+      // pieces that reach the tree's keys use them)
+      bool bad_tree;
+      const uint64_t anc = wave_tree_mask(par_me, a.N, lane, &bad_tree);
+      mw[0] = __shfl(anc, node, 64);
+      mw[1] = mw[2] = mw[3] = 0ull;
+      if (bad_tree && tid == 0) report(a.dev_status, TV_DEV_BAD_TREE);
+    }
     // tile t0 (and the query and mask loads issued before it)
     wait_tile(min(C::kStages - 2, t1 - 1 - t0));
     __asm__ volatile("" ::: "memory");

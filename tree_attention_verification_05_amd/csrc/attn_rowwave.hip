@@ -48,6 +48,14 @@ __global__ __launch_bounds__(kWaves * 64) void attn_rowwave_kernel(AttnArgs a) {
   __syncthreads();
   if (!active) return;  // no barrier below this point
 
+  const uint64_t* mrow = a.mask ? a.mask + (static_cast<size_t>(b) * a.N + i) * W : nullptr;
+  uint64_t own = 0;  // without masks: node i's word, built from the parents (N <= 64)
+  if (!a.mask) {
+    bool bad_tree;
+    const int p = lane < a.N ? a.parents[static_cast<size_t>(b) * a.N + lane] : -1;
+    own = __shfl(wave_tree_mask(p, a.N, lane, &bad_tree), i, 64);
+    if (bad_tree && lane == 0) report(a.dev_status, TV_DEV_BAD_TREE);
+  }
   const int P = a.prefix_lens[b];
   float acc[R];
 #pragma unroll
@@ -58,7 +66,6 @@ __global__ __launch_bounds__(kWaves * 64) void attn_rowwave_kernel(AttnArgs a) {
     for (int r = 0; r < R; ++r) Elt<T>::store(out + lane + 64 * r, 0.f);
     return;
   }
-  const uint64_t* mrow = a.mask + (static_cast<size_t>(b) * a.N + i) * W;
   const int32_t* table = a.block_table + static_cast<size_t>(b) * a.max_blocks;
   const int total = P + a.N;
   float m = -INFINITY, l = 0.f;
@@ -71,7 +78,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_rowwave_kernel(AttnArgs a) {
       bool vis = true;
       if (t >= P) {
         const int j = t - P;
-        vis = (mrow[j >> 6] >> (j & 63)) & 1ull;
+        vis = ((mrow ? mrow[j >> 6] : own) >> (j & 63)) & 1ull;
       }
       const int blk = table[t / kBlockSize];
       if (blk < 0 || blk >= a.num_blocks) {

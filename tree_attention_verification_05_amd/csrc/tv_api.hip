@@ -49,13 +49,18 @@ size_t tv_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_
   return attention_mfma_workspace_bytes(B, N, Hq, Hkv, D, max_prefix_len);
 }
 
-tv_status tv_tree_attention(const void* q, const void* k_cache, const void* v_cache,
-                            int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
-                            int32_t block_size, const int32_t* prefix_lens, int32_t max_prefix_len,
-                            const uint64_t* mask, void* out, int32_t B, int32_t N, int32_t Hq,
-                            int32_t Hkv, int32_t D, float scale, tv_dtype dtype, void* workspace,
-                            size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
-  if (!q || !k_cache || !v_cache || !block_table || !prefix_lens || !mask || !out) return TV_ERR_NULL;
+}  // extern "C"
+
+// tv_tree_attention and tv_tree_attention_parents: the same checks and
+// launch, with the masks given (mask) or built from the parents in the
+// attention kernels (parents, N <= 64)
+static tv_status tree_attention(const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                                const int32_t* block_table, int32_t max_blocks, int32_t block_size,
+                                const int32_t* prefix_lens, int32_t max_prefix_len, const uint64_t* mask,
+                                const int32_t* parents, void* out, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                                int32_t D, float scale, tv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                int32_t* dev_status, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !prefix_lens || !(mask || parents) || !out) return TV_ERR_NULL;
   const bool token_major = (dtype & TV_KV_TOKEN_MAJOR) != 0;
   dtype = static_cast<tv_dtype>(dtype & ~TV_KV_TOKEN_MAJOR);
   if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_DTYPE;
@@ -64,6 +69,7 @@ tv_status tv_tree_attention(const void* q, const void* k_cache, const void* v_ca
     return TV_ERR_SHAPE;
   if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
   if (block_size != kBlockSize) return TV_ERR_UNSUPPORTED;
+  if (!mask && N > 64) return TV_ERR_UNSUPPORTED;  // one wave builds the masks
   if (static_cast<long>(max_prefix_len) + N > static_cast<long>(max_blocks) * block_size)
     return TV_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
@@ -72,7 +78,7 @@ tv_status tv_tree_attention(const void* q, const void* k_cache, const void* v_ca
   if (need > 0 && (!workspace || workspace_bytes < need)) return TV_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return TV_ERR_ALIGN;
 
-  AttnArgs a;
+  AttnArgs a{};
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -82,6 +88,7 @@ tv_status tv_tree_attention(const void* q, const void* k_cache, const void* v_ca
   a.prefix_lens = prefix_lens;
   a.max_prefix_len = max_prefix_len;
   a.mask = mask;
+  a.parents = mask ? nullptr : parents;
   a.out = out;
   a.B = B;
   a.N = N;
@@ -96,6 +103,32 @@ tv_status tv_tree_attention(const void* q, const void* k_cache, const void* v_ca
   a.dev_status = dev_status;
   if (dtype == TV_BF16) return launched(launch_attention_mfma(a, stream));
   return launched(launch_attention_rowwave(a, dtype, stream));
+}
+
+extern "C" {
+
+tv_status tv_tree_attention(const void* q, const void* k_cache, const void* v_cache,
+                            int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                            int32_t block_size, const int32_t* prefix_lens, int32_t max_prefix_len,
+                            const uint64_t* mask, void* out, int32_t B, int32_t N, int32_t Hq,
+                            int32_t Hkv, int32_t D, float scale, tv_dtype dtype, void* workspace,
+                            size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
+  if (!mask) return TV_ERR_NULL;
+  return tree_attention(q, k_cache, v_cache, num_blocks, block_table, max_blocks, block_size, prefix_lens,
+                        max_prefix_len, mask, nullptr, out, B, N, Hq, Hkv, D, scale, dtype, workspace,
+                        workspace_bytes, dev_status, stream);
+}
+
+tv_status tv_tree_attention_parents(const void* q, const void* k_cache, const void* v_cache,
+                                    int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                                    int32_t block_size, const int32_t* prefix_lens, int32_t max_prefix_len,
+                                    const int32_t* parents, void* out, int32_t B, int32_t N, int32_t Hq,
+                                    int32_t Hkv, int32_t D, float scale, tv_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
+  if (!parents) return TV_ERR_NULL;
+  return tree_attention(q, k_cache, v_cache, num_blocks, block_table, max_blocks, block_size, prefix_lens,
+                        max_prefix_len, nullptr, parents, out, B, N, Hq, Hkv, D, scale, dtype, workspace,
+                        workspace_bytes, dev_status, stream);
 }
 
 size_t tv_accept_greedy_workspace_size(int32_t B, int32_t N, int32_t V) {

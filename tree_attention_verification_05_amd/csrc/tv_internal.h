@@ -56,6 +56,38 @@ __device__ __forceinline__ void report(int32_t* dev_status, int bits) {
   if (dev_status) atomicOr(dev_status, bits);
 }
 
+// Ancestor-or-self bits of every node of one tree of N <= 64 nodes, computed
+// by a whole wave ("vLLM-TreeEagle" README, 核心组件 item 1 and 技术创新点 1:
+// the mask follows the tree, whatever its shape).  Lane l passes node l's
+// parent (anything for l >= N).  Six rounds of pointer jumping: each node ORs
+// in the bits of the node its jump pointer names and then jumps to that
+// node's jump target, so after round r it holds its ancestors up to 2^r - 1
+// edges up, and after six every depth a 64-node tree can have.  Lane l gets
+// node l's word (0 for l >= N).  When the parents are not a tree
+// (parent[0] != -1, or parent[i] outside [0, i)) every lane gets 0 and *bad
+// is set, as the mask kernel leaves such a sequence.  Every lane of the wave
+// must call it.
+__device__ __forceinline__ uint64_t wave_tree_mask(int p, int N, int lane, bool* bad) {
+  const bool exists = lane < N;
+  const bool ok = !exists || (lane == 0 ? p == -1 : (p >= 0 && p < lane));
+  const bool any_bad = __builtin_amdgcn_ballot_w64(!ok) != 0;
+  uint64_t anc = exists ? (1ull << lane) : 0ull;
+  int jump = (exists && lane > 0 && ok) ? p : -1;
+  // (rounds stop early once no node has an ancestor left to add: a tree of
+  // depth d needs ceil(log2(d + 1)) of them)
+  for (int r = 0; r < 6 && __builtin_amdgcn_ballot_w64(jump >= 0) != 0; ++r) {
+    const int src = jump >= 0 ? jump : lane;
+    const uint64_t up = __shfl(anc, src, 64);
+    const int up_jump = __shfl(jump, src, 64);
+    if (jump >= 0) {
+      anc |= up;
+      jump = up_jump;
+    }
+  }
+  *bad = any_bad;
+  return any_bad ? 0ull : anc;
+}
+
 // ---- ordered 64-bit selection keys (one definition for every kernel that
 // picks a maximum with the lowest index winning ties) ----
 // Orders floats as unsigned integers; -0.0 and +0.0 map to the same value.
@@ -106,7 +138,8 @@ struct AttnArgs {
   int max_blocks;
   const int32_t* prefix_lens;
   int max_prefix_len;
-  const uint64_t* mask;
+  const uint64_t* mask;     // ancestor masks, or NULL:
+  const int32_t* parents;   // the masks are built from the parents (N <= 64)
   void* out;
   int B, N, Hq, Hkv, D;
   int kv_head_rows, kv_slot_rows;  // cache layout (KvLayout)
