@@ -319,6 +319,37 @@ def main():
     q, k, v, depth, table, prefix, status = sb.q, sb.k, sb.v, sb.depth, sb.table, sb.prefix, sb.status
     logits, parents, dt = sb.logits, sb.parents, sb.dt
 
+    def time_call(fn):
+        """W warm-up calls, then K calls after an eviction each, one event
+        pair around each call; the times in ms."""
+        for _ in range(args.warmup):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for s in range(args.steps):
+            evict()
+            ev[s][0].record(stream)
+            fn()
+            ev[s][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([e[0].elapsed_time(e[1]) for e in ev])
+
+    # ---- the boundary's separate calls that the step's two calls fuse (the
+    # mask kernel, attention on given masks, greedy acceptance, compaction),
+    # each on its own ----
+    sep_ms = {
+        "tv_build_tree_mask": time_call(lambda: T.tv_build_tree_mask(parents, mask=sb.mask, depth=depth,
+                                                                     dev_status=status)),
+        "tv_tree_attention": time_call(lambda: T.tv_tree_attention(q, k, v, table, prefix, w.max_prefix_len, sb.mask,
+                                                                   out=sb.out, workspace=sb.attn_ws,
+                                                                   dev_status=status)),
+        "tv_accept_greedy": time_call(lambda: T.tv_accept_greedy(logits, sb.draft, parents, accept_len=sb.acc_len,
+                                                                 accepted_nodes=sb.acc_nodes, bonus_token=sb.bonus,
+                                                                 target_argmax=sb.am, workspace=sb.acc_ws,
+                                                                 dev_status=status)),
+        "tv_kv_compact": time_call(lambda: T.tv_kv_compact(k, v, table, prefix, sb.acc_nodes, sb.acc_len,
+                                                           new_lens=sb.new_lens, dev_status=status)),
+    }
+
     # ---- the tree K/V write (the step's upstream neighbour, before the mask
     # and attention): timed on its own, K calls after an eviction each ----
     k_new, v_new = W.tree_kv_inputs(spec, args.seed)
@@ -492,6 +523,17 @@ def main():
 
     # roofline of the dominant call of the main workload's step
     work = step_work(w, sb.acc_len.cpu().numpy(), sb.acc_nodes.cpu().numpy())
+    fused_into = {"tv_build_tree_mask": "tv_tree_attention_parents", "tv_tree_attention": "tv_tree_attention_parents",
+                  "tv_accept_greedy": "tv_accept_greedy_compact", "tv_kv_compact": "tv_accept_greedy_compact"}
+    for n, t_ms in sep_ms.items():
+        t_us = float(t_ms.mean()) * 1e3
+        rec = {"us": round(t_us, 3), "us_median": round(float(np.median(t_ms)) * 1e3, 3),
+               "bytes": int(work[n]["bytes"]), "GB_s": round(work[n]["bytes"] / (t_us * 1e-6) / 1e9, 1),
+               "in_step": False, "step_call": fused_into[n]}
+        if work[n].get("flops"):
+            rec["flops"] = int(work[n]["flops"])
+            rec["TFLOP_s"] = round(work[n]["flops"] / (t_us * 1e-6) / 1e12, 2)
+        extra[n] = rec
     dom = max(STEP_CALLS, key=lambda n: kern[n]["us"])
     d_us = kern[dom]["us"]
     bound = work[dom].get("bound", "hbm")

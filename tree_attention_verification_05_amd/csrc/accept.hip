@@ -118,6 +118,8 @@ __global__ __launch_bounds__(kThreads) void accept_scan_kernel(const float* __re
   }
 }
 
+// kCompact: the fused call (tv_accept_greedy_compact) also compacts
+template <bool kCompact>
 __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int chunks) {
   __shared__ int s_par[TV_MAX_NODES], s_tok[TV_MAX_NODES], s_am[TV_MAX_NODES];
   __shared__ int s_ok[TV_MAX_NODES], s_dep[TV_MAX_NODES], s_on[TV_MAX_NODES];
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const CompactArgs& c = a.compact;
-  const bool fuse = c.k_cache != nullptr;
+  constexpr bool fuse = kCompact;
   const uint64_t* keys = static_cast<const uint64_t*>(a.workspace);
   const size_t base = static_cast<size_t>(b) * N;
   // every (node, chunk) key of the sequence is contiguous in the workspace;
@@ -302,7 +304,10 @@ hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
                      stream, a.logits, a.V, s.chunk, s.chunks, static_cast<uint64_t*>(a.workspace));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_walk_kernel, dim3(a.B), dim3(kThreads), 0, stream, a, s.chunks);
+  if (a.compact.k_cache)
+    hipLaunchKernelGGL(accept_walk_kernel<true>, dim3(a.B), dim3(kThreads), 0, stream, a, s.chunks);
+  else
+    hipLaunchKernelGGL(accept_walk_kernel<false>, dim3(a.B), dim3(kThreads), 0, stream, a, s.chunks);
   return hipGetLastError();
 }
 
