@@ -25,24 +25,27 @@ template <typename T>
 struct Vec4;
 template <>
 struct Vec4<float> {
-  typedef float4 type;
-  __device__ static void load(const float* p, float (&x)[4]) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
+  typedef float4 raw;  // four elements as loaded
+  __device__ static raw load_raw(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static void unpack(const raw& v, float (&x)[4]) {
     x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
   }
+  __device__ static void load(const float* p, float (&x)[4]) { unpack(load_raw(p), x); }
   __device__ static void store(float* p, const float (&x)[4]) {
     *reinterpret_cast<float4*>(p) = float4{x[0], x[1], x[2], x[3]};
   }
 };
 template <>
 struct Vec4<uint16_t> {
-  __device__ static void load(const uint16_t* p, float (&x)[4]) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
+  typedef uint2 raw;  // four elements as loaded
+  __device__ static raw load_raw(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+  __device__ static void unpack(const raw& v, float (&x)[4]) {
     x[0] = __uint_as_float(v.x << 16);
     x[1] = __uint_as_float(v.x & 0xFFFF0000u);
     x[2] = __uint_as_float(v.y << 16);
     x[3] = __uint_as_float(v.y & 0xFFFF0000u);
   }
+  __device__ static void load(const uint16_t* p, float (&x)[4]) { unpack(load_raw(p), x); }
   __device__ static void store(uint16_t* p, const float (&x)[4]) {
     uint2 v;
     v.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
@@ -58,8 +61,50 @@ __global__ __launch_bounds__(kThreads) void tree_kv_write_kernel(KvWriteArgs a) 
   const int tid = threadIdx.x;
   const int D = a.D, h = D / 2;
   const size_t nidx = static_cast<size_t>(b) * a.N + node;
+  // the chain that fixes where and how the rows go starts first
   const int P = a.prefix_lens[b];
   int d = a.depth[nidx];
+  // D is 64 or 128: items decode with shifts
+  const int quads = h / 4;  // groups of four pairs per head row
+  const int qsh = __builtin_ctz(quads), csh = qsh + 1;  // log2 of quads and of D / 4
+  const T* q = static_cast<const T*>(a.q) + nidx * a.Hq * D;
+  T* qo = static_cast<T*>(a.q_out) + nidx * a.Hq * D;
+  const T* kn = static_cast<const T*>(a.k_new) + nidx * a.Hkv * D;
+  const T* vn = static_cast<const T*>(a.v_new) + nidx * a.Hkv * D;
+  // items: Hq query rows, then Hkv key rows (rotated), then Hkv value rows (copied)
+  const int rot_items = (a.Hq + a.Hkv) * quads;
+  const int items = rot_items + a.Hkv * (D / 4);
+  // the inputs of an item as loaded: the two halves r1, r2 of a rotated
+  // row, or r1 of a value row
+  using Raw = typename Vec4<T>::raw;
+  // Both loads are unconditional, from addresses that are always inside the
+  // inputs (a value row loads its one address twice; past the last item, q's
+  // first four elements), so no branch merges loaded values and nothing
+  // waits for a load before its item is finished.
+  auto fetch = [&](int it, Raw& r1, Raw& r2) __attribute__((always_inline)) {
+    const T* src = q;
+    const T* src2 = q;
+    if (it < rot_items) {
+      const int row = it >> qsh;
+      src = (row < a.Hq ? q + row * D : kn + (row - a.Hq) * D) + (it & (quads - 1)) * 4;
+      src2 = src + h;
+    } else if (it < items) {
+      const int v_it = it - rot_items;
+      src = vn + (v_it >> csh) * D + (v_it & ((D / 4) - 1)) * 4;
+      src2 = src;
+    }
+    r1 = Vec4<T>::load_raw(src);
+    r2 = Vec4<T>::load_raw(src2);
+  };
+  // The rows do not depend on the prefix length, depth or block table: this
+  // thread's first four items are loaded before those, so their latencies
+  // overlap (the rest of a large row set follows the same loop later).
+  Raw p1a, p2a, p1b, p2b, p1c, p2c, p1d, p2d;
+  fetch(tid, p1a, p2a);
+  fetch(tid + kThreads, p1b, p2b);
+  fetch(tid + 2 * kThreads, p1c, p2c);
+  fetch(tid + 3 * kThreads, p1d, p2d);
+
   // where the node's K/V rows go: logical position P + node
   const long t = static_cast<long>(P) + node;
   int blk = -1;
@@ -80,26 +125,20 @@ __global__ __launch_bounds__(kThreads) void tree_kv_write_kernel(KvWriteArgs a) 
   }
   __syncthreads();
 
-  const int quads = h / 4;  // groups of four pairs per head row
-  const T* q = static_cast<const T*>(a.q) + nidx * a.Hq * D;
-  T* qo = static_cast<T*>(a.q_out) + nidx * a.Hq * D;
-  const T* kn = static_cast<const T*>(a.k_new) + nidx * a.Hkv * D;
-  const T* vn = static_cast<const T*>(a.v_new) + nidx * a.Hkv * D;
   const bool write_cache = blk >= 0 && blk < a.num_blocks;
   const int slot = static_cast<int>(t % kBlockSize);
   T* kc = static_cast<T*>(a.k_cache);
   T* vc = static_cast<T*>(a.v_cache);
-  // items: Hq query rows, then Hkv key rows (rotated), then Hkv value rows (copied)
-  const int items = (a.Hq + a.Hkv) * quads + a.Hkv * (D / 4);
-  for (int it = tid; it < items; it += kThreads) {
-    if (it < (a.Hq + a.Hkv) * quads) {
-      const int row = it / quads, j = (it % quads) * 4;
+  // rotate (or copy) an item whose inputs are loaded, and store it
+  auto finish = [&](int it, const Raw& r1, const Raw& r2) __attribute__((always_inline)) {
+    float x1[4], x2[4];
+    Vec4<T>::unpack(r1, x1);
+    Vec4<T>::unpack(r2, x2);
+    if (it < rot_items) {
+      const int row = it >> qsh, j = (it & (quads - 1)) * 4;
       const bool is_q = row < a.Hq;
-      if (!is_q && !write_cache) continue;
-      const T* src = is_q ? q + row * D : kn + (row - a.Hq) * D;
-      float x1[4], x2[4], y1[4], y2[4];
-      Vec4<T>::load(src + j, x1);
-      Vec4<T>::load(src + j + h, x2);
+      if (!is_q && !write_cache) return;
+      float y1[4], y2[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float c = s_cos[j + e], s = s_sin[j + e];
@@ -110,13 +149,20 @@ __global__ __launch_bounds__(kThreads) void tree_kv_write_kernel(KvWriteArgs a) 
                     : kc + kv_row(blk, row - a.Hq, slot, a.Hkv, a.kv_head_rows, a.kv_slot_rows) * D;
       Vec4<T>::store(dst + j, y1);
       Vec4<T>::store(dst + j + h, y2);
-    } else if (write_cache) {
-      const int v_it = it - (a.Hq + a.Hkv) * quads;
-      const int head = v_it / (D / 4), j = (v_it % (D / 4)) * 4;
-      float x[4];
-      Vec4<T>::load(vn + head * D + j, x);
-      Vec4<T>::store(vc + kv_row(blk, head, slot, a.Hkv, a.kv_head_rows, a.kv_slot_rows) * D + j, x);
+    } else if (it < items && write_cache) {
+      const int v_it = it - rot_items;
+      const int head = v_it >> csh, j = (v_it & ((D / 4) - 1)) * 4;
+      Vec4<T>::store(vc + kv_row(blk, head, slot, a.Hkv, a.kv_head_rows, a.kv_slot_rows) * D + j, x1);
     }
+  };
+  finish(tid, p1a, p2a);
+  finish(tid + kThreads, p1b, p2b);
+  finish(tid + 2 * kThreads, p1c, p2c);
+  finish(tid + 3 * kThreads, p1d, p2d);
+  for (int it = tid + 4 * kThreads; it < items; it += kThreads) {
+    Raw r1, r2;
+    fetch(it, r1, r2);
+    finish(it, r1, r2);
   }
 }
 
