@@ -36,7 +36,8 @@ constexpr int kTargetBlocksManyRows = 2048;  // twice as many from 512 rows on
 constexpr long kManyRows = 512;
 constexpr int kDrawMinChunk = 2048;   // draw: floats per workgroup at least
 constexpr int kDrawMaxChunk = 16384;  // draw: at most (sizes the LDS bitmap)
-constexpr int kPickThreads = 256;
+constexpr int kPickThreads = 256;   // four sequences per pick workgroup, one per wave
+constexpr int kStatsBatch = 16;     // walk: chunk statistics of a row loaded together
 
 struct Split {
   int chunk;   // floats per chunk (multiple of 4)
@@ -205,9 +206,15 @@ __global__ __launch_bounds__(kThreads) void stoch_walk_kernel(StochArgs a, float
   for (int i = tid; i < N; i += kThreads) {
     const float2* st = stats + (base + i) * chunks;
     float m = -INFINITY, s = 0.f;
-    for (int c = 0; c < chunks; ++c) {
-      const float2 v = st[c];
-      merge_ms(m, s, v.x, v.y);
+    // sixteen chunk statistics at a time, all in flight together (from
+    // clamped indices, so no load is conditional), then merged in chunk order
+    for (int c0 = 0; c0 < chunks; c0 += kStatsBatch) {
+      float2 v[kStatsBatch];
+#pragma unroll
+      for (int k = 0; k < kStatsBatch; ++k) v[k] = st[min(c0 + k, chunks - 1)];
+#pragma unroll
+      for (int k = 0; k < kStatsBatch; ++k)
+        if (c0 + k < chunks) merge_ms(m, s, v[k].x, v[k].y);
     }
     s_m[i] = m;
     s_s[i] = s;
@@ -386,16 +393,23 @@ __global__ __launch_bounds__(kThreads) void stoch_draw_kernel(StochArgs a, float
   }
 }
 
+// One wave per sequence: lanes load the chunk keys together, and a wave
+// maximum picks the best (the keys order by value, then lower index).
 __global__ __launch_bounds__(kPickThreads) void stoch_pick_kernel(int B, int chunks, const uint64_t* __restrict__ keys,
                                                                   int32_t* __restrict__ bonus) {
-  const int b = blockIdx.x * kPickThreads + threadIdx.x;
-  if (b >= B) return;
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * (kPickThreads / 64) + static_cast<int>(threadIdx.x >> 6);
+  if (b >= B) return;  // the whole wave
   uint64_t best = 0ull;
-  for (int c = 0; c < chunks; ++c) {
+  for (int c = lane; c < chunks; c += 64) {
     const uint64_t k = keys[static_cast<size_t>(b) * chunks + c];
     best = k > best ? k : best;
   }
-  bonus[b] = static_cast<int>(~static_cast<uint32_t>(best & 0xFFFFFFFFu));
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t w = __shfl_xor(best, o, 64);
+    best = w > best ? w : best;
+  }
+  if (lane == 0) bonus[b] = static_cast<int>(~static_cast<uint32_t>(best & 0xFFFFFFFFu));
 }
 
 }  // namespace
@@ -424,7 +438,8 @@ hipError_t launch_accept_stochastic(const StochArgs& a, hipStream_t stream) {
                      l.dr.chunk, l.dr.chunks, static_cast<const StopRecord*>(stop), keys);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(stoch_pick_kernel, dim3((a.B + kPickThreads - 1) / kPickThreads), dim3(kPickThreads), 0,
+  constexpr int kPickSeqs = kPickThreads / 64;
+  hipLaunchKernelGGL(stoch_pick_kernel, dim3((a.B + kPickSeqs - 1) / kPickSeqs), dim3(kPickThreads), 0,
                      stream, a.B, l.dr.chunks, static_cast<const uint64_t*>(keys), a.bonus_token);
   return hipGetLastError();
 }
