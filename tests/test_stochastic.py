@@ -208,6 +208,27 @@ def test_root_only_and_single_child():
     assert al.tolist() == [0, 1]
 
 
+def test_many_chunks_per_row():
+    """A Qwen2-sized vocabulary (V = 152064) over a few short rows: each row's
+    statistics span 19 chunks (the walk loads them in batches of 16, so a
+    second, partial batch follows) and every sequence draws over 75 chunks
+    (more than one key per lane in the pick's wave reduction).  Five
+    sequences also give the pick a second workgroup with three idle waves."""
+    rng = np.random.default_rng(11)
+    B, N, V = 5, 6, 152064
+    par = np.tile(np.array([-1, 0, 0, 1, 1, 2], np.int32), (B, 1))
+    tok = rng.integers(0, V, size=(B, N)).astype(np.int32)
+    tok[:, 0] = 0
+    lg = (rng.normal(size=(B, N, V)) * 2).astype(np.float32)
+    for b in range(B):
+        for c in (1, 3):          # a likely path root -> 1 -> 3
+            lg[b, par[b, c], tok[b, c]] += 20.0
+    u = rng.random((B, N), dtype=np.float32)
+    e = rng.standard_exponential((B, V)).astype(np.float32)
+    al, _, _ = compare(lg, tok, par, 0.8, u, e, label="many-chunks")
+    assert al.max() >= 1
+
+
 def test_invalid_sequences_fall_back_to_the_root_draw():
     w, x, tok = small_inputs(3, seed=5)
     tok = tok.copy()
