@@ -268,10 +268,18 @@ __device__ __forceinline__ int tiles_of(const AttnArgs& a, int P) { return (P + 
 // robin (u % 8).  With several row chunks per KV head, the chunks of one
 // (share, KV head) are given to workgroups u, u + 8, ... of one XCD, which
 // start together and share the K/V tiles through that XCD's L2.
+// Every sequence also carries kSeqCostTiles positions before its tiles in
+// the flat range: a share pays for each sequence boundary it crosses (the
+// piece's epilogue stores, the next piece's query loads and its pipeline
+// refill), measured at 7-9 us, about six tiles, per extra piece on the
+// batched and 70B-chain workloads.  Shares stay equal in positions, so one
+// that crosses more boundaries gets fewer tiles and all end together.
+constexpr int kSeqCostTiles = 6;
+
 struct Start {
-  int S, T;        // flat tiles, share length
-  int b, base;     // sequence holding the share's first tile (-1: none), and its first lane tile
-  int ntiles;      // tiles of sequence b
+  int S, T;        // flat positions (tiles plus per-sequence cost), share length
+  int b, base;     // sequence holding the share's first position (-1: none), and its first position
+  int ntiles;      // tiles of sequence b (its tiles start at base + kSeqCostTiles)
 };
 
 template <int NW>
@@ -284,7 +292,7 @@ __device__ Start balanced_start(const AttnArgs& a, int shares, int share_idx, in
   for (int b = tid; b < a.B; b += NW * 64) {
     const int P = a.prefix_lens[b];
     if (P < 0 || P > a.max_prefix_len) report(a.dev_status, TV_DEV_BAD_CACHE);
-    local += tiles_of(a, clamp_prefix(a, P));
+    local += kSeqCostTiles + tiles_of(a, clamp_prefix(a, P));
   }
   local = wave_sum(local);
   if (lane == 0) red[wave] = local;
@@ -305,7 +313,7 @@ __device__ Start balanced_start(const AttnArgs& a, int shares, int share_idx, in
   int running = 0;
   for (int c = 0; c < a.B; c += NW * 64) {
     const int b = c + tid;
-    const int v = b < a.B ? tiles_of(a, clamp_prefix(a, a.prefix_lens[b])) : 0;
+    const int v = b < a.B ? kSeqCostTiles + tiles_of(a, clamp_prefix(a, a.prefix_lens[b])) : 0;
     const int incl = wave_inclusive_scan(v, lane);
     if (lane == 63) red[wave] = incl;
     __syncthreads();
@@ -327,7 +335,7 @@ __device__ Start balanced_start(const AttnArgs& a, int shares, int share_idx, in
   }
   st.b = found[0];
   st.base = found[1];
-  st.ntiles = found[2];
+  st.ntiles = found[2] - kSeqCostTiles;
   return st;
 }
 
@@ -786,33 +794,43 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     hdr[1] = st.T;
   }
   // the cut at this share's start, for the merge: the sequence it splits,
-  // that sequence's first lane tile and tile count, and the cut's rank among
-  // the sequence's cuts (-1: the share starts at a sequence start or past the end)
+  // the flat position of that sequence's first tile and its tile count, and
+  // the cut's rank among the sequence's cuts (-1: the share starts at or
+  // before a sequence's first tile, or past the end)
   if (lane_id == 0 && tid == 0) {
     int4 cut = {-1, 0, 0, 0};
-    if (st.b >= 0 && share * st.T > st.base) cut = int4{st.b, st.base, st.ntiles, share - st.base / st.T - 1};
+    const int first_tile = st.base + kSeqCostTiles;
+    if (st.b >= 0 && share * st.T > first_tile)
+      cut = int4{st.b, first_tile, st.ntiles, share - first_tile / st.T - 1};
     reinterpret_cast<int4*>(hdr + 4)[share] = cut;
   }
   if (st.b < 0) return;  // whole workgroup: the lane's tiles ended before this share
+  // flat positions [j, j1) of this share; sequence b's tiles occupy
+  // [seq_base + kSeqCostTiles, seq_base + kSeqCostTiles + ntiles)
   const int j1 = min(st.S, share * st.T + st.T);
   int j = share * st.T;
   int b = st.b, seq_base = st.base;
   int Praw = a.prefix_lens[b];
   int ntiles = tiles_of(a, clamp_prefix(a, Praw));
-  bool first = true;
   const int no_ids[2 * C::kStages] = {};
-  while (j < j1) {
-    while (j >= seq_base + ntiles) {  // the share continues into the next sequence
-      seq_base += ntiles;
-      ++b;
-      Praw = a.prefix_lens[b];
-      ntiles = tiles_of(a, clamp_prefix(a, Praw));
-    }
-    const int t0 = j - seq_base;
+  for (;;) {
+    const int first_tile = seq_base + kSeqCostTiles;
+    if (j < first_tile) j = first_tile;  // the sequence's cost positions hold no tiles
+    if (j >= j1) break;
+    const int t0 = j - first_tile;
     const int t1 = min(ntiles, t0 + (j1 - j));
-    run_piece(b, kh, rc, Praw, t0, t1, t0 == 0 && t1 == ntiles, first ? v : G + v, no_ids, false);
+    // a cut piece leaves its state in slot v when it starts where the share
+    // starts (it continues a sequence from the share before, or its sequence
+    // starts exactly there), in G + v when its sequence starts inside the share
+    run_piece(b, kh, rc, Praw, t0, t1, t0 == 0 && t1 == ntiles, j == share * st.T ? v : G + v, no_ids,
+              false);
     j += t1 - t0;
-    first = false;
+    if (j >= j1) break;
+    // the share continues into the next sequence
+    seq_base = first_tile + ntiles;
+    ++b;
+    Praw = a.prefix_lens[b];
+    ntiles = tiles_of(a, clamp_prefix(a, Praw));
   }
 }
 
