@@ -103,9 +103,10 @@ struct MfmaParams {
   int waves;       // waves per workgroup (32 rows each)
 };
 
-// workspace: a header written by the attention kernel for the merge (lane
-// tiles S and share length T, then one cut record of four int32 per share),
-// then the partial slots (2G balanced, G fixed) of kRows rows each
+// workspace: a header written by the attention kernel for the merge (flat
+// positions S, the share boundaries' pair length Tp and first-share length
+// Te, then one cut record of four int32 per share), then the partial slots
+// (2G balanced, G fixed) of kRows rows each
 __host__ __device__ constexpr size_t header_bytes(int shares) {
   return (16 + 16 * static_cast<size_t>(shares) + 255) / 256 * 256;
 }
@@ -276,15 +277,33 @@ __device__ __forceinline__ int tiles_of(const AttnArgs& a, int P) { return (P + 
 // that crosses more boundaries gets fewer tiles and all end together.
 constexpr int kSeqCostTiles = 6;
 
+// Share boundaries in the flat range: shares come in pairs of Tp positions,
+// the first share of a pair Te long.  Equal shares: Tp = 2 T, Te = T.
+struct ShareSplit {
+  int Tp, Te;
+  __device__ int start(int k) const { return (k >> 1) * Tp + ((k & 1) ? Te : 0); }
+  __device__ int share_of(int y) const { return 2 * (y / Tp) + ((y % Tp) >= Te ? 1 : 0); }
+};
+
+// Odd-numbered XCDs ran the attention main kernel 3-8 % slower than
+// even-numbered ones on every MI355X measured (per-workgroup timestamps and
+// HW_REG_XCC_ID; the same XCDs stay slow when the KV heads are moved to other
+// XCDs).  With 8 lanes of one row chunk, workgroups are placed so that the
+// even shares of every lane run on even XCDs and the odd shares on odd XCDs,
+// and an even share takes kEvenShare / kShareWeight of each pair.
+constexpr int kEvenShare = 103;
+constexpr int kShareWeight = 200;
+
 struct Start {
-  int S, T;        // flat positions (tiles plus per-sequence cost), share length
+  int S;           // flat positions (tiles plus per-sequence cost)
+  ShareSplit sp;   // share boundaries
   int b, base;     // sequence holding the share's first position (-1: none), and its first position
   int ntiles;      // tiles of sequence b (its tiles start at base + kSeqCostTiles)
 };
 
 template <int NW>
-__device__ Start balanced_start(const AttnArgs& a, int shares, int share_idx, int min_tiles, int* red,
-                               int* found) {
+__device__ Start balanced_start(const AttnArgs& a, int shares, int share_idx, int min_tiles, bool xcd_weighted,
+                               int* red, int* found) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Start st;
   // pass 1: tiles of one lane (and the prefix-length check)
@@ -302,9 +321,17 @@ __device__ Start balanced_start(const AttnArgs& a, int shares, int share_idx, in
   for (int w = 0; w < NW; ++w) tot += red[w];
   __syncthreads();
   st.S = tot;
-  const int even = (st.S + shares - 1) / shares;
-  st.T = even > min_tiles ? even : min_tiles;
-  const int j0 = share_idx * st.T;
+  if (xcd_weighted) {
+    const int pair = (2 * st.S + shares - 1) / shares;
+    st.sp.Tp = pair > 2 * min_tiles ? pair : 2 * min_tiles;
+    st.sp.Te = (st.sp.Tp * kEvenShare + kShareWeight - 1) / kShareWeight;
+  } else {
+    const int even = (st.S + shares - 1) / shares;
+    const int T = even > min_tiles ? even : min_tiles;
+    st.sp.Tp = 2 * T;
+    st.sp.Te = T;
+  }
+  const int j0 = st.sp.start(share_idx);
   if (j0 >= st.S) {
     st.b = -1;
     return st;
@@ -749,8 +776,12 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
       rc_p = (u - G0) % RC;
     }
   }
+  // 8 lanes of one row chunk and an even share count: XCD x = u % 8 runs
+  // lanes x / 2 and x / 2 + 4 at shares of x's parity
+  const bool xcd_weighted = mp.balanced && a.Hkv == 8 && mp.row_chunks == 1 && (G / 8) % 2 == 0;
   const int v = !mp.balanced ? ((w_item / mp.pieces) * mp.row_chunks + rc_p) * mp.pieces + w_item % mp.pieces
-                             : (w_item / a.Hkv) * (a.Hkv * mp.row_chunks) + (w_item % a.Hkv) * mp.row_chunks + rc_p;
+                : xcd_weighted ? (2 * ((u >> 3) >> 1) + (u & 1)) * 8 + ((u & 7) >> 1) + 4 * ((u >> 3) & 1)
+                               : (w_item / a.Hkv) * (a.Hkv * mp.row_chunks) + (w_item % a.Hkv) * mp.row_chunks + rc_p;
   if (!mp.balanced) {
     // ---------------- fixed pieces ----------------
     const int seg_id = v / mp.pieces, piece = v % mp.pieces;
@@ -787,11 +818,12 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   const int lanes = a.Hkv * mp.row_chunks;
   const int lane_id = v % lanes, share = v / lanes;
   const int kh = lane_id / mp.row_chunks, rc = lane_id % mp.row_chunks;
-  const Start st = balanced_start<NW>(a, G / lanes, share, mp.T, red, found);
+  const Start st = balanced_start<NW>(a, G / lanes, share, mp.T, xcd_weighted, red, found);
   int* hdr = static_cast<int*>(a.workspace);
   if (u == 0 && tid == 0) {
     hdr[0] = st.S;
-    hdr[1] = st.T;
+    hdr[1] = st.sp.Tp;
+    hdr[2] = st.sp.Te;
   }
   // the cut at this share's start, for the merge: the sequence it splits,
   // the flat position of that sequence's first tile and its tile count, and
@@ -800,15 +832,16 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   if (lane_id == 0 && tid == 0) {
     int4 cut = {-1, 0, 0, 0};
     const int first_tile = st.base + kSeqCostTiles;
-    if (st.b >= 0 && share * st.T > first_tile)
-      cut = int4{st.b, first_tile, st.ntiles, share - first_tile / st.T - 1};
+    if (st.b >= 0 && st.sp.start(share) > first_tile)
+      cut = int4{st.b, first_tile, st.ntiles, share - st.sp.share_of(first_tile) - 1};
     reinterpret_cast<int4*>(hdr + 4)[share] = cut;
   }
   if (st.b < 0) return;  // whole workgroup: the lane's tiles ended before this share
   // flat positions [j, j1) of this share; sequence b's tiles occupy
   // [seq_base + kSeqCostTiles, seq_base + kSeqCostTiles + ntiles)
-  const int j1 = min(st.S, share * st.T + st.T);
-  int j = share * st.T;
+  const int j_share = st.sp.start(share);
+  const int j1 = min(st.S, st.sp.start(share + 1));
+  int j = j_share;
   int b = st.b, seq_base = st.base;
   int Praw = a.prefix_lens[b];
   int ntiles = tiles_of(a, clamp_prefix(a, Praw));
@@ -822,8 +855,7 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     // a cut piece leaves its state in slot v when it starts where the share
     // starts (it continues a sequence from the share before, or its sequence
     // starts exactly there), in G + v when its sequence starts inside the share
-    run_piece(b, kh, rc, Praw, t0, t1, t0 == 0 && t1 == ntiles, j == share * st.T ? v : G + v, no_ids,
-              false);
+    run_piece(b, kh, rc, Praw, t0, t1, t0 == 0 && t1 == ntiles, j == j_share ? v : G + v, no_ids, false);
     j += t1 - t0;
     if (j >= j1) break;
     // the share continues into the next sequence
@@ -887,15 +919,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, MfmaParams 
     const int* hdr = static_cast<const int*>(a.workspace);
     const int4 cut = reinterpret_cast<const int4*>(hdr + 4)[share];
     if (cut.x < 0) return;
-    const int T = hdr[1];
+    const ShareSplit sp{hdr[1], hdr[2]};
     b = cut.x;
-    f = cut.y / T;
-    const int last = (cut.y + cut.z - 1) / T;
+    f = sp.share_of(cut.y);
+    const int last = sp.share_of(cut.y + cut.z - 1);
     npieces = last - f + 1;
     const int nslices = last - f, slice = cut.w;
     kh = lane / RC;
     rc = lane % RC;
-    cut_first = cut.y != f * T;  // the sequence starts inside share f: that share's last piece
+    cut_first = cut.y != sp.start(f);  // the sequence starts inside share f: that share's last piece
     slot0 = 0;
     hbytes = header_bytes(shares);
     const int rows = min(C::kRows, R - rc * C::kRows);
