@@ -877,7 +877,7 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
 // Threads walk (4-dim chunk, row) items with rows fastest, matching the
 // [slot][D/4][row] partial layout, and fold the pieces four at a time with
 // a running maximum.
-constexpr int kMergeSplit = 2;  // balanced shares: merge workgroups per cut (1 and 4 measured slower)
+constexpr int kMergeSplit = 3;  // balanced shares: merge workgroups per cut (2 and 4 measured slower)
 template <int D, int NW, int kItems, int kGroup>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, MfmaParams mp) {
   using C = Cfg<D, NW>;
