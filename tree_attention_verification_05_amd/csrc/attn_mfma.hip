@@ -101,6 +101,7 @@ struct MfmaParams {
   int pieces;      // fixed: pieces per segment
   int row_chunks;  // row chunks per KV head
   int waves;       // waves per workgroup (32 rows each)
+  int merge_split; // balanced: merge workgroups per cut record
 };
 
 // workspace: a header written by the attention kernel for the merge (flat
@@ -877,13 +878,12 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
 // Threads walk (4-dim chunk, row) items with rows fastest, matching the
 // [slot][D/4][row] partial layout, and fold the pieces four at a time with
 // a running maximum.
-constexpr int kMergeSplit = 3;  // balanced shares: merge workgroups per cut (2 and 4 measured slower)
 template <int D, int NW, int kItems, int kGroup>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, MfmaParams mp) {
   using C = Cfg<D, NW>;
   // kItems items per thread and kGroup pieces of each have their loads in flight together
   const int tid = threadIdx.x;
-  const int u = mp.balanced ? static_cast<int>(blockIdx.x) / kMergeSplit : static_cast<int>(blockIdx.x);
+  const int u = mp.balanced ? static_cast<int>(blockIdx.x) / mp.merge_split : static_cast<int>(blockIdx.x);
   const int G = mp.grid;
   const int RC = mp.row_chunks;
   const int segs = a.Hkv * RC;
@@ -932,7 +932,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, MfmaParams 
     hbytes = header_bytes(shares);
     const int rows = min(C::kRows, R - rc * C::kRows);
     // this workgroup's part of the cut's row slice
-    const int parts = nslices * kMergeSplit, part = slice * kMergeSplit + static_cast<int>(blockIdx.x) % kMergeSplit;
+    const int parts = nslices * mp.merge_split, part = slice * mp.merge_split + static_cast<int>(blockIdx.x) % mp.merge_split;
     r_lo = part * rows / parts;
     n = (part + 1) * rows / parts - r_lo;
     if (n <= 0) return;
@@ -1041,10 +1041,10 @@ hipError_t launch_cfg(const AttnArgs& a, const MfmaParams& mp, hipStream_t strea
   if (e != hipSuccess) return e;
   if (!mp.balanced ? mp.pieces == 1 : mp.grid == a.Hkv * mp.row_chunks) return e;  // no segment is ever shared
   // fixed pieces: one workgroup per (segment, 32 rows x 32 dims), one item
-  // per thread with all pieces in flight; balanced: kMergeSplit per attention
+  // per thread with all pieces in flight; balanced: merge_split per attention
   // workgroup (its cut), four items per thread
   if (mp.balanced) {
-    hipLaunchKernelGGL((attn_merge_kernel<D, NW, 4, 2>), dim3(static_cast<unsigned>(mp.grid * kMergeSplit)), dim3(256), 0,
+    hipLaunchKernelGGL((attn_merge_kernel<D, NW, 4, 2>), dim3(static_cast<unsigned>(mp.grid * mp.merge_split)), dim3(256), 0,
                        stream, a, mp);
   } else {
     const long blocks = static_cast<long>(a.B) * a.Hkv * mp.row_chunks * (C::kRows / 32) * (D / 32);
@@ -1077,6 +1077,7 @@ MfmaParams plan_for(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
   MfmaParams p;
   // the row chunks of a KV head share its K/V tiles through L2
   p.waves = 4;
+  p.merge_split = 1;
   p.row_chunks = (R + p.waves * 32 - 1) / (p.waves * 32);
   const long max_tiles = (static_cast<long>(max_prefix_len) + N + kTile - 1) / kTile;
   const long segments = static_cast<long>(B) * Hkv * p.row_chunks;
@@ -1097,6 +1098,10 @@ MfmaParams plan_for(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
     if (shares < 1) shares = 1;
     p.balanced = 1;
     p.T = kMinTilesPerPiece;
+    // merge workgroups per cut: three with one row chunk per KV head (the
+    // batched workload 127.3 -> 124.7 us against two), two with several (the
+    // Qwen2 workload 161.2 -> 159.6 us against three)
+    p.merge_split = p.row_chunks == 1 ? 3 : 2;
     p.pieces = 0;
     p.grid = static_cast<int>(shares * lanes);
   }
