@@ -136,6 +136,132 @@ __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int
   constexpr bool fuse = kCompact;
   const uint64_t* keys = static_cast<const uint64_t*>(a.workspace);
   const size_t base = static_cast<size_t>(b) * N;
+
+  // fused compaction: the tree region's block ids, P_b / 16 .. (P_b + N - 1) / 16
+  const int P = fuse ? c.prefix_lens[b] : 0;
+  const bool p_ok = P >= 0 && static_cast<long>(P) + N <= static_cast<long>(c.max_blocks) * kBlockSize;
+  const int tab0 = P / kBlockSize;
+  // compaction of steps 0 .. L-1 of s_path (the fused call only)
+  auto compact = [&](int L) __attribute__((always_inline)) {
+    int cbad = p_ok ? 0 : TV_DEV_BAD_CACHE;
+    if (!cbad) {
+      for (int j = tid; j < L; j += kThreads) {
+        const int ts = P + s_path[j], td = P + j;
+        const int bs = s_tab[ts / kBlockSize - tab0], bd = s_tab[td / kBlockSize - tab0];
+        if (bs < 0 || bs >= c.num_blocks || bd < 0 || bd >= c.num_blocks) {
+          cbad |= TV_DEV_BAD_CACHE;
+          continue;
+        }
+        s_src[j] = kv_row(bs, 0, ts % kBlockSize, c.Hkv, c.kv_head_rows, c.kv_slot_rows);
+        s_dst[j] = kv_row(bd, 0, td % kBlockSize, c.Hkv, c.kv_head_rows, c.kv_slot_rows);
+      }
+    }
+    if (cbad) atomicOr(&s_cbad, cbad);
+    __syncthreads();
+    if (s_cbad) {  // the sequence is left untouched
+      if (tid == 0) report(a.dev_status, s_cbad);
+      return;
+    }
+    if (tid == 0 && c.new_lens) c.new_lens[b] = P + L;
+    compact_copy_columns(c, s_src, s_dst, L, tid, kThreads);
+  };
+
+  if (N <= 64) {
+    // ---- a tree of at most 64 nodes: one wave holds a node per lane and
+    // finds the path in registers (shuffles and ballots instead of LDS round
+    // trips and barriers); the decisions are those of the general path below ----
+    if (tid == 0) s_cbad = 0;
+    if (fuse && p_ok)
+      for (int i = tid; i <= (P + N - 1) / kBlockSize - tab0; i += kThreads)
+        s_tab[i] = c.block_table[static_cast<size_t>(b) * c.max_blocks + tab0 + i];
+    if (wave == 0) {
+      const bool exists = lane < N;
+      int par = -1, tok = 0;
+      if (exists) {
+        par = a.parents[base + lane];
+        tok = a.draft_tokens[base + lane];
+      }
+      // the target argmax of node `lane`: the largest of its row's chunk
+      // keys, sixteen loads in flight at a time
+      uint64_t best = 0ull;
+      const uint64_t* rk = keys + (base + (exists ? lane : 0)) * chunks;
+      for (int c0 = 0; c0 < chunks; c0 += 16) {
+        uint64_t kk[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) kk[u] = rk[min(c0 + u, chunks - 1)];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) best = kk[u] > best ? kk[u] : best;
+      }
+      const int am = static_cast<int>(key_index(best));
+      if (exists && a.target_argmax) a.target_argmax[base + lane] = am;
+      int bad = 0;
+      if (exists) {
+        if (lane == 0 ? par != -1 : (par < 0 || par >= lane)) bad |= TV_DEV_BAD_TREE;
+        if (lane > 0 && (tok < 0 || tok >= V)) bad |= TV_DEV_BAD_TOKEN;
+      }
+      for (int o = 32; o > 0; o >>= 1) bad |= __shfl_xor(bad, o, 64);
+      int path_len = 1;
+      if (bad) {
+        if (lane == 0) report(a.dev_status, bad);
+        if (exists) a.accepted_nodes[base + lane] = lane == 0 ? 0 : -1;
+        const int am0 = __shfl(am, 0, 64);
+        if (lane == 0) {
+          a.accept_len[b] = 0;
+          a.bonus_token[b] = am0;
+          s_path[0] = 0;
+        }
+      } else {
+        // node i is reachable iff every edge on its root path is accepted (the
+        // child's token is its parent's target argmax): the AND of those
+        // edges and the depth, by pointer jumping up the root path
+        const int am_par = __shfl(am, par >= 0 ? par : 0, 64);
+        bool ok = exists && (lane == 0 || tok == am_par);
+        int dep = (exists && lane > 0) ? 1 : 0;
+        int jump = (exists && lane > 0) ? par : -1;
+        for (int r = 0; r < 6 && __builtin_amdgcn_ballot_w64(jump >= 0) != 0; ++r) {
+          const int src = jump >= 0 ? jump : lane;
+          const bool up_ok = __shfl(static_cast<int>(ok), src, 64) != 0;
+          const int up_dep = __shfl(dep, src, 64);
+          const int up_jump = __shfl(jump, src, 64);
+          if (jump >= 0) {
+            ok = ok && up_ok;
+            dep += up_dep;
+            jump = up_jump;
+          }
+        }
+        int dmax = ok ? dep : -1;
+        for (int o = 32; o > 0; o >>= 1) dmax = max(dmax, __shfl_xor(dmax, o, 64));
+        // every node on some deepest accepted path: the ancestors-or-self of
+        // the deepest accepted nodes
+        bool not_tree;
+        const uint64_t anc = wave_tree_mask(par, N, lane, &not_tree);
+        uint64_t on = (ok && dep == dmax) ? anc : 0ull;
+        for (int o = 32; o > 0; o >>= 1) on |= __shfl_xor(on, o, 64);
+        // descend from the root, taking the lowest-index marked child each
+        // step (always there: a marked node's parent is marked)
+        int cur = 0, mine = 0;
+        for (int k = 1; k <= dmax; ++k) {
+          const uint64_t kids = __builtin_amdgcn_ballot_w64(exists && par == cur && ((on >> lane) & 1ull));
+          cur = static_cast<int>(__builtin_ctzll(kids));
+          if (lane == k) mine = cur;
+        }
+        if (exists) a.accepted_nodes[base + lane] = lane <= dmax ? mine : -1;
+        if (lane <= dmax) s_path[lane] = mine;
+        const int bonus = __shfl(am, cur, 64);
+        if (lane == 0) {
+          a.accept_len[b] = dmax;
+          a.bonus_token[b] = bonus;
+        }
+        path_len = dmax + 1;
+      }
+      if (lane == 0) s_dmax = path_len;
+    }
+    __syncthreads();
+    if (fuse) compact(s_dmax);
+    return;
+  }
+
+  // ---- the general path (up to 256 nodes), through LDS ----
   // every (node, chunk) key of the sequence is contiguous in the workspace;
   // the first eight per thread are loaded together with the tree and the
   // draft tokens, so both latencies overlap
@@ -158,10 +284,6 @@ __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int
     s_dmax = 0;
     s_cbad = 0;
   }
-  // fused compaction: the tree region's block ids, P_b / 16 .. (P_b + N - 1) / 16
-  const int P = fuse ? c.prefix_lens[b] : 0;
-  const bool p_ok = P >= 0 && static_cast<long>(P) + N <= static_cast<long>(c.max_blocks) * kBlockSize;
-  const int tab0 = P / kBlockSize;
   if (fuse && p_ok)
     for (int i = tid; i <= (P + N - 1) / kBlockSize - tab0; i += kThreads)
       s_tab[i] = c.block_table[static_cast<size_t>(b) * c.max_blocks + tab0 + i];
@@ -198,31 +320,6 @@ __global__ __launch_bounds__(kThreads) void accept_walk_kernel(AcceptArgs a, int
   }
   if (bad) atomicOr(&s_bad, bad);
   __syncthreads();
-  // compaction of steps 0 .. L-1 of s_path (the fused call only)
-  auto compact = [&](int L) __attribute__((always_inline)) {
-    int cbad = p_ok ? 0 : TV_DEV_BAD_CACHE;
-    if (!cbad) {
-      for (int j = tid; j < L; j += kThreads) {
-        const int ts = P + s_path[j], td = P + j;
-        const int bs = s_tab[ts / kBlockSize - tab0], bd = s_tab[td / kBlockSize - tab0];
-        if (bs < 0 || bs >= c.num_blocks || bd < 0 || bd >= c.num_blocks) {
-          cbad |= TV_DEV_BAD_CACHE;
-          continue;
-        }
-        s_src[j] = kv_row(bs, 0, ts % kBlockSize, c.Hkv, c.kv_head_rows, c.kv_slot_rows);
-        s_dst[j] = kv_row(bd, 0, td % kBlockSize, c.Hkv, c.kv_head_rows, c.kv_slot_rows);
-      }
-    }
-    if (cbad) atomicOr(&s_cbad, cbad);
-    __syncthreads();
-    if (s_cbad) {  // the sequence is left untouched
-      if (tid == 0) report(a.dev_status, s_cbad);
-      return;
-    }
-    if (tid == 0 && c.new_lens) c.new_lens[b] = P + L;
-    compact_copy_columns(c, s_src, s_dst, L, tid, kThreads);
-  };
-
   if (s_bad) {
     if (tid == 0) report(a.dev_status, s_bad);
     for (int i = tid; i < N; i += kThreads) a.accepted_nodes[base + i] = (i == 0) ? 0 : -1;
