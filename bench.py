@@ -180,7 +180,9 @@ class StepBench:
         self.dt = T.TV_BF16 if self.q.dtype == torch.bfloat16 else T.TV_F32
         ws_bytes = T.tv_tree_attention_workspace_size(B, N, w.spec.Hq, w.spec.Hkv, w.spec.D,
                                                       w.max_prefix_len)
-        self.attn_ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        # (zero-filled once: the arrival counters start at zero, and every call
+        # leaves them so)
+        self.attn_ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
         self.acc_len = torch.empty(B, dtype=torch.int32, device=dev)
         self.acc_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
         self.bonus = torch.empty(B, dtype=torch.int32, device=dev)

@@ -124,10 +124,17 @@ TV_API tv_status tv_build_tree_mask(const int32_t* parents, int32_t B, int32_t N
 
 /*
  * Workspace bytes tv_tree_attention needs for these sizes, either dtype and
- * either cache layout (0 when the key range is not split; the fp32 path uses
- * none).  The workspace holds the split schedule and the partial softmax
- * state of every split (row maxima and sums in fp32, the normalised partial
- * outputs in bf16), and needs no initialisation.
+ * either cache layout (the fp32 path uses none).  The workspace holds
+ * arrival counters (its first 2048 bytes, the same for every shape) and the
+ * partial softmax state of every piece of a split key range (row maxima and
+ * sums in fp32, the normalised partial outputs in bf16).  The workgroup that
+ * finishes the last piece of a split sequence merges it, found through the
+ * counters.  A new workspace must therefore be zero-filled once before its
+ * first call (hipMemset, or a zeroed allocation).  Every call leaves the
+ * counters at zero again, so the workspace then serves any number of later
+ * calls of any shape without clearing.  Calls that share a workspace must be
+ * ordered (same stream), and so must a call and any other use of its
+ * workspace memory.
  */
 TV_API size_t tv_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
                                         int32_t max_prefix_len);
@@ -156,8 +163,9 @@ TV_API size_t tv_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq,
  *                even) or TV_F32 (fp32 throughout), optionally OR'd with
  *                TV_KV_TOKEN_MAJOR.
  *   workspace    device buffer of at least
- *                tv_tree_attention_workspace_size(...) bytes, 16-byte aligned
- *                (may be NULL if that size is 0).
+ *                tv_tree_attention_workspace_size(...) bytes, 16-byte aligned,
+ *                zero-filled before its first use (see above); may be NULL
+ *                for the fp32 path.
  * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_DTYPE, TV_ERR_UNSUPPORTED,
  * TV_ERR_ALIGN, TV_ERR_WORKSPACE, TV_ERR_LAUNCH.  Device: TV_DEV_BAD_CACHE.
  */

@@ -75,6 +75,31 @@ def test_full_config_all_sequences(i):
     verify(full(i), label=f"full{i}")
 
 
+def test_attention_workspace_reused_across_shapes():
+    """One zero-filled workspace serves attention calls of different shapes
+    and both schedules in turn: balanced shares that cut sequences (the
+    workgroup finishing a cut sequence's last piece merges it, found through
+    the arrival counters at the workspace's start) and fixed pieces of one
+    sequence (merged by a second kernel).  Every result matches the oracle,
+    and the counters (the first 2048 bytes) are zero again after every call,
+    as the next call needs them."""
+    cases = [("small3", W.make_small(3)), ("small2", W.make_small(2)), ("full3", full(3)),
+             ("small5", W.make_small(5)), ("small4", W.make_small(4)), ("small3 again", W.make_small(3))]
+    need = max(T.tv_tree_attention_workspace_size(w.B, w.N, w.spec.Hq, w.spec.Hkv, w.spec.D, w.max_prefix_len)
+               for _, w in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for name, w in cases:
+        log(f"[parity] shared attention workspace: {name} B={w.B} N={w.N}")
+        d = upload(w)
+        out = T.tv_tree_attention_parents(d["q"], d["k"], d["v"], d["table"], d["prefix"], w.max_prefix_len,
+                                          d["parents"], workspace=ws, dev_status=d["status"])
+        torch.cuda.synchronize()
+        assert int(d["status"].item()) == 0
+        assert int(torch.count_nonzero(ws[:2048]).item()) == 0, f"{name}: arrival counters not reset"
+        seqs = sorted({0, w.B - 1, int(np.argmin(w.prefix_lens)), int(np.argmax(w.prefix_lens))})
+        check_attention(out, oracle_attention(w, seqs), seqs, w.q.dtype, label=f"shared workspace {name}")
+
+
 def mask_revealing(w, planted=(0.1, 0.5, 0.9), seed=0):
     """A copy of workload ``w`` whose tree keys dominate every score (the
     pins' mask-revealing construction) and whose value rows name their source.
@@ -505,7 +530,7 @@ def test_accept_workspace_per_stream():
         with torch.cuda.stream(s):
             outs.append(T.tv_accept_greedy(*x))
     torch.cuda.synchronize()
-    keys = {k for k in _lib._accept_ws if k[1] in (streams[0].cuda_stream, streams[1].cuda_stream) and k[2] == 0}
+    keys = {k for k in _lib._cached_ws if k[1] in (streams[0].cuda_stream, streams[1].cuda_stream) and k[2] == 0}
     assert len(keys) == 2
     for w, (al, an, bt, am) in zip(cases, outs):
         ref = O.accept_greedy(w.logits.numpy(), w.draft_tokens, w.parents)

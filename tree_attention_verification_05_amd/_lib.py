@@ -140,15 +140,16 @@ def _tv_dtype(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-_accept_ws: Dict[Tuple[int, int, int], torch.Tensor] = {}
+_cached_ws: Dict[Tuple[int, int, int], torch.Tensor] = {}
 
 
-def accept_workspace(device: torch.device, nbytes: int, kind: int = 0) -> torch.Tensor:
+def cached_workspace(device: torch.device, nbytes: int, kind: int = 0) -> torch.Tensor:
     """A workspace for tv_accept_greedy (kind 0), tv_accept_stochastic
-    (kind 1), tv_lm_head_argmax (kind 2) or tv_build_draft_tree (kind 3),
-    kept per device, current stream and kind, and grown when a call needs
-    more (the library needs no initial contents: everything a call reads from
-    it is written earlier in the same call).
+    (kind 1), tv_lm_head_argmax (kind 2), tv_build_draft_tree (kind 3) or
+    tv_tree_attention (kind 4), kept per device, current stream and kind, and
+    grown when a call needs more.  A new buffer is zero-filled: the attention
+    workspace's arrival counters must start at zero (each call leaves them
+    so); the other calls need no initial contents.
 
     One buffer per stream: calls on one stream run in order, so they may
     share it; calls on different streams get different buffers, and a buffer
@@ -158,10 +159,10 @@ def accept_workspace(device: torch.device, nbytes: int, kind: int = 0) -> torch.
     on several streams must pass one per stream."""
     idx = device.index if device.index is not None else torch.cuda.current_device()
     key = (idx, torch.cuda.current_stream(idx).cuda_stream, kind)
-    ws = _accept_ws.get(key)
+    ws = _cached_ws.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
-        _accept_ws[key] = ws
+        _cached_ws[key] = ws
     return ws
 
 
@@ -252,7 +253,7 @@ def _tree_attention(q, k_cache, v_cache, block_table, prefix_lens, max_prefix_le
     _dev(out, "out", q.dtype, q.shape)
     need = tv_tree_attention_workspace_size(B, N, Hq, Hkv, D, max_prefix_len) if dt == TV_BF16 else 0
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = cached_workspace(q.device, need, kind=4)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if dev_status is not None:
         _dev(dev_status, "dev_status", torch.int32)
@@ -305,7 +306,7 @@ def tv_accept_greedy(logits: torch.Tensor, draft_tokens: torch.Tensor, parents: 
     dev = logits.device
     need = int(lib.tv_accept_greedy_workspace_size(B, N, V))
     if workspace is None:
-        workspace = accept_workspace(dev, need)
+        workspace = cached_workspace(dev, need)
     if dev_status is not None:
         _dev(dev_status, "dev_status", torch.int32)
     _check("tv_accept_greedy", lib.tv_accept_greedy(
@@ -371,7 +372,7 @@ def tv_accept_stochastic(logits: torch.Tensor, draft_tokens: torch.Tensor, paren
     _dev(bonus_token, "bonus_token", torch.int32, (B,))
     need = int(lib.tv_accept_stochastic_workspace_size(B, N, V))
     if workspace is None:
-        workspace = accept_workspace(dev, need, kind=1)
+        workspace = cached_workspace(dev, need, kind=1)
     if dev_status is not None:
         _dev(dev_status, "dev_status", torch.int32)
     _check("tv_accept_stochastic", lib.tv_accept_stochastic(
@@ -408,7 +409,7 @@ def tv_lm_head_argmax(hidden: torch.Tensor, weight: torch.Tensor,
         _dev(max_score, "max_score", torch.float32, lead)
     need = int(lib.tv_lm_head_argmax_workspace_size(M, H, V))
     if workspace is None:
-        workspace = accept_workspace(dev, need, kind=2)
+        workspace = cached_workspace(dev, need, kind=2)
     _check("tv_lm_head_argmax", lib.tv_lm_head_argmax(
         _ptr(hidden), _ptr(weight), M, H, V, TV_BF16, _ptr(argmax), _ptr(max_score), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(hidden)))
@@ -443,7 +444,7 @@ def tv_build_draft_tree(draft_logits: torch.Tensor, N: int,
         _dev(scores, "scores", torch.float32, (B, N))
     need = int(lib.tv_build_draft_tree_workspace_size(B, depth, topk, V))
     if workspace is None:
-        workspace = accept_workspace(dev, need, kind=3)
+        workspace = cached_workspace(dev, need, kind=3)
     _check("tv_build_draft_tree", lib.tv_build_draft_tree(
         _ptr(draft_logits), B, depth, topk, V, N, _ptr(root_tokens), _ptr(parents), _ptr(tokens),
         _ptr(scores), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -508,7 +509,7 @@ def tv_accept_greedy_compact(logits: torch.Tensor, draft_tokens: torch.Tensor, p
     _dev(new_lens, "new_lens", torch.int32, (B,))
     need = int(lib.tv_accept_greedy_workspace_size(B, N, V))
     if workspace is None:
-        workspace = accept_workspace(dev, need)
+        workspace = cached_workspace(dev, need)
     if dev_status is not None:
         _dev(dev_status, "dev_status", torch.int32)
     _check("tv_accept_greedy_compact", lib.tv_accept_greedy_compact(

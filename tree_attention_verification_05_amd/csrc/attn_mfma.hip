@@ -10,8 +10,10 @@
 // and every query head of the group.  Each of the NW waves owns 32 rows
 // (waves past the last row only help load tiles).  Sequences differ in
 // length, so the tiles of all segments are laid end to end and every
-// workgroup takes an equal share of that flat range (see balanced_start);
-// a segment cut between workgroups is merged by a second kernel.
+// workgroup takes an equal share of that flat range (see balanced_start).
+// A segment cut between workgroups is merged by the workgroup that finishes
+// its last piece, or, where segments are cut into many pieces, by a second
+// kernel.
 //
 // Memory pipeline: 32-key tiles stream from HBM straight into LDS with
 // buffer_load_dwordx4 ... lds (each lane's 16 bytes land at the wave's LDS
@@ -101,13 +103,20 @@ struct MfmaParams {
   int pieces;      // fixed: pieces per segment
   int row_chunks;  // row chunks per KV head
   int waves;       // waves per workgroup (32 rows each)
-  int merge_split; // balanced: merge workgroups per cut record
+  int fused_merge; // balanced: the last piece of a cut segment merges it (else a second kernel)
+  int merge_split; // balanced, second kernel: merge workgroups per cut record
 };
 
-// workspace: a header written by the attention kernel for the merge (flat
-// positions S, the share boundaries' pair length Tp and first-share length
-// Te, then one cut record of four int32 per share), then the partial slots
-// (2G balanced, G fixed) of kRows rows each
+// workspace: kMaxCounters arrival counters (int32; fused balanced merges use
+// one per share and lane; zero between calls, since the last arrival of a
+// cut sequence resets its counter); balanced shares: a header for the second
+// merge kernel (flat positions S, the share boundaries' pair length Tp and
+// first-share length Te, then one cut record of four int32 per share); then
+// the partial slots (2G balanced, G fixed) of kRows rows each.  The counters
+// have the same place and size for every shape, so one workspace,
+// zero-filled once, serves calls of any shape.
+constexpr int kMaxCounters = 512;
+constexpr size_t kCounterBytes = kMaxCounters * sizeof(int);
 __host__ __device__ constexpr size_t header_bytes(int shares) {
   return (16 + 16 * static_cast<size_t>(shares) + 255) / 256 * 256;
 }
@@ -134,7 +143,8 @@ __device__ __forceinline__ PartialView partial_view_at(void* ws, size_t hbytes, 
 template <int D>
 __device__ __forceinline__ PartialView partial_view(const AttnArgs& a, const MfmaParams& mp, int G) {
   const size_t nslots = static_cast<size_t>(mp.balanced ? 2 * G : G) * (mp.waves * 32);
-  return partial_view_at<D>(a.workspace, header_bytes(mp.balanced ? G / (a.Hkv * mp.row_chunks) : 0), nslots);
+  const size_t hbytes = mp.balanced ? header_bytes(G / (a.Hkv * mp.row_chunks)) : 0;
+  return partial_view_at<D>(a.workspace, kCounterBytes + hbytes, nslots);
 }
 
 // v_cvt_pk_bf16_f32: round to nearest even
@@ -143,6 +153,71 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   v[0] = static_cast<__bf16>(lo);
   v[1] = static_cast<__bf16>(hi);
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Partial states that a workgroup on another XCD merges within the same
+// kernel (balanced shares) are stored and loaded at agent scope: the stores
+// write through this XCD's L2 (sc1) and the loads bypass the reader's (sc1),
+// so no L2 write-back or invalidation of the whole cache is needed (agent
+// fences cost both, on every workgroup).
+__device__ __forceinline__ void store_agent(u32x2* p, u32x2 v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x2 load_agent(u32x2* p) {
+  return __builtin_bit_cast(u32x2, __hip_atomic_load(reinterpret_cast<uint64_t*>(p), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float load_agent(float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The log-sum-exp fold of one item (four dims of one row) over a group of
+// kGroup pieces: row maxima m (log2 units, scaled), row sums l and the
+// normalised outputs ov (bf16 pairs).  The running state (M, L, o) starts at
+// (-inf, 0, 0); a piece without visible keys (or an empty one) has m = -inf
+// and contributes nothing, whatever its other values.
+template <int kGroup>
+__device__ __forceinline__ void fold_pieces(float& M, float& L, float (&o)[4], const float (&m)[kGroup],
+                                            const float (&l)[kGroup], const u32x2 (&ov)[kGroup]) {
+  float Mn = M;
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j) Mn = fmaxf(Mn, m[j]);
+  if (Mn == -INFINITY) return;  // no visible key in any piece so far
+  const float sc = exp2_fast(M - Mn);  // 0 while M is -inf
+  L *= sc;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] *= sc;
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j) {
+    const bool use = m[j] != -INFINITY;
+    const float w = use ? exp2_fast(m[j] - Mn) * l[j] : 0.f;
+    L += w;
+    const float x0 = __uint_as_float(ov[j][0] << 16), x1 = __uint_as_float(ov[j][0] & 0xFFFF0000u);
+    const float x2 = __uint_as_float(ov[j][1] << 16), x3 = __uint_as_float(ov[j][1] & 0xFFFF0000u);
+    o[0] += use ? w * x0 : 0.f;
+    o[1] += use ? w * x1 : 0.f;
+    o[2] += use ? w * x2 : 0.f;
+    o[3] += use ? w * x3 : 0.f;
+  }
+  M = Mn;
+}
+
+// bf16 output of one item: four dims of chunk row r (row r = node * g + head
+// in group) of KV head kh
+__device__ __forceinline__ void store_item(const AttnArgs& a, int D, int b, int kh, int r, int q, const float (&o)[4],
+                                           float L) {
+  const int g = a.Hq / a.Hkv;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int node = r / g, hg = r % g;
+  uint16_t* op = static_cast<uint16_t*>(a.out) + ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D + 4 * q;
+  u32x2 w;
+  w[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
+  w[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+  *reinterpret_cast<u32x2*>(op) = w;
 }
 
 // op(x[l], x[l ^ 32]) for every lane l, with one v_permlane32_swap
@@ -751,12 +826,20 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
           u32x2 w;
           w[0] = pack_bf16x2(acc[db][4 * jj] * inv, acc[db][4 * jj + 1] * inv);
           w[1] = pack_bf16x2(acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv);
-          po[static_cast<size_t>(q) * C::kRows] = w;
+          if (mp.fused_merge)
+            store_agent(po + static_cast<size_t>(q) * C::kRows, w);
+          else
+            po[static_cast<size_t>(q) * C::kRows] = w;
         }
       (void)nslots;
       if (hh == 0) {
-        pv.m[prow] = m_c;
-        pv.l[prow] = lt;
+        if (mp.fused_merge) {
+          store_agent(pv.m + prow, m_c);
+          store_agent(pv.l + prow, lt);
+        } else {
+          pv.m[prow] = m_c;
+          pv.l[prow] = lt;
+        }
       }
     }
   };
@@ -820,24 +903,103 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   const int lane_id = v % lanes, share = v / lanes;
   const int kh = lane_id / mp.row_chunks, rc = lane_id % mp.row_chunks;
   const Start st = balanced_start<NW>(a, G / lanes, share, mp.T, xcd_weighted, red, found);
-  int* hdr = static_cast<int*>(a.workspace);
-  if (u == 0 && tid == 0) {
-    hdr[0] = st.S;
-    hdr[1] = st.sp.Tp;
-    hdr[2] = st.sp.Te;
-  }
-  // the cut at this share's start, for the merge: the sequence it splits,
-  // the flat position of that sequence's first tile and its tile count, and
-  // the cut's rank among the sequence's cuts (-1: the share starts at or
-  // before a sequence's first tile, or past the end)
-  if (lane_id == 0 && tid == 0) {
-    int4 cut = {-1, 0, 0, 0};
-    const int first_tile = st.base + kSeqCostTiles;
-    if (st.b >= 0 && st.sp.start(share) > first_tile)
-      cut = int4{st.b, first_tile, st.ntiles, share - st.sp.share_of(first_tile) - 1};
-    reinterpret_cast<int4*>(hdr + 4)[share] = cut;
+  if (!mp.fused_merge) {
+    // for the second merge kernel: S and the share boundaries, and the cut
+    // at this share's start: the sequence it splits, the flat position of
+    // that sequence's first tile and its tile count, and the cut's rank
+    // among the sequence's cuts (-1: the share starts at or before a
+    // sequence's first tile, or past the end)
+    int* hdr = reinterpret_cast<int*>(static_cast<char*>(a.workspace) + kCounterBytes);
+    if (u == 0 && tid == 0) {
+      hdr[0] = st.S;
+      hdr[1] = st.sp.Tp;
+      hdr[2] = st.sp.Te;
+    }
+    if (lane_id == 0 && tid == 0) {
+      int4 cut = {-1, 0, 0, 0};
+      const int first_tile = st.base + kSeqCostTiles;
+      if (st.b >= 0 && st.sp.start(share) > first_tile)
+        cut = int4{st.b, first_tile, st.ntiles, share - st.sp.share_of(first_tile) - 1};
+      reinterpret_cast<int4*>(hdr + 4)[share] = cut;
+    }
   }
   if (st.b < 0) return;  // whole workgroup: the lane's tiles ended before this share
+  // A sequence cut by share boundaries has one piece in each of the shares
+  // f .. l of this lane that its tiles [first_tile, first_tile + nt) touch.
+  // Every piece stores its partial state at agent scope, waits until each
+  // wave's stores are acknowledged (written through to device-coherent
+  // memory), and after a workgroup barrier counts itself in the sequence's
+  // arrival counter, number f * lanes + lane (f is the share where the
+  // sequence's first tile lies, and no other cut sequence of the lane starts
+  // its tiles there).  The workgroup whose count completes the set resets
+  // the counter to zero and merges the pieces, loading them at agent scope
+  // only after its count returned.  Nothing waits for another workgroup.
+  int* counters = static_cast<int*>(a.workspace);
+  __shared__ int s_last;
+  auto merge_if_last = [&](int bb, int first_tile, int nt) __attribute__((always_inline)) {
+    const int f = st.sp.share_of(first_tile);
+    const int npieces = st.sp.share_of(first_tile + nt - 1) - f + 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      int* cnt = counters + f * lanes + lane_id;
+      const int before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = before == npieces - 1;
+      if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // piece k runs in share f + k, in slot (f + k) * lanes + lane; the piece
+    // in share f is in the share's second slot (G + ...) when the sequence's
+    // tiles start inside that share (cut_first).  Thread t takes row
+    // t % kRows of the chunk and half t / kRows of its dims, folding the
+    // pieces two at a time with every load of a pair in flight together
+    // (three at a time, or the merge as a separate function, raised the
+    // register count or spilled, and measured slower).
+    const bool cut_first = first_tile != st.sp.start(f);
+    constexpr int kQ = D / 8;  // 4-dim chunks per thread
+    constexpr int kFold = 2;   // pieces whose loads are in flight together
+    static_assert(C::kThreads == 2 * C::kRows, "two threads per row");
+    const int rl = tid % C::kRows, q0 = (tid / C::kRows) * kQ;
+    if (rc * C::kRows + rl >= R) return;
+    const PartialView pv = partial_view<D>(a, mp, G);
+    float M = -INFINITY, L = 0.f;
+    float o[kQ][4];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) o[q][0] = o[q][1] = o[q][2] = o[q][3] = 0.f;
+    for (int k0 = 0; k0 < npieces; k0 += kFold) {
+      float m[kFold], l[kFold];
+      u32x2 ov[kQ][kFold];
+#pragma unroll
+      for (int j = 0; j < kFold; ++j) {
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) ov[q][j] = u32x2{0u, 0u};
+        if (k0 + j < npieces) {
+          const int vv = (f + k0 + j) * lanes + lane_id;
+          const size_t sl = static_cast<size_t>((k0 + j == 0 && cut_first) ? G + vv : vv);
+          m[j] = load_agent(pv.m + sl * C::kRows + rl);
+          l[j] = load_agent(pv.l + sl * C::kRows + rl);
+#pragma unroll
+          for (int q = 0; q < kQ; ++q) ov[q][j] = load_agent(pv.o + (sl * (D / 4) + q0 + q) * C::kRows + rl);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        // (every chunk of the row has the same maxima and sums)
+        float Mq = M, Lq = L;
+        fold_pieces<kFold>(Mq, Lq, o[q], m, l, ov[q]);
+        if (q == kQ - 1) {
+          M = Mq;
+          L = Lq;
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) store_item(a, D, bb, kh, rc * C::kRows + rl, q0 + q, o[q], L);
+  };
   // flat positions [j, j1) of this share; sequence b's tiles occupy
   // [seq_base + kSeqCostTiles, seq_base + kSeqCostTiles + ntiles)
   const int j_share = st.sp.start(share);
@@ -856,7 +1018,9 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
     // a cut piece leaves its state in slot v when it starts where the share
     // starts (it continues a sequence from the share before, or its sequence
     // starts exactly there), in G + v when its sequence starts inside the share
-    run_piece(b, kh, rc, Praw, t0, t1, t0 == 0 && t1 == ntiles, j == j_share ? v : G + v, no_ids, false);
+    const bool whole = t0 == 0 && t1 == ntiles;
+    run_piece(b, kh, rc, Praw, t0, t1, whole, j == j_share ? v : G + v, no_ids, false);
+    if (!whole && mp.fused_merge) merge_if_last(b, first_tile, ntiles);
     j += t1 - t0;
     if (j >= j1) break;
     // the share continues into the next sequence
@@ -867,91 +1031,92 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
   }
 }
 
-// Merge the partial states of segments that several workgroups shared
-// (log-sum-exp rule) and write bf16 outputs.  One workgroup per attention
-// workgroup; each merges a slice of the rows of one split segment:
-//   fixed pieces: workgroup (segment, p) takes row slice p of `pieces` and
-//     merges all `pieces` slots (empty pieces carry maxima of -inf);
-//   balanced shares: workgroup (share v, lane) takes the cut at the start of
-//     share v, if any: slice i of the n cuts of the split sequence, whose
-//     pieces are the shares f .. f + n it touches.
-// Threads walk (4-dim chunk, row) items with rows fastest, matching the
-// [slot][D/4][row] partial layout, and fold the pieces four at a time with
-// a running maximum.
-template <int D, int NW, int kItems, int kGroup>
+// Merge the partial states of a sequence cut into fixed pieces (log-sum-exp
+// rule) and write bf16 outputs: workgroup (segment, block of 32 rows x 8
+// four-dim chunks) with one item (four dims of one row) per thread, rows
+// fastest to match the [slot][D/4][row] partial layout, and all `pieces`
+// slots of the item in flight together (empty pieces carry maxima of -inf).
+template <int D, int NW>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, MfmaParams mp) {
   using C = Cfg<D, NW>;
-  // kItems items per thread and kGroup pieces of each have their loads in flight together
+  constexpr int kGroup = 16;  // pieces folded at a time
+  constexpr int kQBlocks = D / 4 / 8;
+  constexpr int kBlocksPerSeg = C::kRows / 32 * kQBlocks;
   const int tid = threadIdx.x;
-  const int u = mp.balanced ? static_cast<int>(blockIdx.x) / mp.merge_split : static_cast<int>(blockIdx.x);
+  const int u = static_cast<int>(blockIdx.x);
+  const int RC = mp.row_chunks;
+  const int segs = a.Hkv * RC;
+  const int R = (a.Hq / a.Hkv) * a.N;
+  const int seg_id = u / kBlocksPerSeg, blk = u % kBlocksPerSeg;
+  const int b = seg_id / segs, seg = seg_id % segs;
+  const int kh = seg / RC, rc = seg % RC;
+  const int rows = min(C::kRows, R - rc * C::kRows);
+  const int r_lo = (blk / kQBlocks) * 32;
+  const int n = min(32, rows - r_lo);
+  if (n <= 0 || (tid & 31) >= n) return;
+  const int q = (blk % kQBlocks) * 8 + (tid >> 5), rl = r_lo + (tid & 31);
+  const PartialView pv = partial_view<D>(a, mp, mp.grid);
+  const size_t slot0 = static_cast<size_t>(seg_id) * mp.pieces;
+  float M = -INFINITY, L = 0.f;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < mp.pieces; k0 += kGroup) {
+    float m[kGroup], l[kGroup];
+    u32x2 ov[kGroup];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+      ov[j] = u32x2{0u, 0u};
+      if (k0 + j < mp.pieces) {
+        const size_t sl = slot0 + k0 + j;
+        m[j] = pv.m[sl * C::kRows + rl];
+        l[j] = pv.l[sl * C::kRows + rl];
+        ov[j] = pv.o[(sl * (D / 4) + q) * C::kRows + rl];
+      }
+    }
+    fold_pieces<kGroup>(M, L, o, m, l, ov);
+  }
+  store_item(a, D, b, kh, rc * C::kRows + rl, q, o, L);
+}
+
+// The second merge kernel of balanced shares (launches whose segments are
+// cut into many pieces): merge_split workgroups per share and lane take the
+// cut at the start of share v, if any, and of its rows the part given by
+// the cut's rank among the sequence's cuts: the sequence's pieces are the
+// shares f .. l it touches, and its n = l - f cuts share its rows.  Items are
+// (4-dim chunk, row), rows fastest, four per thread, pieces two at a time.
+template <int D, int NW>
+__global__ __launch_bounds__(256) void attn_merge_cuts_kernel(AttnArgs a, MfmaParams mp) {
+  using C = Cfg<D, NW>;
+  constexpr int kItems = 4, kGroup = 2, kStep = 256;
+  const int tid = threadIdx.x;
+  const int u = static_cast<int>(blockIdx.x) / mp.merge_split;
   const int G = mp.grid;
   const int RC = mp.row_chunks;
   const int segs = a.Hkv * RC;
-  const int g = a.Hq / a.Hkv;
-  const int R = g * a.N;
-  int b, kh, rc, npieces, slot0, lane = 0, f = 0, cut_first = 0;
-  int r_lo, n, item0, istep;  // rows r_lo .. r_lo + n of the chunk; this thread's items
-  size_t hbytes;
-  if (!mp.balanced) {
-    // workgroup (segment, block of 32 rows x 8 four-dim chunks), one item per thread
-    constexpr int kQBlocks = D / 4 / 8;
-    constexpr int kBlocksPerSeg = C::kRows / 32 * kQBlocks;
-    const int seg_id = u / kBlocksPerSeg, blk = u % kBlocksPerSeg;
-    npieces = mp.pieces;
-    b = seg_id / segs;
-    const int seg = seg_id % segs;
-    kh = seg / RC;
-    rc = seg % RC;
-    slot0 = seg_id * mp.pieces;
-    hbytes = header_bytes(0);
-    const int rows = min(C::kRows, R - rc * C::kRows);
-    r_lo = (blk / kQBlocks) * 32;
-    n = min(32, rows - r_lo);
-    if (n <= 0) return;
-    // items are (chunk q, row): this block's chunks start at 8 (blk % kQBlocks)
-    item0 = ((blk % kQBlocks) * 8 + (tid >> 5)) * n + (tid & 31);
-    if ((tid & 31) >= n) return;
-    istep = 1 << 24;  // one item
-  } else {
-    const int shares = G / segs;
-    const int share = u / segs;
-    lane = u % segs;
-    const int* hdr = static_cast<const int*>(a.workspace);
-    const int4 cut = reinterpret_cast<const int4*>(hdr + 4)[share];
-    if (cut.x < 0) return;
-    const ShareSplit sp{hdr[1], hdr[2]};
-    b = cut.x;
-    f = sp.share_of(cut.y);
-    const int last = sp.share_of(cut.y + cut.z - 1);
-    npieces = last - f + 1;
-    const int nslices = last - f, slice = cut.w;
-    kh = lane / RC;
-    rc = lane % RC;
-    cut_first = cut.y != sp.start(f);  // the sequence starts inside share f: that share's last piece
-    slot0 = 0;
-    hbytes = header_bytes(shares);
-    const int rows = min(C::kRows, R - rc * C::kRows);
-    // this workgroup's part of the cut's row slice
-    const int parts = nslices * mp.merge_split, part = slice * mp.merge_split + static_cast<int>(blockIdx.x) % mp.merge_split;
-    r_lo = part * rows / parts;
-    n = (part + 1) * rows / parts - r_lo;
-    if (n <= 0) return;
-    item0 = tid;
-    istep = 256;
-  }
-  (void)hbytes;
+  const int R = (a.Hq / a.Hkv) * a.N;
+  const int share = u / segs, lane = u % segs;
+  const int* hdr = reinterpret_cast<const int*>(static_cast<const char*>(a.workspace) + kCounterBytes);
+  const int4 cut = reinterpret_cast<const int4*>(hdr + 4)[share];
+  if (cut.x < 0) return;
+  const ShareSplit sp{hdr[1], hdr[2]};
+  const int b = cut.x;
+  const int f = sp.share_of(cut.y);
+  const int npieces = sp.share_of(cut.y + cut.z - 1) - f + 1;
+  const int kh = lane / RC, rc = lane % RC;
+  // the sequence's tiles start inside share f: its piece there is that
+  // share's second slot
+  const bool cut_first = cut.y != sp.start(f);
+  const int rows = min(C::kRows, R - rc * C::kRows);
+  const int parts = (npieces - 1) * mp.merge_split;
+  const int part = cut.w * mp.merge_split + static_cast<int>(blockIdx.x) % mp.merge_split;
+  const int r_lo = part * rows / parts;
+  const int n = (part + 1) * rows / parts - r_lo;
+  if (n <= 0) return;
   const PartialView pv = partial_view<D>(a, mp, G);
-  auto slot_of = [&](int k) __attribute__((always_inline)) {
-    if (!mp.balanced) return slot0 + k;
-    const int vv = (f + k) * segs + lane;  // workgroup of share f + k in this lane
-    return (k == 0 && cut_first) ? G + vv : vv;
-  };
   const int nitems = n * (D / 4);
-  // kItems items per thread at a time, pieces kGroup at a time: every load
-  // of a round is issued before any is used
-  for (int it0 = item0; it0 < nitems; it0 += kItems * istep) {
-    float M[kItems], L[kItems];
-    float o[kItems][4];
+  for (int it0 = tid; it0 < nitems; it0 += kItems * kStep) {
+    float M[kItems], L[kItems], o[kItems][4];
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
       M[i] = -INFINITY;
@@ -963,7 +1128,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, MfmaParams 
       u32x2 ov[kItems][kGroup];
 #pragma unroll
       for (int i = 0; i < kItems; ++i) {
-        const int item = it0 + i * istep;
+        const int item = it0 + i * kStep;
         const int q = item / n, rl = r_lo + item % n;
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) {
@@ -971,7 +1136,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, MfmaParams 
           l[i][j] = 0.f;
           ov[i][j] = u32x2{0u, 0u};
           if (item < nitems && k0 + j < npieces) {
-            const size_t sl = static_cast<size_t>(slot_of(k0 + j));
+            const int vv = (f + k0 + j) * segs + lane;
+            const size_t sl = static_cast<size_t>((k0 + j == 0 && cut_first) ? G + vv : vv);
             m[i][j] = pv.m[sl * C::kRows + rl];
             l[i][j] = pv.l[sl * C::kRows + rl];
             ov[i][j] = pv.o[(sl * (D / 4) + q) * C::kRows + rl];
@@ -979,46 +1145,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, MfmaParams 
         }
       }
 #pragma unroll
-      for (int i = 0; i < kItems; ++i) {
-        float Mn = M[i];
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) Mn = fmaxf(Mn, m[i][j]);
-        if (Mn == -INFINITY) continue;  // no visible key in any piece so far
-        const float sc = exp2_fast(M[i] - Mn);  // 0 while M is -inf
-        L[i] *= sc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[i][e] *= sc;
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) {
-          // a piece without visible keys (or an empty one) has m = -inf and
-          // contributes nothing; its other values are not used
-          const bool use = m[i][j] != -INFINITY;
-          const float w = use ? exp2_fast(m[i][j] - Mn) * l[i][j] : 0.f;
-          L[i] += w;
-          const float x0 = __uint_as_float(ov[i][j][0] << 16), x1 = __uint_as_float(ov[i][j][0] & 0xFFFF0000u);
-          const float x2 = __uint_as_float(ov[i][j][1] << 16), x3 = __uint_as_float(ov[i][j][1] & 0xFFFF0000u);
-          o[i][0] += use ? w * x0 : 0.f;
-          o[i][1] += use ? w * x1 : 0.f;
-          o[i][2] += use ? w * x2 : 0.f;
-          o[i][3] += use ? w * x3 : 0.f;
-        }
-        M[i] = Mn;
-      }
+      for (int i = 0; i < kItems; ++i) fold_pieces<kGroup>(M[i], L[i], o[i], m[i], l[i], ov[i]);
     }
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-      const int item = it0 + i * istep;
+      const int item = it0 + i * kStep;
       if (item >= nitems) break;
-      const int q = item / n, rl = r_lo + item % n;
-      const float inv = L[i] > 0.f ? 1.f / L[i] : 0.f;
-      const int r = rc * C::kRows + rl;
-      const int node = r / g, hg = r % g;
-      uint16_t* op = static_cast<uint16_t*>(a.out) +
-                     ((static_cast<size_t>(b) * a.N + node) * a.Hq + kh * g + hg) * D + 4 * q;
-      u32x2 w;
-      w[0] = pack_bf16x2(o[i][0] * inv, o[i][1] * inv);
-      w[1] = pack_bf16x2(o[i][2] * inv, o[i][3] * inv);
-      *reinterpret_cast<u32x2*>(op) = w;
+      store_item(a, D, b, kh, rc * C::kRows + r_lo + item % n, item / n, o[i], L[i]);
     }
   }
 }
@@ -1039,18 +1172,17 @@ hipError_t launch_cfg(const AttnArgs& a, const MfmaParams& mp, hipStream_t strea
                        shmem, stream, a, mp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (!mp.balanced ? mp.pieces == 1 : mp.grid == a.Hkv * mp.row_chunks) return e;  // no segment is ever shared
-  // fixed pieces: one workgroup per (segment, 32 rows x 32 dims), one item
-  // per thread with all pieces in flight; balanced: merge_split per attention
-  // workgroup (its cut), four items per thread
   if (mp.balanced) {
-    hipLaunchKernelGGL((attn_merge_kernel<D, NW, 4, 2>), dim3(static_cast<unsigned>(mp.grid * mp.merge_split)), dim3(256), 0,
-                       stream, a, mp);
-  } else {
-    const long blocks = static_cast<long>(a.B) * a.Hkv * mp.row_chunks * (C::kRows / 32) * (D / 32);
-    hipLaunchKernelGGL((attn_merge_kernel<D, NW, 1, 16>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       a, mp);
+    // merged in the attention kernel, or nothing to merge with one share per lane
+    if (mp.fused_merge || mp.grid == a.Hkv * mp.row_chunks) return e;
+    hipLaunchKernelGGL((attn_merge_cuts_kernel<D, NW>), dim3(static_cast<unsigned>(mp.grid * mp.merge_split)),
+                       dim3(256), 0, stream, a, mp);
+    return hipGetLastError();
   }
+  if (mp.pieces == 1) return e;  // no segment is ever shared
+  // fixed pieces: one workgroup per (segment, 32 rows x 32 dims)
+  const long blocks = static_cast<long>(a.B) * a.Hkv * mp.row_chunks * (C::kRows / 32) * (D / 32);
+  hipLaunchKernelGGL((attn_merge_kernel<D, NW>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a, mp);
   return hipGetLastError();
 }
 
@@ -1060,6 +1192,10 @@ hipError_t launch_cfg(const AttnArgs& a, const MfmaParams& mp, hipStream_t strea
 // MFMAs; an 8-wave workgroup (one per unit, in lockstep at every tile
 // barrier) measured slower even where it halves the row chunks.
 constexpr int kComputeUnits = 256;
+// balanced shares: with two or more shares per lane, G = shares * lanes is at
+// most one round of resident workgroups; a single share per lane cuts no
+// sequence and counts nothing
+static_assert(kMaxCounters >= kComputeUnits * 2, "one arrival counter per balanced workgroup");
 constexpr int kMinTilesPerPiece = 4;  // balanced shares
 // fixed pieces: each cut adds a partial state of kRows rows, written and
 // merged; 5 tiles per piece (14 pieces, 224 workgroups) is the measured sweet
@@ -1077,6 +1213,7 @@ MfmaParams plan_for(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
   MfmaParams p;
   // the row chunks of a KV head share its K/V tiles through L2
   p.waves = 4;
+  p.fused_merge = 0;
   p.merge_split = 1;
   p.row_chunks = (R + p.waves * 32 - 1) / (p.waves * 32);
   const long max_tiles = (static_cast<long>(max_prefix_len) + N + kTile - 1) / kTile;
@@ -1098,9 +1235,15 @@ MfmaParams plan_for(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
     if (shares < 1) shares = 1;
     p.balanced = 1;
     p.T = kMinTilesPerPiece;
-    // merge workgroups per cut: three with one row chunk per KV head (the
-    // batched workload 127.3 -> 124.7 us against two), two with several (the
-    // Qwen2 workload 161.2 -> 159.6 us against three)
+    // Who merges a cut sequence: with many segments (a sequence at the
+    // longest prefix spans fewer than four shares) the workgroup finishing
+    // its last piece, in the attention kernel (the batched workload 123 ->
+    // 119 us, the 70B-shaped chain 278 -> 266 us); with few, whose cut
+    // sequences have eight or more pieces that one workgroup would fold in
+    // series, a second kernel with many workgroups per cut (the Qwen2
+    // workload: 156 us, against 159 us fused).  Merge workgroups per cut
+    // there: three with one row chunk per KV head, two with several.
+    p.fused_merge = segments * 4 > resident;
     p.merge_split = p.row_chunks == 1 ? 3 : 2;
     p.pieces = 0;
     p.grid = static_cast<int>(shares * lanes);
@@ -1113,8 +1256,8 @@ MfmaParams plan_for(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
 size_t attention_mfma_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int max_prefix_len) {
   const MfmaParams p = plan_for(B, N, Hq, Hkv, D, max_prefix_len);
   const size_t slots = static_cast<size_t>(p.balanced ? 2 * p.grid : p.grid) * p.waves * 32;
-  const int shares = p.balanced ? p.grid / (Hkv * p.row_chunks) : 0;
-  return header_bytes(shares) + slots * (2 * D + 2 * sizeof(float));
+  const size_t hbytes = p.balanced ? header_bytes(p.grid / (Hkv * p.row_chunks)) : 0;
+  return kCounterBytes + hbytes + slots * (2 * D + 2 * sizeof(float));
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
