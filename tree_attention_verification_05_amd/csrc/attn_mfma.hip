@@ -701,6 +701,25 @@ void attn_mfma_kernel(AttnArgs a, MfmaParams mp) {
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop), pb, acc[db], 0, 0, 0);
           }
         }
+        if constexpr (POLICY != kNonTemporal) {
+          // Several row chunks per KV head share each K/V tile through the
+          // L2, and the matrix cores, not HBM, set the pace.  A wave issues
+          // in order, so the next tile's eight dependent score MFMAs, left
+          // back to back, would stall it for their whole latency: interleave
+          // three VALU instructions of the softmax after each of them and
+          // four after each PV MFMA (the Qwen2 workload 160.0 -> 153.5 us;
+          // 6/2, 4/3, 4/4, 2/4, 2/5, 3/3 and exp-first groups measured
+          // between 153 and 165 us).  The HBM-bound instance keeps the
+          // compiler's order (3-4 % slower on the batched workload there).
+          static_for<0, 8>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+          });
+          static_for<0, 8>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          });
+        }
     };
     // S^T of the piece's first tile
     auto compute_s = [&](auto stage_c, f32x16& sc) __attribute__((always_inline)) {
