@@ -152,8 +152,8 @@ TARGETS = {3: ("hbm", 0.60), 4: ("mfma", 0.40), 5: ("hbm", 0.60)}
 ATTN_CALL = "tv_tree_attention_parents"
 STEP_CALLS = [ATTN_CALL, "tv_accept_greedy_compact"]
 TIME_BASE = ("mean HIP-event time of each call, events recorded on the launch stream around the "
-             "call's launches (for attention: main kernel, launch gap and merge kernel), one "
-             "eviction before every step")
+             "call's launches (for attention: the main kernel, plus the launch gap and merge kernel "
+             "where a second kernel merges the split key ranges), one eviction before every step")
 
 
 class StepBench:
