@@ -293,7 +293,7 @@ class StepBench:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no "
               "multi-GPU path; the per-GPU shard runs as --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
