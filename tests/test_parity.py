@@ -413,6 +413,34 @@ def test_device_status_bits():
     assert int(st.item()) & T.TV_DEV_BAD_CACHE
 
 
+def test_device_status_on_fused_merge_schedule():
+    """Forty sequences: enough segments that cut sequences are merged inside
+    the attention kernel.  A block id outside the cache in one sequence and a
+    prefix length above max_prefix_len in another are reported
+    (TV_DEV_BAD_CACHE); every other sequence, cut ones included, still
+    matches the oracle, and the arrival counters end at zero."""
+    w0 = _variant(3, name="fused-status", tag=111, B=40, prefix=(100, 600), V=1000)
+    bad_block, bad_len = 5, 9
+    table = w0.block_table.copy()
+    table[bad_block, 0] = w0.num_blocks
+    prefix = w0.prefix_lens.copy()
+    prefix[bad_len] = w0.max_prefix_len + 10
+    w = dataclasses.replace(w0, block_table=table, prefix_lens=prefix)
+    log(f"[parity] device status on the fused merge schedule: B={w.B}")
+    d = upload(w)
+    # the bound the caller states stays that of the intact batch
+    mpl = w0.max_prefix_len
+    need = T.tv_tree_attention_workspace_size(w.B, w.N, w.spec.Hq, w.spec.Hkv, w.spec.D, mpl)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    out = T.tv_tree_attention_parents(d["q"], d["k"], d["v"], d["table"], d["prefix"], mpl,
+                                      d["parents"], workspace=ws, dev_status=d["status"])
+    torch.cuda.synchronize()
+    assert int(d["status"].item()) == T.TV_DEV_BAD_CACHE
+    assert int(torch.count_nonzero(ws[:2048]).item()) == 0
+    seqs = [b for b in range(w.B) if b not in (bad_block, bad_len)]
+    check_attention(out, oracle_attention(w0, seqs), seqs, w.q.dtype, label="fused-merge status")
+
+
 @pytest.mark.parametrize("which", ["small1", "small2", "small3", "small4", "small5", "full2", "full3", "full4",
                                    "full5", "small3-token-major", "bad-tree", "n64"])
 def test_attention_from_parents(which):
