@@ -135,11 +135,15 @@ __global__ __launch_bounds__(kThreads) void stoch_stats_kernel(const float* __re
         s = (m == -INFINITY) ? 0.f : s * exp2f(m - gm);
         m = gm;
       }
+      // the bare v_exp_f32: exp2f adds a scaling for results in the denormal
+      // range (six more instructions per entry), and such terms add nothing
+      // to a sum whose largest term is 1 (all three calls 2-3 % faster, the
+      // same accepted paths and draws)
       if (m != -INFINITY) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s += exp2f(v[u][e] * k2 - m);
+          for (int e = 0; e < 4; ++e) s += __builtin_amdgcn_exp2f(v[u][e] * k2 - m);
       }
     }
   } else {
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void stoch_stats_kernel(const float* __re
         s = (m == -INFINITY) ? 0.f : s * exp2f(m - y);
         m = y;
       }
-      if (m != -INFINITY) s += exp2f(y - m);
+      if (m != -INFINITY) s += __builtin_amdgcn_exp2f(y - m);
     }
   }
   for (int o = 32; o > 0; o >>= 1) {
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void stoch_draw_kernel(StochArgs a, float
   bool bad = false;
   // one vocabulary entry: r(v) / E(v) as a key
   auto score = [&](int v, float lg, float e, float q) {
-    const float p = exp2f(lg * k2 - m) * inv_s;
+    const float p = __builtin_amdgcn_exp2f(lg * k2 - m) * inv_s;
     float rv;
     if (qrow)
       rv = fmaxf(p - q, 0.f);
